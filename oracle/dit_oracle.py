@@ -1,0 +1,229 @@
+"""CPU oracle of the Flux-style single-stream DiT block forward.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+``cpu_baseline`` leg may import this module.  The GPU library never calls it,
+and it shares no code with the GPU library: the only common dependency is the
+seeded input module ``dit_inputs``, which holds no block arithmetic.
+
+Everything here is the plain definition of the block, computed in float64
+with numpy (a matrix product is the only library primitive used as a step).
+No blocking, fusion or reordering beyond what the definitions state.  The
+block is the one named on the page "ChituDiffusion: torch.compile and CUDA
+Graph on Flux.1-dev" (chenyy20.com, 2026-06-21), section 2 (one Flux
+single-stream block, S=4608, dim 3072, 24 heads x 128, bf16); its ops are the
+ones that page lists in section 1.1 (LayerNorm, GELU, the adaLN modulation
+(1+scale)*x+shift), RoPE as complex rotation (section 3.1) and exact
+attention (the flash / sdpa backends of sections 2 and 4).
+
+Readings of what the pages leave open (all are documented with the tests):
+  * block layout: parallel attention and MLP branches sharing one
+    LayerNorm+modulate; linear1 emits [q | k | v | mlp], linear2 consumes
+    [attn_out | gelu(mlp)]; one gated residual;
+  * modulation chunks in the order shift, scale, gate; SiLU before the linear;
+  * LayerNorm: biased variance, eps inside the square root, no affine;
+  * QK RMSNorm per head (eps 1e-6, weight of length head_dim shared by heads),
+    then RoPE on adjacent pairs (2j, 2j+1) with base 10000; the head dim is
+    split in equal chunks, one per position axis, in axis order;
+  * attention: no mask, scale 1/sqrt(head_dim), softmax over all tokens;
+  * GELU in its tanh form.
+
+Parity status: every function below is pinned by the CPU tests in
+tests/test_oracle_pins.py against library routines, closed forms, invariants
+or brute force; the RoPE axis-split / pairing conventions are pinned by those
+invariants but not by any value printed on the pages (the pages print no
+numeric example of the block).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+# -------------------------------------------------------------- activations
+def silu(z):
+    """SiLU(z) = z * sigmoid(z) = z / (1 + e^{-z}); feeds the modulation linear."""
+    z = np.asarray(z, F64)
+    return z / (1.0 + np.exp(-z))
+
+
+def gelu_tanh(g):
+    """GELU, tanh form: 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))).
+    GELU is one of the fused elementwise ops of section 1.1 of the Flux page;
+    the tanh form is the one fixed for this block."""
+    g = np.asarray(g, F64)
+    return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))
+
+
+# ----------------------------------------------------------------- linears
+def linear(a, w, b=None):
+    """nn.Linear convention: a [rows, in] times w [out, in] transposed, plus b."""
+    out = np.asarray(a, F64) @ np.asarray(w, F64).T
+    if b is not None:
+        out = out + np.asarray(b, F64)
+    return out
+
+
+# ----------------------------------------------------- adaLN modulation GEMV
+def modulation(temb, w_mod, b_mod):
+    """m = W_mod . SiLU(temb) + b_mod, split into (shift, scale, gate), each [d].
+    adaLN modulation of section 1.1 of the Flux page."""
+    m = linear(silu(temb)[None, :], w_mod, b_mod)[0]
+    d = m.shape[0] // 3
+    return m[:d], m[d:2 * d], m[2 * d:]
+
+
+# ----------------------------------------------------- LayerNorm + modulate
+def layer_norm(x, eps):
+    """Row LayerNorm with no affine: (x - mean) / sqrt(var + eps), biased var."""
+    x = np.asarray(x, F64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+def modulate(xn, shift, scale):
+    """adaLN modulation (1 + scale) * x + shift (section 1.1 of the Flux page)."""
+    return xn * (1.0 + np.asarray(scale, F64)) + np.asarray(shift, F64)
+
+
+def layer_norm_modulate(x, shift, scale, eps=1e-6):
+    return modulate(layer_norm(x, eps), shift, scale)
+
+
+# ---------------------------------------------------------- gated residual
+def gated_residual(x, gate, h):
+    """y = x + gate * h, gate broadcast over rows (one per channel)."""
+    return np.asarray(x, F64) + np.asarray(gate, F64) * np.asarray(h, F64)
+
+
+# --------------------------------------------------------- QK RMSNorm heads
+def rms_norm_heads(t, num_heads, head_dim, weight, eps=1e-6):
+    """Per-token, per-head RMSNorm of t [S, H*Dh]: t_h / sqrt(mean(t_h^2) + eps) * w."""
+    t = np.asarray(t, F64).reshape(t.shape[0], num_heads, head_dim)
+    r = np.sqrt((t ** 2).mean(axis=-1, keepdims=True) + eps)
+    return (t / r * np.asarray(weight, F64)).reshape(t.shape[0], num_heads * head_dim)
+
+
+# -------------------------------------------------------------------- RoPE
+def rope_angles(pos, axes_dims, head_dim, base=10000.0):
+    """Rotation angle of every (token, pair) [S, head_dim/2].
+
+    Pairs are consecutive dims (2j, 2j+1).  The head dim is cut into chunks of
+    ``axes_dims`` dims, one per position axis; pair j' of a chunk of D dims on
+    axis a turns by  pos[t, a] * base^(-2 j' / D).
+    """
+    pos = np.asarray(pos, F64)
+    assert sum(axes_dims) == head_dim
+    cols = []
+    for a, D in enumerate(axes_dims):
+        jp = np.arange(D // 2, dtype=F64)
+        freq = base ** (-2.0 * jp / D)
+        cols.append(pos[:, a:a + 1] * freq[None, :])
+    return np.concatenate(cols, axis=1)
+
+
+def rope_apply(t, theta, num_heads, head_dim):
+    """Rotate each pair (a, b) = (t[2j], t[2j+1]) of every head by theta[t, j]:
+    (a cos - b sin, a sin + b cos) -- the pair read as a complex number times
+    e^{i theta} (RoPE as complex arithmetic, section 3.1 of the Flux page)."""
+    S = t.shape[0]
+    t = np.asarray(t, F64).reshape(S, num_heads, head_dim // 2, 2)
+    c = np.cos(theta)[:, None, :]
+    s = np.sin(theta)[:, None, :]
+    a, b = t[..., 0], t[..., 1]
+    out = np.stack([a * c - b * s, a * s + b * c], axis=-1)
+    return out.reshape(S, num_heads * head_dim)
+
+
+# --------------------------------------------------------------- attention
+def softmax_rows(s):
+    s = s - s.max(axis=-1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def attention(q, k, v, num_heads, head_dim, q_rows=None):
+    """Exact softmax attention per head, no mask: o = softmax(q k^T / sqrt(Dh)) v.
+    q, k, v are [S, H*Dh] (heads in column blocks); returns o [len(q_rows), H*Dh].
+    ``q_rows`` restricts the queries (each output row is computed in full);
+    query rows are processed in chunks only to bound memory."""
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    rows = np.arange(q.shape[0]) if q_rows is None else np.asarray(q_rows)
+    out = np.empty((rows.shape[0], num_heads * head_dim), F64)
+    scale = 1.0 / np.sqrt(head_dim)
+    for h in range(num_heads):
+        cs = slice(h * head_dim, (h + 1) * head_dim)
+        kh, vh = k[:, cs], v[:, cs]
+        for r0 in range(0, rows.shape[0], 1024):
+            rr = rows[r0:r0 + 1024]
+            p = softmax_rows((q[rr, cs] @ kh.T) * scale)
+            out[r0:r0 + len(rr), cs] = p @ vh
+    return out
+
+
+# ------------------------------------------------------------- whole block
+def block_forward(shape, w, x, temb, pos, rows=None, return_intermediates=False):
+    """One single-stream block forward.
+
+    Steps (the order used throughout this project):
+      1. shift, scale, gate = W_mod . SiLU(temb) + b_mod
+      2. u = LN(x) * (1 + scale) + shift
+      3. z = u W1^T + b1  ->  q, k, v, g
+      4. q, k <- per-head RMSNorm (w_q, w_k); 5. RoPE on q and k
+      6. o = softmax(q k^T / sqrt(Dh)) v per head
+      7. a = GELU_tanh(g)
+      8. h = [o | a] W2^T + b2
+      9. y = x + gate * h
+    ``rows`` restricts the output to those tokens (keys and values still cover
+    every token, so each returned row is exact).
+    """
+    d, H, Dh = shape.dim, shape.num_heads, shape.head_dim
+    x = np.asarray(x, F64)
+    shift, scale, gate = modulation(temb, w.w_mod, w.b_mod)
+    u = layer_norm_modulate(x, shift, scale, shape.ln_eps)
+    rr = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    theta = rope_angles(pos, shape.rope_axes_dims, Dh, shape.rope_base)
+    # keys / values for every token
+    w1 = np.asarray(w.w1, F64)
+    b1 = np.asarray(w.b1, F64)
+    kk = linear(u, w1[d:2 * d], b1[d:2 * d])
+    vv = linear(u, w1[2 * d:3 * d], b1[2 * d:3 * d])
+    kk = rope_apply(rms_norm_heads(kk, H, Dh, w.k_norm_w, shape.qk_eps), theta, H, Dh)
+    # queries and mlp only for the requested rows
+    ur = u[rr]
+    qq = linear(ur, w1[0:d], b1[0:d])
+    qq = rope_apply(rms_norm_heads(qq, H, Dh, w.q_norm_w, shape.qk_eps), theta[rr], H, Dh)
+    g = linear(ur, w1[3 * d:], b1[3 * d:])
+    # attention for the requested rows: queries are the rows' own q
+    o = _attention_rows(qq, kk, vv, H, Dh)
+    a = gelu_tanh(g)
+    hb = linear(np.concatenate([o, a], axis=1), w.w2, w.b2)
+    y = gated_residual(x[rr], gate, hb)
+    if return_intermediates:
+        return y, dict(shift=shift, scale=scale, gate=gate, u=u[rr], q=qq, k=kk[rr],
+                       v=vv[rr], k_all=kk, v_all=vv, o=o, g=g, a=a, h=hb)
+    return y
+
+
+def _attention_rows(q_rows, k, v, num_heads, head_dim):
+    """attention() with a query matrix that already holds only the wanted rows."""
+    qfull = np.asarray(q_rows, F64)
+    return attention(qfull, k, v, num_heads, head_dim, q_rows=np.arange(qfull.shape[0]))
+
+
+def stack_forward(shape, weights_list, x_in, temb_steps, pos, chain=False):
+    """Denoising-loop replay of a block stack: for each step s, run every block
+    in order on the step input with temb_s; the step input is x_in, or the
+    previous step's output when ``chain`` is set.  Returns [n_steps, S, d]."""
+    outs = []
+    xs = np.asarray(x_in, F64)
+    for s in range(len(temb_steps)):
+        cur = xs if (chain and s > 0) else np.asarray(x_in, F64)
+        for w in weights_list:
+            cur = block_forward(shape, w, cur, temb_steps[s], pos)
+        outs.append(cur)
+        xs = cur
+    return np.stack(outs)
