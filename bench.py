@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the Flux single-stream DiT block forward on one MI355X.
+
+A step is one denoising step of a 57-block stack of Flux-shaped
+single-stream blocks (S=4608, dim 3072, 24 heads x 128, MLP 12288, bf16,
+independent random weights), replayed as one captured hipGraph per step.
+The headline value is milliseconds per block forward (step time / 57).
+Beside it: per-kernel times from HIP events (GEMM TFLOP/s, attention
+TFLOP/s, fused LayerNorm+modulate and gated-residual HBM GB/s with buffer
+rotation so the 256 MB last-level cache cannot hold the working set), the
+roofline fraction of the dominant kernel, and the CPU oracle's time for one
+block on the host cores.
+
+Prints ONE JSON line on stdout.  Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--blocks 57] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per DiT block forward (S=4608,d=3072 bf16) + fused-norm HBM GB/s"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+S, D, H, DH, MLP = 4608, 3072, 24, 128, 12288
+N1, N2 = 3 * D + MLP, D + MLP
+GEMM1_FLOP = 2.0 * S * D * N1
+GEMM2_FLOP = 2.0 * S * N2 * D
+ATTN_FLOP = 4.0 * H * S * S * DH
+BLOCK_FLOP = GEMM1_FLOP + GEMM2_FLOP + ATTN_FLOP + 2.0 * 3 * D * D
+NORM_BYTES = 2 * S * D * 2                   # read x, write u (bf16)
+GRES_BYTES = 3 * S * D * 2                   # read x and h, write y
+QKNORM_BYTES = 4 * S * D * 2                 # read and write q and k
+MOD_BYTES = 3 * D * D * 2                    # the modulation weight
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "dit_common.hpp"):
+        with open(os.path.join(ROOT, "diffusion_transformer_dit_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    PMC summary, or None when it is absent or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", "gemm_linear1_flux_traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_launches(fn, iters, warm=2):
+    import torch
+    for _ in range(warm):
+        fn(0)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        fn(i)
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def cpu_baseline():
+    """The oracle (numpy float64) on one full Flux-shape block on the host cores."""
+    import numpy as np
+    import dit_inputs as DI
+    from oracle import dit_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    shape = DI.FLUX
+    w = DI.block_weights(shape)
+    x, temb = DI.block_activations(shape)
+    pos = DI.positions(shape)
+    t0 = time.perf_counter()
+    y = O.block_forward(shape, w, x, temb, pos)
+    dt = time.perf_counter() - t0
+    assert np.all(np.isfinite(y))
+    return dict(value=round(dt * 1000.0, 1), unit="ms per block", cores=int(threads), kind="oracle",
+                sample="one full Flux-shape block forward (S=4608, d=3072, 24x128, MLP 12288) "
+                       "in numpy float64, BLAS threads = cores; 1 of the 57 blocks of a step")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--blocks", type=int, default=57)
+    ap.add_argument("--kernel-iters", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the block's multi-GPU sharding is a design, not built)", file=sys.stderr)
+        return 2
+
+    import torch
+    from diffusion_transformer_dit_amd import binding as B
+    import dit_inputs as DI
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3000)
+
+    def randn(shape, sigma):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * sigma).to(torch.bfloat16)
+
+    nb = args.blocks
+    log(f"allocating {nb} Flux blocks ({nb * (3 * D * D + N1 * D + D * N2) * 2 / 1e9:.1f} GB of weights)")
+    blocks = []
+    for b in range(nb):
+        blocks.append(B.BlockWeights(randn((3 * D, D), 0.02), randn((3 * D,), 0.02), randn((N1, D), 0.02),
+                                     randn((N1,), 0.02), randn((D, N2), 0.02), randn((D,), 0.02),
+                                     torch.ones(DH, device=dev), torch.ones(DH, device=dev)))
+    x_in = randn((S, D), 1.0)
+    n_total = args.warmup + args.steps
+    temb = randn((max(n_total, 1), D), 1.0)
+    pos = torch.from_numpy(DI.positions(DI.FLUX)).to(dev)
+    rc, rs = B.rope_table(pos, list(DI.FLUX.rope_axes_dims), DH)
+    cfg = B.make_config(S, D, H, DH, MLP)
+    ws = B.alloc_workspace(B.stack_workspace_bytes(cfg))
+    out = torch.empty(max(n_total, 1), S, D, dtype=torch.bfloat16, device=dev)
+    st = B.Stack()
+    torch.cuda.synchronize()
+
+    # ---- warmup (the first replay captures the graph)
+    if args.warmup:
+        st.replay(cfg, blocks, x_in, temb[:args.warmup], rc, rs, out[:args.warmup], ws)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    # ---- timed region: exactly K steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    st.replay(cfg, blocks, x_in, temb[args.warmup:n_total], rc, rs, out[args.warmup:n_total], ws)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / max(args.steps, 1)
+    ms_block = ms_step / nb
+    assert torch.isfinite(out[args.warmup:n_total].float()).all(), "non-finite output"
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, {ms_block:.4f} ms/block (wall {wall:.3f} s)")
+
+    # ---- per-kernel timing on the same stream, one block's worth of buffers
+    w0 = blocks[0]
+    u = torch.empty(S, D, dtype=torch.bfloat16, device=dev)
+    qkv = torch.empty(S, 3 * D, dtype=torch.bfloat16, device=dev)
+    cat = torch.empty(S, N2, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(S, D, dtype=torch.bfloat16, device=dev)
+    mod = B.modulation(temb[0], w0.tensors[0], w0.tensors[1])
+    B.modulate_norm(x_in, mod[:D], mod[D:2 * D], 1e-6, out=u)
+    it = args.kernel_iters
+    k = {}
+    k["linear1_gelu"] = time_launches(lambda i: B.linear1_gelu(u, w0.tensors[2], w0.tensors[3], qkv, cat, MLP), it)
+    k["qk_rmsnorm_rope"] = time_launches(
+        lambda i: B.qk_rmsnorm_rope(qkv, w0.tensors[6], w0.tensors[7], rc, rs, H, DH), it)
+    B.linear1_gelu(u, w0.tensors[2], w0.tensors[3], qkv, cat, MLP)
+    B.qk_rmsnorm_rope(qkv, w0.tensors[6], w0.tensors[7], rc, rs, H, DH)
+    k["attention"] = time_launches(lambda i: B.attention(qkv, cat, H, DH), it)
+    gate = mod[2 * D:]
+    k["linear2_gated_residual"] = time_launches(
+        lambda i: B.linear2_gated_residual(cat, w0.tensors[4], w0.tensors[5], x_in, gate, y), it)
+    # modulation GEMV over the 57 distinct weights (each 56.6 MB; never cache resident together)
+    k["modulation"] = time_launches(
+        lambda i: B.modulation(temb[0], blocks[i % nb].tensors[0], blocks[i % nb].tensors[1], out=mod), it)
+    # memory-bound chain with buffer rotation: 12 sets x 56.6 MB > 256 MB MALL
+    nrot = 12
+    xs = [randn((S, D), 1.0) for _ in range(nrot)]
+    hs = [randn((S, D), 1.0) for _ in range(nrot)]
+    us = [torch.empty(S, D, dtype=torch.bfloat16, device=dev) for _ in range(nrot)]
+    shift = (torch.randn(D, generator=g, device=dev) * 0.1)
+    scale = (torch.randn(D, generator=g, device=dev) * 0.1)
+    gvec = (torch.randn(D, generator=g, device=dev) * 0.1)
+    norm_iters = max(it, 4 * nrot)
+    k["modulate_norm"] = time_launches(
+        lambda i: B.modulate_norm(xs[i % nrot], shift, scale, 1e-6, out=us[i % nrot]), norm_iters)
+    k["gated_residual"] = time_launches(
+        lambda i: B.gated_residual(xs[i % nrot], hs[i % nrot], gvec, out=us[i % nrot]), norm_iters)
+    # cache-warm single buffer, reported as a footnote only
+    k_warm_norm = time_launches(lambda i: B.modulate_norm(xs[0], shift, scale, 1e-6, out=us[0]), norm_iters)
+    torch.cuda.synchronize()
+    for name, ms in k.items():
+        log(f"kernel {name}: {ms * 1000:.1f} us")
+
+    tf = lambda flop, ms: flop / (ms * 1e-3) / 1e12
+    gbs = lambda byt, ms: byt / (ms * 1e-3) / 1e9
+    kernels = {
+        "linear1_gelu": dict(us=k["linear1_gelu"] * 1e3, tflops=tf(GEMM1_FLOP, k["linear1_gelu"]),
+                             frac=tf(GEMM1_FLOP, k["linear1_gelu"]) / BF16_PEAK_TFLOPS),
+        "linear2_gated_residual": dict(us=k["linear2_gated_residual"] * 1e3,
+                                       tflops=tf(GEMM2_FLOP, k["linear2_gated_residual"]),
+                                       frac=tf(GEMM2_FLOP, k["linear2_gated_residual"]) / BF16_PEAK_TFLOPS),
+        "attention": dict(us=k["attention"] * 1e3, tflops=tf(ATTN_FLOP, k["attention"]),
+                          frac=tf(ATTN_FLOP, k["attention"]) / BF16_PEAK_TFLOPS),
+        "modulate_norm": dict(us=k["modulate_norm"] * 1e3, gbs=gbs(NORM_BYTES, k["modulate_norm"]),
+                              frac=gbs(NORM_BYTES, k["modulate_norm"]) / HBM_PEAK_GBS,
+                              cache_warm_gbs=gbs(NORM_BYTES, k_warm_norm)),
+        "gated_residual": dict(us=k["gated_residual"] * 1e3, gbs=gbs(GRES_BYTES, k["gated_residual"]),
+                               frac=gbs(GRES_BYTES, k["gated_residual"]) / HBM_PEAK_GBS),
+        "qk_rmsnorm_rope": dict(us=k["qk_rmsnorm_rope"] * 1e3, gbs=gbs(QKNORM_BYTES, k["qk_rmsnorm_rope"]),
+                                frac=gbs(QKNORM_BYTES, k["qk_rmsnorm_rope"]) / HBM_PEAK_GBS),
+        "modulation": dict(us=k["modulation"] * 1e3, gbs=gbs(MOD_BYTES, k["modulation"]),
+                           frac=gbs(MOD_BYTES, k["modulation"]) / HBM_PEAK_GBS),
+    }
+    for v in kernels.values():
+        for kk in list(v):
+            v[kk] = round(v[kk], 4 if kk == "frac" else 2)
+    sum_kernels_ms = sum(k[n] for n in ("modulation", "linear1_gelu", "qk_rmsnorm_rope", "attention",
+                                        "linear2_gated_residual")) + k_warm_norm
+
+    g1 = tf(GEMM1_FLOP, k["linear1_gelu"])
+    traffic = load_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(ms_block, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, x and temb ~ N(0,1); no trained weights)",
+        "config": {"workload": "flux_single_stream_block_stack", "seq_len": S, "dim": D, "num_heads": H,
+                   "head_dim": DH, "mlp_hidden": MLP, "blocks": nb, "rope": "2d (64 row | 64 col dims)",
+                   "replay": "one hipGraph of the whole stack per denoising step"},
+        "block_tflops": round(BLOCK_FLOP / (ms_block * 1e-3) / 1e12, 1),
+        "fused_norm_gbs": kernels["modulate_norm"]["gbs"],
+        "fused_norm_frac": kernels["modulate_norm"]["frac"],
+        "roofline": {"bound": "mfma", "kernel": "linear1_gelu (GEMM1 + bias + GELU epilogue)",
+                     "achieved": round(g1, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(g1 / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "flop_per_launch": GEMM1_FLOP},
+        "kernels": kernels,
+        "launch_overhead_frac": round(max(0.0, 1.0 - sum_kernels_ms / ms_block), 4),
+        "context": {"pages_h20_ms_per_57_block_forward_eager": 762.7,
+                    "pages_h20_ms_per_57_block_forward_compiled": 637.8,
+                    "this_ms_per_57_block_step": round(ms_block * 57, 2),
+                    "note": "H20 figures cover 19 double- and 38 single-stream Flux blocks; context only"},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one Flux block ...")
+        result["cpu_baseline"] = cpu_baseline()
+        log(f"cpu oracle: {result['cpu_baseline']['value']} ms/block on {result['cpu_baseline']['cores']} threads")
+    st.close()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,305 @@
+"""Thin ctypes binding of libdit_block (argument marshalling only).
+
+Every function takes torch tensors that live on the GPU, checks dtype /
+shape / contiguity, and passes raw pointers and the current HIP stream to the
+C ABI declared in include/dit_block.h.  All arithmetic happens in the HIP
+kernels; if the shared library is missing this module raises at import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdit_block.so")
+
+DIT_OK, DIT_ERR_INVALID_ARG, DIT_ERR_UNSUPPORTED, DIT_ERR_WORKSPACE, DIT_ERR_HIP, \
+    DIT_ERR_CAPTURE, DIT_ERR_GRAPH_KEY = range(7)
+DIT_STACK_CHAIN = 1
+
+ERROR_NAMES = {1: "DIT_ERR_INVALID_ARG", 2: "DIT_ERR_UNSUPPORTED", 3: "DIT_ERR_WORKSPACE",
+               4: "DIT_ERR_HIP", 5: "DIT_ERR_CAPTURE", 6: "DIT_ERR_GRAPH_KEY"}
+
+
+class DitError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class BlockConfig(ctypes.Structure):
+    _fields_ = [("seq_len", ctypes.c_int32), ("dim", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("mlp_hidden", ctypes.c_int32), ("temb_dim", ctypes.c_int32),
+                ("ln_eps", ctypes.c_float), ("qk_eps", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+
+class BlockWeightsC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_mod", "b_mod", "w1", "b1", "w2", "b2", "q_norm_w", "k_norm_w")]
+
+
+VP, I64, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+
+SIGNATURES = {
+    "dit_modulation": ([VP, VP, VP, VP, I64, I64, VP], ctypes.c_int),
+    "dit_modulate_norm": ([VP, VP, VP, VP, I64, I64, F32, VP], ctypes.c_int),
+    "dit_gated_residual": ([VP, VP, VP, VP, I64, I64, VP], ctypes.c_int),
+    "dit_linear1_gelu": ([VP, VP, VP, VP, VP, I64, I64, I64, VP], ctypes.c_int),
+    "dit_qk_rmsnorm_rope": ([VP, VP, VP, VP, VP, I64, I64, I64, F32, VP], ctypes.c_int),
+    "dit_attention": ([VP, VP, I64, I64, I64, I64, VP], ctypes.c_int),
+    "dit_linear2_gated_residual": ([VP, VP, VP, VP, VP, VP, I64, I64, I64, VP], ctypes.c_int),
+    "dit_rope_table": ([VP, I64, I32, VP, I64, F32, VP, VP, VP], ctypes.c_int),
+    "dit_block_workspace_bytes": ([VP], SZ),
+    "dit_block_forward": ([VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
+    "dit_stack_create": ([VP], ctypes.c_int),
+    "dit_stack_destroy": ([VP], ctypes.c_int),
+    "dit_stack_workspace_bytes": ([VP], SZ),
+    "dit_stack_replay": ([VP, VP, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
+    "dit_last_error": ([], ctypes.c_char_p),
+    "dit_version": ([], ctypes.c_char_p),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m diffusion_transformer_dit_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = load_library()
+
+
+def _check(rc: int):
+    if rc != DIT_OK:
+        raise DitError(rc, _lib.dit_last_error().decode())
+
+
+def version() -> str:
+    return _lib.dit_version().decode()
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+BF16, F32T, I32T = torch.bfloat16, torch.float32, torch.int32
+
+
+# --------------------------------------------------------------------- steps
+def modulation(temb, w_mod, b_mod=None, out=None, stream=None):
+    """mod = W_mod . SiLU(temb) + b_mod (fp32 [3d], shift | scale | gate)."""
+    _need(temb, BF16, "temb", 1)
+    _need(w_mod, BF16, "w_mod", 2)
+    if b_mod is not None:
+        _need(b_mod, BF16, "b_mod", 1)
+    three_d, tdim = w_mod.shape
+    if temb.numel() != tdim or three_d % 3:
+        raise ValueError("shape mismatch between temb and w_mod")
+    out = torch.empty(three_d, dtype=F32T, device=temb.device) if out is None else out
+    _need(out, F32T, "out", 1)
+    _check(_lib.dit_modulation(_p(temb), _p(w_mod), _p(b_mod), _p(out), three_d // 3, tdim, _stream(stream)))
+    return out
+
+
+def modulate_norm(x, shift, scale, eps=1e-6, out=None, stream=None):
+    """out = LN(x) * (1 + scale) + shift, one pass."""
+    _need(x, BF16, "x", 2)
+    _need(shift, F32T, "shift", 1)
+    _need(scale, F32T, "scale", 1)
+    rows, cols = x.shape
+    if shift.numel() != cols or scale.numel() != cols:
+        raise ValueError("shift/scale length must equal x.shape[1]")
+    out = torch.empty_like(x) if out is None else out
+    _need(out, BF16, "out", 2)
+    _check(_lib.dit_modulate_norm(_p(x), _p(shift), _p(scale), _p(out), rows, cols, eps, _stream(stream)))
+    return out
+
+
+def gated_residual(x, h, gate, out=None, stream=None):
+    """y = x + gate * h."""
+    _need(x, BF16, "x", 2)
+    _need(h, BF16, "h", 2)
+    _need(gate, F32T, "gate", 1)
+    if h.shape != x.shape or gate.numel() != x.shape[1]:
+        raise ValueError("shape mismatch")
+    out = torch.empty_like(x) if out is None else out
+    _need(out, BF16, "out", 2)
+    _check(_lib.dit_gated_residual(_p(x), _p(h), _p(gate), _p(out), x.shape[0], x.shape[1], _stream(stream)))
+    return out
+
+
+def linear1_gelu(u, w1, b1, qkv, cat, mlp_hidden, stream=None):
+    """qkv <- (u W1^T + b1)[:, :3d]; cat[:, d:] <- GELU_tanh((u W1^T + b1)[:, 3d:])."""
+    _need(u, BF16, "u", 2)
+    _need(w1, BF16, "w1", 2)
+    _need(qkv, BF16, "qkv", 2)
+    _need(cat, BF16, "cat", 2)
+    if b1 is not None:
+        _need(b1, BF16, "b1", 1)
+    S, d = u.shape
+    if w1.shape != (3 * d + mlp_hidden, d) or qkv.shape != (S, 3 * d) or cat.shape != (S, d + mlp_hidden):
+        raise ValueError("shape mismatch")
+    _check(_lib.dit_linear1_gelu(_p(u), _p(w1), _p(b1), _p(qkv), _p(cat), S, d, mlp_hidden, _stream(stream)))
+
+
+def qk_rmsnorm_rope(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, num_heads, head_dim, eps=1e-6, stream=None):
+    """In place on the q and k blocks of qkv: per-head RMSNorm, then RoPE."""
+    _need(qkv, BF16, "qkv", 2)
+    for t, n in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w"), (rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        _need(t, F32T, n)
+    S = qkv.shape[0]
+    if qkv.shape[1] != 3 * num_heads * head_dim or rope_cos.shape != (S, head_dim // 2) \
+            or rope_sin.shape != (S, head_dim // 2) or q_norm_w.numel() != head_dim or k_norm_w.numel() != head_dim:
+        raise ValueError("shape mismatch")
+    _check(_lib.dit_qk_rmsnorm_rope(_p(qkv), _p(q_norm_w), _p(k_norm_w), _p(rope_cos), _p(rope_sin),
+                                    S, num_heads, head_dim, eps, _stream(stream)))
+
+
+def attention(qkv, out, num_heads, head_dim, stream=None):
+    """out[:, :H*Dh] <- softmax(q k^T / sqrt(Dh)) v per head; q, k, v from qkv."""
+    _need(qkv, BF16, "qkv", 2)
+    _need(out, BF16, "out", 2)
+    S = qkv.shape[0]
+    if qkv.shape[1] != 3 * num_heads * head_dim or out.shape[0] != S:
+        raise ValueError("shape mismatch")
+    _check(_lib.dit_attention(_p(qkv), _p(out), S, num_heads, head_dim, out.shape[1], _stream(stream)))
+    return out
+
+
+def linear2_gated_residual(cat, w2, b2, x, gate, y, stream=None):
+    """y <- x + gate * (cat W2^T + b2)."""
+    for t, n in ((cat, "cat"), (w2, "w2"), (x, "x"), (y, "y")):
+        _need(t, BF16, n, 2)
+    _need(gate, F32T, "gate", 1)
+    if b2 is not None:
+        _need(b2, BF16, "b2", 1)
+    S, n2 = cat.shape
+    d = x.shape[1]
+    if w2.shape != (d, n2) or x.shape != (S, d) or y.shape != (S, d) or gate.numel() != d:
+        raise ValueError("shape mismatch")
+    _check(_lib.dit_linear2_gated_residual(_p(cat), _p(w2), _p(b2), _p(x), _p(gate), _p(y),
+                                           S, d, n2 - d, _stream(stream)))
+    return y
+
+
+def rope_table(positions, axes_dims, head_dim, base=10000.0, stream=None):
+    """cos/sin [S, head_dim/2] fp32 from integer positions [S, n_axes] (int32, on the GPU)."""
+    _need(positions, I32T, "positions", 2)
+    S, n_axes = positions.shape
+    dims = (ctypes.c_int32 * len(axes_dims))(*axes_dims)
+    if len(axes_dims) != n_axes:
+        raise ValueError("one axis dim per position column")
+    c = torch.empty(S, head_dim // 2, dtype=F32T, device=positions.device)
+    s = torch.empty_like(c)
+    _check(_lib.dit_rope_table(_p(positions), S, n_axes, ctypes.cast(dims, VP), head_dim, base,
+                               _p(c), _p(s), _stream(stream)))
+    return c, s
+
+
+# --------------------------------------------------------------------- block
+def make_config(seq_len, dim, num_heads, head_dim, mlp_hidden, temb_dim=0, ln_eps=1e-6, qk_eps=1e-6, flags=0):
+    return BlockConfig(seq_len, dim, num_heads, head_dim, mlp_hidden, temb_dim, ln_eps, qk_eps, flags)
+
+
+class BlockWeights:
+    """Device weights of one block (holds the tensors alive) and their C view."""
+
+    def __init__(self, w_mod, b_mod, w1, b1, w2, b2, q_norm_w, k_norm_w):
+        for t, n in ((w_mod, "w_mod"), (w1, "w1"), (w2, "w2")):
+            _need(t, BF16, n, 2)
+        for t, n in ((b_mod, "b_mod"), (b1, "b1"), (b2, "b2")):
+            if t is not None:
+                _need(t, BF16, n, 1)
+        _need(q_norm_w, F32T, "q_norm_w", 1)
+        _need(k_norm_w, F32T, "k_norm_w", 1)
+        self.tensors = (w_mod, b_mod, w1, b1, w2, b2, q_norm_w, k_norm_w)
+        self.c = BlockWeightsC(*[None if t is None else t.data_ptr() for t in self.tensors])
+
+
+def block_workspace_bytes(cfg: BlockConfig) -> int:
+    return int(_lib.dit_block_workspace_bytes(ctypes.byref(cfg)))
+
+
+def stack_workspace_bytes(cfg: BlockConfig) -> int:
+    return int(_lib.dit_stack_workspace_bytes(ctypes.byref(cfg)))
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def block_forward(cfg, weights: BlockWeights, x, temb, rope_cos, rope_sin, y=None, workspace=None, stream=None):
+    """One block forward on the current stream; y may be x (in place)."""
+    _need(x, BF16, "x", 2)
+    _need(temb, BF16, "temb", 1)
+    _need(rope_cos, F32T, "rope_cos", 2)
+    _need(rope_sin, F32T, "rope_sin", 2)
+    y = torch.empty_like(x) if y is None else y
+    _need(y, BF16, "y", 2)
+    if x.shape != (cfg.seq_len, cfg.dim) or y.shape != x.shape:
+        raise ValueError("x / y shape does not match the config")
+    if workspace is None:
+        workspace = alloc_workspace(block_workspace_bytes(cfg), x.device)
+    _check(_lib.dit_block_forward(ctypes.byref(cfg), ctypes.byref(weights.c), _p(x), _p(temb), _p(rope_cos),
+                                  _p(rope_sin), _p(y), _p(workspace), workspace.numel(), _stream(stream)))
+    return y
+
+
+class Stack:
+    """A block stack captured once as a hipGraph and replayed per denoising step."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(_lib.dit_stack_create(ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            _lib.dit_stack_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def replay(self, cfg, blocks, x_in, temb_steps, rope_cos, rope_sin, out, workspace, stream=None):
+        _need(x_in, BF16, "x_in", 2)
+        _need(temb_steps, BF16, "temb_steps", 2)
+        _need(out, BF16, "out", 3)
+        _need(workspace, torch.uint8, "workspace", 1)
+        n_steps = temb_steps.shape[0]
+        if out.shape != (n_steps, cfg.seq_len, cfg.dim):
+            raise ValueError("out must be [n_steps, S, d]")
+        arr = (BlockWeightsC * len(blocks))(*[b.c for b in blocks])
+        self._keep = (blocks, arr)
+        _check(_lib.dit_stack_replay(self.handle, ctypes.byref(cfg), ctypes.cast(arr, VP), len(blocks), _p(x_in),
+                                     _p(temb_steps), n_steps, _p(rope_cos), _p(rope_sin), _p(out), _p(workspace),
+                                     workspace.numel(), _stream(stream)))
+        return out

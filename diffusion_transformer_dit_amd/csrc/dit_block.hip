@@ -1,0 +1,395 @@
+// C ABI of libdit_block: argument checks, the block schedule (six launches)
+// and the captured block stack.  Host code only; the kernels live in
+// elementwise.hip, gemm.hip and attention.hip.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dit_block.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  if (std::getenv("DIT_LOG")) std::fprintf(stderr, "[libdit_block] error %d: %s\n", code, buf);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DIT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define DIT_CHECK_HIP(expr, what)          \
+  do {                                     \
+    hipError_t _e = (expr);                \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+constexpr int64_t kMaxRowCols = 8192;  // row kernels keep a row in one wavefront's registers
+constexpr int64_t kMaxInt = 0x7fffffff;
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int check_rows_cols(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0) return fail(DIT_ERR_INVALID_ARG, "rows=%lld cols=%lld", (long long)rows, (long long)cols);
+  if (cols % 8 != 0 || cols > kMaxRowCols)
+    return fail(DIT_ERR_UNSUPPORTED, "cols=%lld must be a multiple of 8 and <= %lld", (long long)cols, (long long)kMaxRowCols);
+  if (rows > kMaxInt || rows * cols > (int64_t(1) << 40)) return fail(DIT_ERR_UNSUPPORTED, "rows=%lld too large", (long long)rows);
+  return DIT_OK;
+}
+
+// dims shared by the whole-block paths
+struct Dims {
+  int S, d, H, Dh, mlp, tdim;
+};
+
+int check_dims(int64_t S, int64_t d, int64_t H, int64_t Dh, int64_t mlp, int64_t tdim) {
+  if (S < 0 || d <= 0 || H <= 0 || Dh <= 0 || mlp <= 0 || tdim <= 0)
+    return fail(DIT_ERR_INVALID_ARG, "bad dims S=%lld d=%lld H=%lld Dh=%lld mlp=%lld temb=%lld",
+                (long long)S, (long long)d, (long long)H, (long long)Dh, (long long)mlp, (long long)tdim);
+  if (Dh != 64 && Dh != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim=%lld not in {64,128}", (long long)Dh);
+  if (H * Dh != d) return fail(DIT_ERR_INVALID_ARG, "num_heads*head_dim=%lld != dim=%lld", (long long)(H * Dh), (long long)d);
+  if (d % 64 != 0 || d > kMaxRowCols) return fail(DIT_ERR_UNSUPPORTED, "dim=%lld must be a multiple of 64 and <= 8192", (long long)d);
+  if (mlp % 64 != 0 || mlp > (int64_t(1) << 20)) return fail(DIT_ERR_UNSUPPORTED, "mlp_hidden=%lld must be a multiple of 64", (long long)mlp);
+  if (tdim % 8 != 0 || tdim > kMaxRowCols) return fail(DIT_ERR_UNSUPPORTED, "temb_dim=%lld must be a multiple of 8 and <= 8192", (long long)tdim);
+  if (S > (1 << 24)) return fail(DIT_ERR_UNSUPPORTED, "seq_len=%lld too large", (long long)S);
+  return DIT_OK;
+}
+
+int dims_of(const dit_block_config* cfg, Dims* out) {
+  if (!cfg) return fail(DIT_ERR_INVALID_ARG, "cfg is NULL");
+  const int tdim = cfg->temb_dim ? cfg->temb_dim : cfg->dim;
+  int rc = check_dims(cfg->seq_len, cfg->dim, cfg->num_heads, cfg->head_dim, cfg->mlp_hidden, tdim);
+  if (rc) return rc;
+  if (!(cfg->ln_eps >= 0.f) || !(cfg->qk_eps >= 0.f)) return fail(DIT_ERR_INVALID_ARG, "eps must be >= 0");
+  *out = Dims{cfg->seq_len, cfg->dim, cfg->num_heads, cfg->head_dim, cfg->mlp_hidden, tdim};
+  return DIT_OK;
+}
+
+int check_weights(const dit_block_weights* w) {
+  if (!w) return fail(DIT_ERR_INVALID_ARG, "weights is NULL");
+  if (!w->w_mod || !w->w1 || !w->w2 || !w->q_norm_w || !w->k_norm_w)
+    return fail(DIT_ERR_INVALID_ARG, "a required weight pointer is NULL");
+  return DIT_OK;
+}
+
+struct WsLayout {
+  size_t mod, u, qkv, cat, block_end, xbuf, tbuf, stack_end;
+};
+
+WsLayout layout(const Dims& D) {
+  WsLayout L;
+  size_t o = 0;
+  L.mod = o; o = align256(o + size_t(3) * D.d * sizeof(float));
+  L.u = o;   o = align256(o + size_t(D.S) * D.d * 2);
+  L.qkv = o; o = align256(o + size_t(D.S) * 3 * D.d * 2);
+  L.cat = o; o = align256(o + size_t(D.S) * (D.d + D.mlp) * 2);
+  L.block_end = o;
+  L.xbuf = o; o = align256(o + size_t(D.S) * D.d * 2);
+  L.tbuf = o; o = align256(o + size_t(D.tdim) * 2);
+  L.stack_end = o;
+  return L;
+}
+
+// The six launches of one block on `st`.  x and y may alias.
+int enqueue_block(const Dims& D, const dit_block_config* cfg, const dit_block_weights* w,
+                  const dit_bf16* x, const dit_bf16* temb, const float* rcos, const float* rsin,
+                  dit_bf16* y, unsigned char* ws, hipStream_t st) {
+  const WsLayout L = layout(D);
+  float* mod = reinterpret_cast<float*>(ws + L.mod);
+  dit_bf16* u = reinterpret_cast<dit_bf16*>(ws + L.u);
+  dit_bf16* qkv = reinterpret_cast<dit_bf16*>(ws + L.qkv);
+  dit_bf16* cat = reinterpret_cast<dit_bf16*>(ws + L.cat);
+  DIT_CHECK_HIP(dit::launch_modulation(temb, w->w_mod, w->b_mod, mod, 3 * D.d, D.tdim, st), "modulation");
+  if (D.S == 0) return DIT_OK;
+  DIT_CHECK_HIP(dit::launch_modulate_norm(x, mod, mod + D.d, u, D.S, D.d, cfg->ln_eps, st), "modulate_norm");
+  DIT_CHECK_HIP(dit::launch_linear1(u, w->w1, w->b1, qkv, cat, D.S, D.d, D.mlp, st), "linear1");
+  DIT_CHECK_HIP(dit::launch_qk_rmsnorm_rope(qkv, w->q_norm_w, w->k_norm_w, rcos, rsin, D.S, D.H, D.Dh,
+                                            cfg->qk_eps, st), "qk_rmsnorm_rope");
+  DIT_CHECK_HIP(dit::launch_attention(qkv, cat, D.S, D.H, D.Dh, D.d + D.mlp, st), "attention");
+  DIT_CHECK_HIP(dit::launch_linear2(cat, w->w2, w->b2, x, mod + 2 * D.d, y, D.S, D.d, D.mlp, st), "linear2");
+  return DIT_OK;
+}
+
+int check_linear(int64_t S, int64_t d, int64_t mlp) {
+  if (S < 0 || d <= 0 || mlp <= 0)
+    return fail(DIT_ERR_INVALID_ARG, "seq_len=%lld dim=%lld mlp_hidden=%lld", (long long)S, (long long)d, (long long)mlp);
+  if (d % 64 != 0 || mlp % 64 != 0 || d > kMaxRowCols || mlp > (int64_t(1) << 20) || S > (1 << 24))
+    return fail(DIT_ERR_UNSUPPORTED, "dim=%lld and mlp_hidden=%lld must be multiples of 64 (dim <= 8192)",
+                (long long)d, (long long)mlp);
+  return DIT_OK;
+}
+
+int check_not_capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(st, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone) return fail(DIT_ERR_CAPTURE, "stream is capturing");
+  return DIT_OK;
+}
+
+}  // namespace
+
+// ============================================================== single steps
+extern "C" int dit_modulation(const dit_bf16* temb, const dit_bf16* w_mod, const dit_bf16* b_mod,
+                              float* mod, int64_t dim, int64_t temb_dim, void* stream) {
+  if (!temb || !w_mod || !mod) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if (dim <= 0 || temb_dim <= 0) return fail(DIT_ERR_INVALID_ARG, "dim=%lld temb_dim=%lld", (long long)dim, (long long)temb_dim);
+  if (temb_dim % 8 != 0 || temb_dim > kMaxRowCols) return fail(DIT_ERR_UNSUPPORTED, "temb_dim=%lld", (long long)temb_dim);
+  if (3 * dim > kMaxInt) return fail(DIT_ERR_UNSUPPORTED, "dim too large");
+  DIT_CHECK_HIP(dit::launch_modulation(temb, w_mod, b_mod, mod, int(3 * dim), int(temb_dim), as_stream(stream)), "modulation");
+  return DIT_OK;
+}
+
+extern "C" int dit_modulate_norm(const dit_bf16* x, const float* shift, const float* scale, dit_bf16* out,
+                                 int64_t rows, int64_t cols, float eps, void* stream) {
+  if (!x || !shift || !scale || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  int rc = check_rows_cols(rows, cols);
+  if (rc) return rc;
+  if (!(eps >= 0.f)) return fail(DIT_ERR_INVALID_ARG, "eps must be >= 0");
+  DIT_CHECK_HIP(dit::launch_modulate_norm(x, shift, scale, out, int(rows), int(cols), eps, as_stream(stream)), "modulate_norm");
+  return DIT_OK;
+}
+
+extern "C" int dit_gated_residual(const dit_bf16* x, const dit_bf16* h, const float* gate, dit_bf16* y,
+                                  int64_t rows, int64_t cols, void* stream) {
+  if (!x || !h || !gate || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  int rc = check_rows_cols(rows, cols);
+  if (rc) return rc;
+  DIT_CHECK_HIP(dit::launch_gated_residual(x, h, gate, y, int(rows), int(cols), as_stream(stream)), "gated_residual");
+  return DIT_OK;
+}
+
+extern "C" int dit_linear1_gelu(const dit_bf16* u, const dit_bf16* w1, const dit_bf16* b1, dit_bf16* qkv,
+                                dit_bf16* cat, int64_t seq_len, int64_t dim, int64_t mlp_hidden, void* stream) {
+  if (!u || !w1 || !qkv || !cat) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  int rc = check_linear(seq_len, dim, mlp_hidden);
+  if (rc) return rc;
+  DIT_CHECK_HIP(dit::launch_linear1(u, w1, b1, qkv, cat, int(seq_len), int(dim), int(mlp_hidden), as_stream(stream)), "linear1");
+  return DIT_OK;
+}
+
+extern "C" int dit_qk_rmsnorm_rope(dit_bf16* qkv, const float* q_norm_w, const float* k_norm_w,
+                                   const float* rope_cos, const float* rope_sin, int64_t seq_len,
+                                   int64_t num_heads, int64_t head_dim, float eps, void* stream) {
+  if (!qkv || !q_norm_w || !k_norm_w || !rope_cos || !rope_sin) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  int rc = check_dims(seq_len, num_heads * head_dim, num_heads, head_dim, 64, 8);
+  if (rc) return rc;
+  if (!(eps >= 0.f)) return fail(DIT_ERR_INVALID_ARG, "eps must be >= 0");
+  DIT_CHECK_HIP(dit::launch_qk_rmsnorm_rope(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, int(seq_len),
+                                            int(num_heads), int(head_dim), eps, as_stream(stream)), "qk_rmsnorm_rope");
+  return DIT_OK;
+}
+
+extern "C" int dit_attention(const dit_bf16* qkv, dit_bf16* out, int64_t seq_len, int64_t num_heads,
+                             int64_t head_dim, int64_t ld_out, void* stream) {
+  if (!qkv || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  int rc = check_dims(seq_len, num_heads * head_dim, num_heads, head_dim, 64, 8);
+  if (rc) return rc;
+  if (ld_out < num_heads * head_dim || ld_out % 4 != 0 || ld_out > kMaxInt)
+    return fail(DIT_ERR_INVALID_ARG, "ld_out=%lld must be >= H*Dh and a multiple of 4", (long long)ld_out);
+  DIT_CHECK_HIP(dit::launch_attention(qkv, out, int(seq_len), int(num_heads), int(head_dim), int(ld_out),
+                                      as_stream(stream)), "attention");
+  return DIT_OK;
+}
+
+extern "C" int dit_linear2_gated_residual(const dit_bf16* cat, const dit_bf16* w2, const dit_bf16* b2,
+                                          const dit_bf16* x, const float* gate, dit_bf16* y, int64_t seq_len,
+                                          int64_t dim, int64_t mlp_hidden, void* stream) {
+  if (!cat || !w2 || !x || !gate || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  int rc = check_linear(seq_len, dim, mlp_hidden);
+  if (rc) return rc;
+  DIT_CHECK_HIP(dit::launch_linear2(cat, w2, b2, x, gate, y, int(seq_len), int(dim), int(mlp_hidden),
+                                    as_stream(stream)), "linear2");
+  return DIT_OK;
+}
+
+extern "C" int dit_rope_table(const int32_t* positions, int64_t seq_len, int32_t n_axes, const int32_t* axes_dims,
+                              int64_t head_dim, float base, float* rope_cos, float* rope_sin, void* stream) {
+  if (!positions || !axes_dims || !rope_cos || !rope_sin) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if (seq_len < 0 || seq_len > (1 << 24)) return fail(DIT_ERR_INVALID_ARG, "seq_len=%lld", (long long)seq_len);
+  if (n_axes < 1 || n_axes > 8) return fail(DIT_ERR_INVALID_ARG, "n_axes=%d not in [1,8]", n_axes);
+  if (head_dim <= 0 || head_dim % 8 != 0 || head_dim > 1024) return fail(DIT_ERR_INVALID_ARG, "head_dim=%lld", (long long)head_dim);
+  if (!(base > 1.0f)) return fail(DIT_ERR_INVALID_ARG, "base must be > 1");
+  int64_t sum = 0;
+  for (int a = 0; a < n_axes; ++a) {
+    if (axes_dims[a] <= 0 || axes_dims[a] % 2 != 0) return fail(DIT_ERR_INVALID_ARG, "axes_dims[%d]=%d must be even and > 0", a, axes_dims[a]);
+    sum += axes_dims[a];
+  }
+  if (sum != head_dim) return fail(DIT_ERR_INVALID_ARG, "axes_dims sum to %lld, head_dim is %lld", (long long)sum, (long long)head_dim);
+  DIT_CHECK_HIP(dit::launch_rope_table(positions, int(seq_len), n_axes, axes_dims, int(head_dim), base, rope_cos,
+                                       rope_sin, as_stream(stream)), "rope_table");
+  return DIT_OK;
+}
+
+// ============================================================== whole block
+extern "C" size_t dit_block_workspace_bytes(const dit_block_config* cfg) {
+  Dims D;
+  if (dims_of(cfg, &D)) return 0;
+  return layout(D).block_end;
+}
+
+extern "C" int dit_block_forward(const dit_block_config* cfg, const dit_block_weights* w, const dit_bf16* x,
+                                 const dit_bf16* temb, const float* rope_cos, const float* rope_sin, dit_bf16* y,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  Dims D;
+  int rc = dims_of(cfg, &D);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (!x || !temb || !rope_cos || !rope_sin || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  const WsLayout L = layout(D);
+  if (!workspace || ws_bytes < L.block_end)
+    return fail(DIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.block_end);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(DIT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return enqueue_block(D, cfg, w, x, temb, rope_cos, rope_sin, y, static_cast<unsigned char*>(workspace),
+                       as_stream(stream));
+}
+
+// ============================================================== block stack
+struct dit_stack {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipStream_t cap = nullptr;
+  std::vector<uintptr_t> key;
+};
+
+namespace {
+std::vector<uintptr_t> make_key(const dit_block_config* cfg, const dit_block_weights* blocks, int n_blocks,
+                                const dit_bf16* x_in, const float* rcos, const float* rsin, void* ws,
+                                size_t ws_bytes) {
+  std::vector<uintptr_t> k;
+  k.push_back(uintptr_t(cfg->seq_len));
+  k.push_back(uintptr_t(cfg->dim));
+  k.push_back(uintptr_t(cfg->num_heads));
+  k.push_back(uintptr_t(cfg->head_dim));
+  k.push_back(uintptr_t(cfg->mlp_hidden));
+  k.push_back(uintptr_t(cfg->temb_dim));
+  uint32_t e1, e2;
+  std::memcpy(&e1, &cfg->ln_eps, 4);
+  std::memcpy(&e2, &cfg->qk_eps, 4);
+  k.push_back(e1);
+  k.push_back(e2);
+  k.push_back(cfg->flags);
+  k.push_back(uintptr_t(n_blocks));
+  k.push_back(uintptr_t(x_in));
+  k.push_back(uintptr_t(rcos));
+  k.push_back(uintptr_t(rsin));
+  k.push_back(uintptr_t(ws));
+  k.push_back(uintptr_t(ws_bytes));
+  for (int b = 0; b < n_blocks; ++b) {
+    const dit_block_weights& w = blocks[b];
+    for (const void* p : {(const void*)w.w_mod, (const void*)w.b_mod, (const void*)w.w1, (const void*)w.b1,
+                          (const void*)w.w2, (const void*)w.b2, (const void*)w.q_norm_w, (const void*)w.k_norm_w})
+      k.push_back(uintptr_t(p));
+  }
+  return k;
+}
+}  // namespace
+
+extern "C" int dit_stack_create(dit_stack** out) {
+  if (!out) return fail(DIT_ERR_INVALID_ARG, "out is NULL");
+  *out = new (std::nothrow) dit_stack();
+  if (!*out) return fail(DIT_ERR_INVALID_ARG, "out of host memory");
+  return DIT_OK;
+}
+
+extern "C" int dit_stack_destroy(dit_stack* st) {
+  if (!st) return DIT_OK;
+  if (st->exec) hipGraphExecDestroy(st->exec);
+  if (st->graph) hipGraphDestroy(st->graph);
+  if (st->cap) hipStreamDestroy(st->cap);
+  delete st;
+  return DIT_OK;
+}
+
+extern "C" size_t dit_stack_workspace_bytes(const dit_block_config* cfg) {
+  Dims D;
+  if (dims_of(cfg, &D)) return 0;
+  return layout(D).stack_end;
+}
+
+extern "C" int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks,
+                                int n_blocks, const dit_bf16* x_in, const dit_bf16* temb_steps, int n_steps,
+                                const float* rope_cos, const float* rope_sin, dit_bf16* out, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  if (!st) return fail(DIT_ERR_INVALID_ARG, "stack is NULL");
+  Dims D;
+  int rc = dims_of(cfg, &D);
+  if (rc) return rc;
+  if (!blocks || n_blocks <= 0) return fail(DIT_ERR_INVALID_ARG, "n_blocks=%d", n_blocks);
+  if (n_steps < 0) return fail(DIT_ERR_INVALID_ARG, "n_steps=%d", n_steps);
+  for (int b = 0; b < n_blocks; ++b)
+    if ((rc = check_weights(&blocks[b]))) return rc;
+  if (!x_in || !temb_steps || !rope_cos || !rope_sin || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  const WsLayout L = layout(D);
+  if (!workspace || ws_bytes < L.stack_end)
+    return fail(DIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.stack_end);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(DIT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t s = as_stream(stream);
+  if ((rc = check_not_capturing(s))) return rc;
+
+  const bool chain = (cfg->flags & DIT_STACK_CHAIN) != 0;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  dit_bf16* xbuf = reinterpret_cast<dit_bf16*>(ws + L.xbuf);
+  dit_bf16* tbuf = reinterpret_cast<dit_bf16*>(ws + L.tbuf);
+  const size_t act_bytes = size_t(D.S) * D.d * 2;
+
+  std::vector<uintptr_t> key = make_key(cfg, blocks, n_blocks, x_in, rope_cos, rope_sin, workspace, ws_bytes);
+  if (st->exec && key != st->key)
+    return fail(DIT_ERR_GRAPH_KEY, "stack was captured for another config / pointer set; destroy and re-create it");
+  if (!st->exec) {
+    dit::prepare_device();  // device queries happen before capture
+    if (!st->cap) DIT_CHECK_HIP(hipStreamCreateWithFlags(&st->cap, hipStreamNonBlocking), "hipStreamCreate");
+    DIT_CHECK_HIP(hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
+    int brc = DIT_OK;
+    for (int b = 0; b < n_blocks && brc == DIT_OK; ++b) {
+      const dit_bf16* xin = (b == 0 && !chain) ? x_in : xbuf;
+      brc = enqueue_block(D, cfg, &blocks[b], xin, tbuf, rope_cos, rope_sin, xbuf, ws, st->cap);
+    }
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(st->cap, &g);
+    if (brc != DIT_OK) {
+      if (g) hipGraphDestroy(g);
+      return brc;
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+    hipGraphExec_t ex = nullptr;
+    e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+      hipGraphDestroy(g);
+      return hip_fail(e, "hipGraphInstantiate");
+    }
+    st->graph = g;
+    st->exec = ex;
+    st->key = key;
+  }
+  for (int step = 0; step < n_steps; ++step) {
+    if (chain && step == 0)
+      DIT_CHECK_HIP(hipMemcpyAsync(xbuf, x_in, act_bytes, hipMemcpyDeviceToDevice, s), "copy x_in");
+    DIT_CHECK_HIP(hipMemcpyAsync(tbuf, temb_steps + size_t(step) * D.tdim, size_t(D.tdim) * 2,
+                                 hipMemcpyDeviceToDevice, s), "copy temb");
+    DIT_CHECK_HIP(hipGraphLaunch(st->exec, s), "hipGraphLaunch");
+    DIT_CHECK_HIP(hipMemcpyAsync(out + size_t(step) * D.S * D.d, xbuf, act_bytes, hipMemcpyDeviceToDevice, s),
+                  "copy out");
+  }
+  return DIT_OK;
+}
+
+// ============================================================== diagnostics
+extern "C" const char* dit_last_error(void) { return g_err.c_str(); }
+extern "C" const char* dit_version(void) { return "libdit_block 0.1.0 (gfx950)"; }

@@ -1,0 +1,76 @@
+// Device-side helpers shared by the gfx950 kernels of libdit_block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest, ties to even
+// (inputs here are finite).
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+__device__ __forceinline__ uint32_t f2bf_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f2bf_bits(lo) | (f2bf_bits(hi) << 16);
+}
+
+// 8 bf16 held in a 16-byte vector -> 8 floats
+__device__ __forceinline__ void unpack8(const u32x4& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf_lo(v[i]);
+    f[2 * i + 1] = bf_hi(v[i]);
+  }
+}
+__device__ __forceinline__ u32x4 pack8(const float* f) {
+  u32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = pack_bf2(f[2 * i], f[2 * i + 1]);
+  return v;
+}
+
+// Sum / max over the 64 lanes of a wavefront (butterfly; every lane gets the result).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = width / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Fast transcendental building blocks on the hardware instructions.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// GELU, tanh form: 0.5 g (1 + tanh(u)) with u = sqrt(2/pi) (g + 0.044715 g^3).
+// Since 0.5 (1 + tanh(u)) = 1 / (1 + e^{-2u}), this is g / (1 + 2^{-2u log2 e}).
+__device__ __forceinline__ float gelu_tanh(float g) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  float u = c * (g + 0.044715f * g * g * g);
+  return g * rcp_fast(1.0f + exp2_fast(-2.0f * kLog2e * u));
+}
+
+__device__ __forceinline__ float silu(float z) { return z * rcp_fast(1.0f + exp2_fast(-kLog2e * z)); }
+
+}  // namespace dit

@@ -1,0 +1,379 @@
+// Memory-bound kernels of the single-stream block, for gfx950:
+//   modulation GEMV (SiLU(temb) -> shift | scale | gate),
+//   fused LayerNorm + adaLN modulate, gated residual,
+//   per-head QK RMSNorm + RoPE, RoPE cos/sin tables.
+// These are the "cast / modulate / norm" HBM round trips between the GEMMs
+// that the Flux page (ChituDiffusion, section 2) finds in the eager trace and
+// that its section 1.1 fuses; here each is one pass over HBM with 16-byte
+// loads and stores and wavefront-reduced row statistics in fp32.
+#include <cmath>
+
+#include "dit_common.hpp"
+#include "launch.hpp"
+
+namespace dit {
+
+// ------------------------------------------------------------------------
+// Row kernels: one wavefront per row, each lane owning NCH 16-byte chunks
+// (8 bf16) at chunk index lane + 64*j.  A wave walks `rows_per_wave` rows and
+// keeps the per-column vectors (modulation / gate) in registers across them;
+// the next row's loads are issued before the current row is finished.
+// ------------------------------------------------------------------------
+template <int NCH>
+__global__ void __launch_bounds__(256)
+ln_modulate_kernel(const bf16_t* __restrict__ x, const float* __restrict__ shift,
+                   const float* __restrict__ scale, bf16_t* __restrict__ out,
+                   int rows, int cols, int rows_per_wave, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int nchunk = cols >> 3;
+  const int r0 = wave * rows_per_wave;
+  if (r0 >= rows) return;
+  const int r1 = min(rows, r0 + rows_per_wave);
+
+  float sc[NCH][8], sh[NCH][8];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = lane + 64 * j;
+    if (c < nchunk) {
+      const f32x4* ps = reinterpret_cast<const f32x4*>(scale + 8 * c);
+      const f32x4* pt = reinterpret_cast<const f32x4*>(shift + 8 * c);
+      f32x4 s0 = ps[0], s1 = ps[1], t0 = pt[0], t1 = pt[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[j][e] = 1.0f + s0[e];
+        sc[j][4 + e] = 1.0f + s1[e];
+        sh[j][e] = t0[e];
+        sh[j][4 + e] = t1[e];
+      }
+    }
+  }
+  const float inv_n = 1.0f / float(cols);
+
+  u32x4 cur[NCH], nxt[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = lane + 64 * j;
+    if (c < nchunk) cur[j] = reinterpret_cast<const u32x4*>(x + size_t(r0) * cols)[c];
+  }
+  for (int r = r0; r < r1; ++r) {
+    if (r + 1 < r1) {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nchunk) nxt[j] = reinterpret_cast<const u32x4*>(x + size_t(r + 1) * cols)[c];
+      }
+    }
+    float v[NCH][8];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) {
+        unpack8(cur[j], v[j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += v[j][e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+      }
+    }
+    const float mean = wave_sum(s) * inv_n;
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float dlt = v[j][e] - mean;
+          q += dlt * dlt;
+        }
+      }
+    }
+    const float var = wave_sum(q) * inv_n;
+    const float rstd = __frsqrt_rn(var + eps);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (v[j][e] - mean) * rstd * sc[j][e] + sh[j][e];
+        reinterpret_cast<u32x4*>(out + size_t(r) * cols)[c] = pack8(o);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) cur[j] = nxt[j];
+  }
+}
+
+template <int NCH>
+__global__ void __launch_bounds__(256)
+gated_residual_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ h,
+                      const float* __restrict__ gate, bf16_t* __restrict__ y, int rows,
+                      int cols, int rows_per_wave) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int nchunk = cols >> 3;
+  const int r0 = wave * rows_per_wave;
+  if (r0 >= rows) return;
+  const int r1 = min(rows, r0 + rows_per_wave);
+
+  float g[NCH][8];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = lane + 64 * j;
+    if (c < nchunk) {
+      const f32x4* pg = reinterpret_cast<const f32x4*>(gate + 8 * c);
+      f32x4 g0 = pg[0], g1 = pg[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        g[j][e] = g0[e];
+        g[j][4 + e] = g1[e];
+      }
+    }
+  }
+  for (int r = r0; r < r1; ++r) {
+    u32x4 xv[NCH], hv[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) {
+        xv[j] = reinterpret_cast<const u32x4*>(x + size_t(r) * cols)[c];
+        hv[j] = reinterpret_cast<const u32x4*>(h + size_t(r) * cols)[c];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) {
+        float a[8], b[8], o[8];
+        unpack8(xv[j], a);
+        unpack8(hv[j], b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = a[e] + g[j][e] * b[e];
+        reinterpret_cast<u32x4*>(y + size_t(r) * cols)[c] = pack8(o);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Modulation GEMV: mod[r] = sum_c W[r, c] * SiLU(temb[c]) + b[r].
+// SiLU(temb) is computed once per workgroup into LDS; each wave then streams
+// `rows_per_wave` rows of W with 16-byte loads and reduces across the wave.
+// ------------------------------------------------------------------------
+template <int NCH>
+__global__ void __launch_bounds__(256)
+mod_gemv_kernel(const bf16_t* __restrict__ temb, const bf16_t* __restrict__ w,
+                const bf16_t* __restrict__ b, float* __restrict__ mod, int rows, int cols,
+                int rows_per_wave) {
+  __shared__ __attribute__((aligned(16))) float s_act[NCH * 512];
+  const int nchunk = cols >> 3;
+  for (int i = threadIdx.x; i < cols; i += blockDim.x) s_act[i] = silu(bf2f(temb[i]));
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int r0 = wave * rows_per_wave;
+  if (r0 >= rows) return;
+  const int r1 = min(rows, r0 + rows_per_wave);
+  for (int r = r0; r < r1; ++r) {
+    u32x4 wv[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) wv[j] = reinterpret_cast<const u32x4*>(w + size_t(r) * cols)[c];
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) {
+        float f[8];
+        unpack8(wv[j], f);
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(&s_act[8 * c]);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(&s_act[8 * c + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc += f[e] * a0[e];
+          acc += f[4 + e] * a1[e];
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) mod[r] = acc + (b ? bf2f(b[r]) : 0.f);
+  }
+}
+
+// ------------------------------------------------------------------------
+// Per-head QK RMSNorm + RoPE, in place.  One thread owns 8 consecutive dims
+// (4 rotation pairs) of one (token, q|k, head) row; the DH/8 threads of a row
+// reduce the sum of squares with lane shuffles.
+// ------------------------------------------------------------------------
+template <int DH>
+__global__ void __launch_bounds__(256)
+qk_rmsnorm_rope_kernel(bf16_t* __restrict__ qkv, const float* __restrict__ qw,
+                       const float* __restrict__ kw, const float* __restrict__ rcos,
+                       const float* __restrict__ rsin, int S, int H, float eps) {
+  constexpr int TPR = DH / 8;  // threads per head row
+  const int d = H * DH;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long nthreads = (long long)S * 2 * H * TPR;
+  // Rows never straddle a wave (TPR divides 64), so inactive lanes are whole rows.
+  const bool active = gid < nthreads;
+  const long long g = active ? gid : 0;
+  const int part = int(g % TPR);  // chunk inside the head row
+  const long long row = g / TPR;  // (token, q|k, head)
+  const int head = int(row % H);
+  const int qk = int((row / H) % 2);
+  const int t = int(row / (2 * H));
+  bf16_t* p = qkv + (size_t)t * 3 * d + qk * d + head * DH + part * 8;
+  u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  float f[8];
+  unpack8(v, f);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+  ss = group_sum<TPR>(ss);
+  const float rs = __frsqrt_rn(ss * (1.0f / DH) + eps);
+  const float* w = (qk == 0 ? qw : kw) + part * 8;
+  const f32x4 w0 = *reinterpret_cast<const f32x4*>(w);
+  const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + 4);
+  const f32x4 c4 = *reinterpret_cast<const f32x4*>(rcos + (size_t)t * (DH / 2) + part * 4);
+  const f32x4 s4 = *reinterpret_cast<const f32x4*>(rsin + (size_t)t * (DH / 2) + part * 4);
+  float n[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    n[e] = f[e] * rs * w0[e];
+    n[4 + e] = f[4 + e] * rs * w1[e];
+  }
+  float o[8];
+#pragma unroll
+  for (int pr = 0; pr < 4; ++pr) {
+    const float a = n[2 * pr], b = n[2 * pr + 1];
+    o[2 * pr] = a * c4[pr] - b * s4[pr];
+    o[2 * pr + 1] = a * s4[pr] + b * c4[pr];
+  }
+  if (active) *reinterpret_cast<u32x4*>(p) = pack8(o);
+}
+
+// ------------------------------------------------------------------------
+// RoPE tables: angle = pos[t, a] * base^(-2 j' / D_a) for pair j (axis a,
+// index j' inside the axis chunk of D_a dims).
+// ------------------------------------------------------------------------
+struct RopeAxes {
+  int n_axes;
+  int dims[8];
+};
+
+__global__ void rope_table_kernel(const int32_t* __restrict__ pos, RopeAxes ax, int S, int half,
+                                  float log2_base, float* __restrict__ rcos,
+                                  float* __restrict__ rsin) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)S * half) return;
+  const int t = int(i / half);
+  const int j = int(i % half);
+  int a = 0, start = 0;
+  while (a < ax.n_axes - 1 && j >= start + ax.dims[a] / 2) {
+    start += ax.dims[a] / 2;
+    ++a;
+  }
+  const int jp = j - start;
+  const float freq = exp2f(-(2.0f * float(jp) / float(ax.dims[a])) * log2_base);
+  const float ang = float(pos[(size_t)t * ax.n_axes + a]) * freq;
+  float s, c;
+  sincosf(ang, &s, &c);
+  rcos[i] = c;
+  rsin[i] = s;
+}
+
+// ------------------------------------------------------------------------ launchers
+static int rows_per_wave_for(int rows, int target_waves) {
+  int rpw = (rows + target_waves - 1) / target_waves;
+  return rpw < 1 ? 1 : rpw;
+}
+
+hipError_t launch_modulate_norm(const bf16_t* x, const float* shift, const float* scale,
+                                bf16_t* out, int rows, int cols, float eps, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const int nch = (cols / 8 + 63) / 64;
+  const int rpw = rows_per_wave_for(rows, 2048);
+  const int waves = (rows + rpw - 1) / rpw;
+  dim3 grid((waves + 3) / 4), block(256);
+  switch (nch) {
+#define CASE(N) \
+  case N: ln_modulate_kernel<N><<<grid, block, 0, st>>>(x, shift, scale, out, rows, cols, rpw, eps); break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8) CASE(9) CASE(10) CASE(11) CASE(12)
+    CASE(13) CASE(14) CASE(15) CASE(16)
+#undef CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gated_residual(const bf16_t* x, const bf16_t* h, const float* gate, bf16_t* y,
+                                 int rows, int cols, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const int nch = (cols / 8 + 63) / 64;
+  const int rpw = rows_per_wave_for(rows, 2048);
+  const int waves = (rows + rpw - 1) / rpw;
+  dim3 grid((waves + 3) / 4), block(256);
+  switch (nch) {
+#define CASE(N) \
+  case N: gated_residual_kernel<N><<<grid, block, 0, st>>>(x, h, gate, y, rows, cols, rpw); break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8) CASE(9) CASE(10) CASE(11) CASE(12)
+    CASE(13) CASE(14) CASE(15) CASE(16)
+#undef CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_modulation(const bf16_t* temb, const bf16_t* w, const bf16_t* b, float* mod,
+                             int rows, int cols, hipStream_t st) {
+  const int nch = (cols / 8 + 63) / 64;
+  const int rpw = rows_per_wave_for(rows, 4096);
+  const int waves = (rows + rpw - 1) / rpw;
+  dim3 grid((waves + 3) / 4), block(256);
+  switch (nch) {
+#define CASE(N) \
+  case N: mod_gemv_kernel<N><<<grid, block, 0, st>>>(temb, w, b, mod, rows, cols, rpw); break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8) CASE(9) CASE(10) CASE(11) CASE(12)
+    CASE(13) CASE(14) CASE(15) CASE(16)
+#undef CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_rmsnorm_rope(bf16_t* qkv, const float* qw, const float* kw, const float* rcos,
+                                  const float* rsin, int S, int H, int DH, float eps,
+                                  hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  const long long threads = (long long)S * 2 * H * (DH / 8);
+  dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (DH == 128)
+    qk_rmsnorm_rope_kernel<128><<<grid, block, 0, st>>>(qkv, qw, kw, rcos, rsin, S, H, eps);
+  else if (DH == 64)
+    qk_rmsnorm_rope_kernel<64><<<grid, block, 0, st>>>(qkv, qw, kw, rcos, rsin, S, H, eps);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const int32_t* pos, int S, int n_axes, const int32_t* axes_dims,
+                             int DH, float base, float* rcos, float* rsin, hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  RopeAxes ax;
+  ax.n_axes = n_axes;
+  for (int i = 0; i < 8; ++i) ax.dims[i] = i < n_axes ? axes_dims[i] : 0;
+  const int half = DH / 2;
+  const long long n = (long long)S * half;
+  const double l2b = std::log2((double)base);
+  rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(pos, ax, S, half, (float)l2b,
+                                                                 rcos, rsin);
+  return hipGetLastError();
+}
+
+}  // namespace dit

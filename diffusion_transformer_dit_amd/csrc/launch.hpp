@@ -1,0 +1,38 @@
+// Internal launch functions of libdit_block (one per kernel family).  Each
+// only enqueues on `st` and returns the launch status; callers validate the
+// arguments first.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+typedef uint16_t bf16_t;
+
+// Cache device properties used for launch shapes (call before a stream capture).
+void prepare_device();
+
+hipError_t launch_modulation(const bf16_t* temb, const bf16_t* w, const bf16_t* b, float* mod,
+                             int rows, int cols, hipStream_t st);
+hipError_t launch_modulate_norm(const bf16_t* x, const float* shift, const float* scale,
+                                bf16_t* out, int rows, int cols, float eps, hipStream_t st);
+hipError_t launch_gated_residual(const bf16_t* x, const bf16_t* h, const float* gate, bf16_t* y,
+                                 int rows, int cols, hipStream_t st);
+hipError_t launch_qk_rmsnorm_rope(bf16_t* qkv, const float* qw, const float* kw, const float* rcos,
+                                  const float* rsin, int S, int H, int DH, float eps,
+                                  hipStream_t st);
+hipError_t launch_rope_table(const int32_t* pos, int S, int n_axes, const int32_t* axes_dims,
+                             int DH, float base, float* rcos, float* rsin, hipStream_t st);
+
+// linear1: z = u W1^T + b1; cols < 3d -> qkv[S,3d]; cols >= 3d -> gelu -> cat[:, d + ...]
+hipError_t launch_linear1(const bf16_t* u, const bf16_t* w1, const bf16_t* b1, bf16_t* qkv,
+                          bf16_t* cat, int S, int d, int mlp, hipStream_t st);
+// linear2: y = x + gate * (cat W2^T + b2)
+hipError_t launch_linear2(const bf16_t* cat, const bf16_t* w2, const bf16_t* b2, const bf16_t* x,
+                          const float* gate, bf16_t* y, int S, int d, int mlp, hipStream_t st);
+// attention over qkv [S, 3*H*DH] -> out [S, ld_out] columns [0, H*DH)
+hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
+                            hipStream_t st);
+
+}  // namespace dit

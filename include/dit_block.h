@@ -1,0 +1,189 @@
+/*
+ * libdit_block -- forward pass of a Flux-style single-stream DiT block on
+ * AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The block is the one profiled on the page "ChituDiffusion: torch.compile
+ * and CUDA Graph on Flux.1-dev" (chenyy20.com), section 2: one Flux
+ * single-stream block, S = 4608 tokens, dim 3072, 24 heads x 128, bf16.
+ * Its memory-bound ops (LayerNorm, the adaLN modulation (1+scale)*x+shift,
+ * GELU, the gated residual) are the ones section 1.1 of that page fuses;
+ * the stack replay is the capture-once / replay-many scheme of sections
+ * 1.2-1.3 and 7 (fixed shapes, fixed addresses, static buffers).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers unless marked HOST.  Matrices are
+ *     row-major.  Activations are token-major [S, features] with heads in
+ *     contiguous column blocks; weights use the [out, in] layout.
+ *   - dit_bf16 holds raw bfloat16 bits.  Vectors marked float are fp32.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on `stream` and returns; none
+ *     synchronises the host, and none allocates device memory.  The caller
+ *     owns every buffer, the workspace and the stream.
+ *   - Every call returns DIT_OK (0) or an error code.  Arguments are checked
+ *     before any HIP call; on error nothing is enqueued and dit_last_error()
+ *     returns a message (thread-local).  HIP launch failures give DIT_ERR_HIP.
+ *   - Supported shapes: any seq_len >= 1 (ragged tails are handled);
+ *     dim % 64 == 0; head_dim in {64, 128} with num_heads*head_dim == dim;
+ *     mlp_hidden % 64 == 0; temb_dim % 8 == 0.  Others give
+ *     DIT_ERR_UNSUPPORTED.
+ */
+#ifndef DIT_BLOCK_H
+#define DIT_BLOCK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t dit_bf16;
+
+enum {
+  DIT_OK = 0,
+  DIT_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad config field */
+  DIT_ERR_UNSUPPORTED = 2,  /* shape outside the supported set */
+  DIT_ERR_WORKSPACE = 3,    /* workspace missing or too small */
+  DIT_ERR_HIP = 4,          /* a HIP runtime call failed */
+  DIT_ERR_CAPTURE = 5,      /* stream is capturing when the call may not be captured */
+  DIT_ERR_GRAPH_KEY = 6     /* stack replay with a different (config, pointers) key */
+};
+
+/* flags of dit_block_config */
+#define DIT_STACK_CHAIN 1u  /* step s+1 of a stack replay starts from step s's output */
+
+typedef struct {
+  int32_t seq_len;     /* S, tokens */
+  int32_t dim;         /* d, model width */
+  int32_t num_heads;   /* H */
+  int32_t head_dim;    /* Dh, H*Dh == d */
+  int32_t mlp_hidden;  /* width of the MLP branch */
+  int32_t temb_dim;    /* length of the conditioning vector (0 means d) */
+  float ln_eps;        /* LayerNorm epsilon, e.g. 1e-6 */
+  float qk_eps;        /* QK RMSNorm epsilon, e.g. 1e-6 */
+  uint32_t flags;      /* DIT_STACK_CHAIN */
+} dit_block_config;
+
+typedef struct {
+  const dit_bf16* w_mod;  /* [3d, temb_dim]  modulation linear (shift|scale|gate rows) */
+  const dit_bf16* b_mod;  /* [3d] or NULL */
+  const dit_bf16* w1;     /* [3d+mlp, d]     linear1, output columns q | k | v | mlp */
+  const dit_bf16* b1;     /* [3d+mlp] or NULL */
+  const dit_bf16* w2;     /* [d, d+mlp]      linear2, input columns attn_out | gelu(mlp) */
+  const dit_bf16* b2;     /* [d] or NULL */
+  const float* q_norm_w;  /* [head_dim]      RMSNorm weight of q, shared by heads */
+  const float* k_norm_w;  /* [head_dim]      RMSNorm weight of k */
+} dit_block_weights;
+
+/* ---- single steps of the block (each is one kernel launch) -------------- */
+
+/* Modulation GEMV (adaLN): mod = W_mod . SiLU(temb) + b_mod, fp32 [3*dim],
+ * laid out shift[dim] | scale[dim] | gate[dim].  SiLU(z) = z/(1+e^-z).
+ * temb [temb_dim] bf16; w_mod [3*dim, temb_dim] bf16; b_mod [3*dim] or NULL. */
+int dit_modulation(const dit_bf16* temb, const dit_bf16* w_mod, const dit_bf16* b_mod,
+                   float* mod, int64_t dim, int64_t temb_dim, void* stream);
+
+/* Fused LayerNorm + adaLN modulate (Flux page, section 1.1), one pass:
+ * out[r,:] = (x[r,:] - mean_r) / sqrt(var_r + eps) * (1 + scale) + shift.
+ * Row statistics in fp32, biased variance, no affine; one bf16 rounding at
+ * the store.  x, out [rows, cols] bf16 (out may equal x); shift, scale
+ * [cols] fp32.  cols % 8 == 0 and cols <= 8192. */
+int dit_modulate_norm(const dit_bf16* x, const float* shift, const float* scale,
+                      dit_bf16* out, int64_t rows, int64_t cols, float eps, void* stream);
+
+/* Gated residual: y[r,c] = x[r,c] + gate[c] * h[r,c]; x, h, y [rows, cols]
+ * bf16 (y may equal x or h); gate [cols] fp32.  cols % 8 == 0, cols <= 8192. */
+int dit_gated_residual(const dit_bf16* x, const dit_bf16* h, const float* gate,
+                       dit_bf16* y, int64_t rows, int64_t cols, void* stream);
+
+/* linear1 with fused epilogue: z = u . W1^T + b1 over [S, 3d+mlp];
+ * columns [0,3d) -> qkv [S, 3d] (q | k | v); columns [3d, 3d+mlp) ->
+ * GELU_tanh -> cat[:, d : d+mlp] of cat [S, d+mlp].
+ * u [S, d] bf16; w1 [3d+mlp, d]; b1 [3d+mlp] or NULL. */
+int dit_linear1_gelu(const dit_bf16* u, const dit_bf16* w1, const dit_bf16* b1,
+                     dit_bf16* qkv, dit_bf16* cat, int64_t seq_len, int64_t dim,
+                     int64_t mlp_hidden, void* stream);
+
+/* Per-head QK RMSNorm then RoPE, in place on the q and k blocks of qkv
+ * [S, 3*H*Dh]: t <- t / sqrt(mean(t^2) + eps) * w, then each pair
+ * (t[2j], t[2j+1]) is turned by the angle whose cos/sin are rope_cos/sin
+ * [S, Dh/2] fp32 (RoPE as complex rotation, Flux page section 3.1).
+ * q_norm_w, k_norm_w [Dh] fp32.  v is untouched. */
+int dit_qk_rmsnorm_rope(dit_bf16* qkv, const float* q_norm_w, const float* k_norm_w,
+                        const float* rope_cos, const float* rope_sin, int64_t seq_len,
+                        int64_t num_heads, int64_t head_dim, float eps, void* stream);
+
+/* Exact softmax attention per head, no mask (the flash / sdpa backends of the
+ * Flux page, sections 2 and 4), softmax statistics and accumulation in fp32:
+ * out[t, h*Dh:(h+1)*Dh] = softmax_u(q_t . k_u / sqrt(Dh)) v_u, with q, k, v
+ * read from qkv [S, 3*H*Dh]; out has leading dimension ld_out (>= H*Dh),
+ * only columns [0, H*Dh) are written. */
+int dit_attention(const dit_bf16* qkv, dit_bf16* out, int64_t seq_len, int64_t num_heads,
+                  int64_t head_dim, int64_t ld_out, void* stream);
+
+/* linear2 with fused gated residual: y = x + gate * (cat . W2^T + b2).
+ * cat [S, d+mlp]; w2 [d, d+mlp]; b2 [d] or NULL; x, y [S, d] (y may equal x);
+ * gate [d] fp32. */
+int dit_linear2_gated_residual(const dit_bf16* cat, const dit_bf16* w2, const dit_bf16* b2,
+                               const dit_bf16* x, const float* gate, dit_bf16* y,
+                               int64_t seq_len, int64_t dim, int64_t mlp_hidden, void* stream);
+
+/* RoPE angle tables: for token t and pair j of the head, cos/sin of
+ * positions[t, a] * base^(-2 j' / D_a), where the head dim is cut into
+ * n_axes chunks of axes_dims[a] dims (HOST array, each even, summing to
+ * head_dim), j' is the pair's index inside its chunk and a its axis.
+ * positions [S, n_axes] int32; rope_cos, rope_sin [S, head_dim/2] fp32. */
+int dit_rope_table(const int32_t* positions, int64_t seq_len, int32_t n_axes,
+                   const int32_t* axes_dims, int64_t head_dim, float base,
+                   float* rope_cos, float* rope_sin, void* stream);
+
+/* ---- whole block --------------------------------------------------------- */
+
+/* Bytes of workspace dit_block_forward needs (0 on an invalid config). */
+size_t dit_block_workspace_bytes(const dit_block_config* cfg);
+
+/* One block forward: modulation GEMV, LayerNorm+modulate, linear1+GELU,
+ * QK RMSNorm+RoPE, attention, linear2+gated residual; six launches on
+ * `stream`.  x, y [S, d] bf16 (y may equal x: the block then runs in place);
+ * temb [temb_dim] bf16; rope_cos/sin [S, head_dim/2] fp32; workspace is a
+ * device buffer of at least dit_block_workspace_bytes(cfg) bytes, 256-byte
+ * aligned. */
+int dit_block_forward(const dit_block_config* cfg, const dit_block_weights* w,
+                      const dit_bf16* x, const dit_bf16* temb, const float* rope_cos,
+                      const float* rope_sin, dit_bf16* y, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* ---- block stack replayed over denoising steps --------------------------- */
+
+typedef struct dit_stack dit_stack;  /* opaque: owns the captured graph */
+
+int dit_stack_create(dit_stack** out);
+int dit_stack_destroy(dit_stack* st);
+
+/* Bytes of workspace dit_stack_replay needs (0 on an invalid config). */
+size_t dit_stack_workspace_bytes(const dit_block_config* cfg);
+
+/* Runs n_steps denoising steps of the n_blocks-block stack: step s feeds
+ * x_in (or, with DIT_STACK_CHAIN, step s-1's output) through blocks
+ * 0..n_blocks-1 in order with temb_steps[s], and writes out[s].  The block
+ * sequence is captured once as a hipGraph on the first call and replayed
+ * once per step (capture-once / replay-many, Flux page sections 1.2-1.3).
+ * blocks: HOST array [n_blocks] of device weight pointers; temb_steps
+ * [n_steps, temb_dim]; out [n_steps, S, d].  The graph is keyed by the
+ * config, every pointer and n_blocks; a later call with another key returns
+ * DIT_ERR_GRAPH_KEY (destroy and re-create the stack to re-capture). */
+int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks,
+                     int n_blocks, const dit_bf16* x_in, const dit_bf16* temb_steps,
+                     int n_steps, const float* rope_cos, const float* rope_sin, dit_bf16* out,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- diagnostics ------------------------------------------------------------ */
+
+const char* dit_last_error(void);  /* message for the last non-OK return on this thread */
+const char* dit_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_BLOCK_H */

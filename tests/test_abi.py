@@ -1,0 +1,113 @@
+"""CPU tests of the C ABI: the library loads, exports every declared entry
+point, and rejects bad arguments with the documented codes before any HIP
+call (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit_block.h")
+LIB = os.path.join(ROOT, "diffusion_transformer_dit_amd", "libdit_block.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from diffusion_transformer_dit_amd import build
+        build.build()
+    from diffusion_transformer_dit_amd import binding
+    return binding._lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dit_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version(lib):
+    from diffusion_transformer_dit_amd import binding
+    assert "gfx950" in binding.version()
+
+
+def cfg(**kw):
+    from diffusion_transformer_dit_amd import binding
+    base = dict(seq_len=256, dim=256, num_heads=4, head_dim=64, mlp_hidden=1024)
+    base.update(kw)
+    return binding.make_config(**base)
+
+
+def test_workspace_bytes(lib):
+    from diffusion_transformer_dit_amd import binding
+    c = cfg()
+    a = lambda n: (n + 255) // 256 * 256
+    S, d, mlp = 256, 256, 1024
+    want = a(3 * d * 4) + a(S * d * 2) + a(S * 3 * d * 2) + a(S * (d + mlp) * 2)
+    assert binding.block_workspace_bytes(c) == want
+    assert binding.stack_workspace_bytes(c) == want + a(S * d * 2) + a(d * 2)
+    assert binding.block_workspace_bytes(cfg(head_dim=96, num_heads=3, dim=288)) == 0
+    assert binding.block_workspace_bytes(cfg(num_heads=3)) == 0
+
+
+def test_invalid_arguments_are_rejected_before_hip(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    P = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    assert lib.dit_modulate_norm(None, P, P, P, 4, 8, 1e-6, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_modulate_norm(P, P, P, P, 4, 12, 1e-6, None) == B.DIT_ERR_UNSUPPORTED
+    assert lib.dit_modulate_norm(P, P, P, P, -1, 8, 1e-6, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_modulate_norm(P, P, P, P, 4, 16384, 1e-6, None) == B.DIT_ERR_UNSUPPORTED
+    assert lib.dit_gated_residual(P, None, P, P, 4, 8, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_attention(P, P, 64, 3, 96, 288, None) == B.DIT_ERR_UNSUPPORTED
+    assert lib.dit_attention(P, P, 64, 2, 64, 100, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_linear1_gelu(P, P, None, P, P, 64, 100, 128, None) == B.DIT_ERR_UNSUPPORTED
+    assert lib.dit_linear2_gated_residual(P, P, None, P, P, P, 64, 128, 96, None) == B.DIT_ERR_UNSUPPORTED
+    assert lib.dit_modulation(P, P, None, P, 256, 12, None) == B.DIT_ERR_UNSUPPORTED
+    dims = (ctypes.c_int32 * 2)(32, 30)
+    assert lib.dit_rope_table(P, 16, 2, ctypes.cast(dims, ctypes.c_void_p), 64, 10000.0, P, P, None) \
+        == B.DIT_ERR_INVALID_ARG
+    assert "sum" in lib.dit_last_error().decode()
+
+
+def test_block_forward_argument_checks(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    P = ctypes.c_void_p(0x1000)
+    c = cfg()
+    w = B.BlockWeightsC(0x1000, 0, 0x1000, 0, 0x1000, 0, 0x1000, 0x1000)
+    need = B.block_workspace_bytes(c)
+    fwd = lambda cc, ww, ws_bytes, ws=P: lib.dit_block_forward(
+        ctypes.byref(cc), ctypes.byref(ww), P, P, P, P, P, ws, ws_bytes, None)
+    assert fwd(c, w, need - 1) == B.DIT_ERR_WORKSPACE
+    assert fwd(c, w, need, None) == B.DIT_ERR_WORKSPACE
+    assert fwd(c, w, need, ctypes.c_void_p(0x1010)) == B.DIT_ERR_WORKSPACE  # not 256-aligned
+    bad = B.BlockWeightsC(0x1000, 0, 0, 0, 0x1000, 0, 0x1000, 0x1000)
+    assert fwd(c, bad, need) == B.DIT_ERR_INVALID_ARG
+    assert fwd(cfg(head_dim=32, num_heads=8), w, need) == B.DIT_ERR_UNSUPPORTED
+    assert fwd(cfg(ln_eps=-1.0), w, need) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_block_forward(None, ctypes.byref(w), P, P, P, P, P, P, need, None) == B.DIT_ERR_INVALID_ARG
+
+
+def test_stack_argument_checks(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    P = ctypes.c_void_p(0x1000)
+    h = ctypes.c_void_p()
+    assert lib.dit_stack_create(ctypes.byref(h)) == B.DIT_OK and h.value
+    c = cfg()
+    w = (B.BlockWeightsC * 1)(B.BlockWeightsC(0x1000, 0, 0x1000, 0, 0x1000, 0, 0x1000, 0x1000))
+    need = B.stack_workspace_bytes(c)
+    rep = lambda st, nb, ns, ws_bytes: lib.dit_stack_replay(
+        st, ctypes.byref(c), ctypes.cast(w, ctypes.c_void_p), nb, P, P, ns, P, P, P, P, ws_bytes, None)
+    assert rep(None, 1, 1, need) == B.DIT_ERR_INVALID_ARG
+    assert rep(h, 0, 1, need) == B.DIT_ERR_INVALID_ARG
+    assert rep(h, 1, -1, need) == B.DIT_ERR_INVALID_ARG
+    assert rep(h, 1, 1, need - 256) == B.DIT_ERR_WORKSPACE
+    assert lib.dit_stack_destroy(h) == B.DIT_OK
+    assert lib.dit_stack_destroy(None) == B.DIT_OK

@@ -1,0 +1,234 @@
+"""GPU parity of each kernel of the block against the CPU oracle, through the
+C ABI, on seeded inputs from dit_inputs.  Sizes span several tiles plus a
+ragged tail; the Flux-size cases compare sampled rows the oracle computes
+one by one."""
+import numpy as np
+import pytest
+
+import dit_inputs as DI
+from oracle import dit_oracle as O
+from tests.parity import assert_parity, dev_bf16, dev_f32, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _vec(seed, n, sigma):
+    return (_rng(seed).standard_normal(n, dtype=np.float32) * np.float32(sigma))
+
+
+# ------------------------------------------------------------ modulation GEMV
+@pytest.mark.parametrize("d,tdim", [(256, 256), (3072, 3072), (1536, 1536), (64, 40)])
+def test_modulation(gpu_lib, d, tdim):
+    temb = DI.draw(11, (tdim,), 1.0)
+    w = DI.draw(12, (3 * d, tdim), 0.02)
+    b = DI.draw(13, (3 * d,), 0.02)
+    mod = gpu_lib.modulation(dev_bf16(temb), dev_bf16(w), dev_bf16(b))
+    ref = np.concatenate(O.modulation(temb, w, b))
+    assert_parity(host(mod), ref, f"modulation d={d}")
+    # without a bias
+    mod0 = gpu_lib.modulation(dev_bf16(temb), dev_bf16(w), None)
+    assert_parity(host(mod0), np.concatenate(O.modulation(temb, w, np.zeros(3 * d))), "modulation nobias")
+
+
+# ------------------------------------------------------------ LN + modulate
+@pytest.mark.parametrize("rows,cols", [(4608, 3072), (37, 264), (256, 256), (1, 8), (129, 8192), (300, 1536)])
+def test_modulate_norm(gpu_lib, rows, cols):
+    ch = DI.chain_inputs(rows, cols)
+    x = ch["x"] * 1.5 + 0.25      # non-zero mean and non-unit spread per row
+    x = DI.round_bf16(x.astype(np.float32))
+    out = gpu_lib.modulate_norm(dev_bf16(x), dev_f32(ch["shift"]), dev_f32(ch["scale"]), 1e-6)
+    ref = O.layer_norm_modulate(x, ch["shift"], ch["scale"], 1e-6)
+    assert_parity(host(out), ref, f"modulate_norm {rows}x{cols}")
+
+
+def test_modulate_norm_empty_and_inplace(gpu_lib):
+    import torch
+    x = dev_bf16(DI.draw(3, (0, 256)))
+    z = dev_f32(np.zeros(256, np.float32))
+    assert gpu_lib.modulate_norm(x, z, z).shape == (0, 256)
+    xv = DI.draw(4, (64, 512))
+    xt = dev_bf16(xv)
+    z512 = dev_f32(np.zeros(512, np.float32))
+    gpu_lib.modulate_norm(xt, z512, z512, 1e-6, out=xt)
+    torch.cuda.synchronize()
+    assert_parity(host(xt), O.layer_norm(xv, 1e-6), "modulate_norm in place")
+
+
+def test_modulate_norm_scale_minus_one_gives_shift(gpu_lib):
+    x = DI.draw(5, (64, 1024))
+    shift = _vec(6, 1024, 1.0)
+    out = gpu_lib.modulate_norm(dev_bf16(x), dev_f32(shift), dev_f32(-np.ones(1024, np.float32)))
+    assert np.array_equal(host(out), np.repeat(DI.round_bf16(shift)[None, :], 64, 0).astype(np.float64))
+
+
+# ------------------------------------------------------------ gated residual
+@pytest.mark.parametrize("rows,cols", [(4608, 3072), (37, 264), (1, 8), (513, 8192)])
+def test_gated_residual(gpu_lib, rows, cols):
+    ch = DI.chain_inputs(rows, cols)
+    y = gpu_lib.gated_residual(dev_bf16(ch["x"]), dev_bf16(ch["h"]), dev_f32(ch["gate"]))
+    ref = O.gated_residual(ch["x"], ch["gate"], ch["h"])
+    assert_parity(host(y), ref, f"gated_residual {rows}x{cols}")
+
+
+def test_gated_residual_gate_zero_is_identity(gpu_lib):
+    ch = DI.chain_inputs(300, 3072)
+    y = gpu_lib.gated_residual(dev_bf16(ch["x"]), dev_bf16(ch["h"]), dev_f32(np.zeros(3072, np.float32)))
+    assert np.array_equal(host(y), ch["x"].astype(np.float64))
+
+
+# ------------------------------------------------------------ RoPE tables
+@pytest.mark.parametrize("shape", [DI.TINY, DI.FLUX, DI.VIDEO])
+def test_rope_table(gpu_lib, shape):
+    import torch
+    pos = DI.positions(shape)
+    c, s = gpu_lib.rope_table(torch.from_numpy(pos).cuda(), list(shape.rope_axes_dims), shape.head_dim,
+                              shape.rope_base)
+    th = O.rope_angles(pos, shape.rope_axes_dims, shape.head_dim, shape.rope_base)
+    assert np.max(np.abs(host(c) - np.cos(th))) < 2e-5
+    assert np.max(np.abs(host(s) - np.sin(th))) < 2e-5
+    # position 0 is exactly the identity rotation
+    zero = np.all(pos == 0, axis=1)
+    assert np.all(host(c)[zero] == 1.0) and np.all(host(s)[zero] == 0.0)
+
+
+# ------------------------------------------------------------ QK RMSNorm + RoPE
+@pytest.mark.parametrize("S,H,Dh", [(4608, 24, 128), (77, 3, 64), (130, 2, 128)])
+def test_qk_rmsnorm_rope(gpu_lib, S, H, Dh):
+    import torch
+    d = H * Dh
+    qkv = DI.draw(21, (S, 3 * d), 1.0)
+    qw = (1 + 0.1 * _rng(22).standard_normal(Dh)).astype(np.float32)
+    kw = (1 + 0.1 * _rng(23).standard_normal(Dh)).astype(np.float32)
+    pos = _rng(24).integers(0, 64, size=(S, 2)).astype(np.int32)
+    pos[:5] = 0
+    th = O.rope_angles(pos, (Dh // 2, Dh // 2), Dh)
+    cos_t, sin_t = gpu_lib.rope_table(torch.from_numpy(pos).cuda(), [Dh // 2, Dh // 2], Dh)
+    t = dev_bf16(qkv)
+    gpu_lib.qk_rmsnorm_rope(t, dev_f32(qw), dev_f32(kw), cos_t, sin_t, H, Dh, 1e-6)
+    g = host(t)
+    q_ref = O.rope_apply(O.rms_norm_heads(qkv[:, :d], H, Dh, qw, 1e-6), th, H, Dh)
+    k_ref = O.rope_apply(O.rms_norm_heads(qkv[:, d:2 * d], H, Dh, kw, 1e-6), th, H, Dh)
+    assert_parity(g[:, :d], q_ref, f"q rmsnorm+rope S={S}")
+    assert_parity(g[:, d:2 * d], k_ref, f"k rmsnorm+rope S={S}")
+    assert np.array_equal(g[:, 2 * d:], qkv[:, 2 * d:].astype(np.float64))  # v untouched
+
+
+# ------------------------------------------------------------ attention
+def _qkv_for_attention(S, H, Dh, seed):
+    """q and k with unit RMS per head (as after the QK RMSNorm), v ~ N(0,1)."""
+    d = H * Dh
+    qkv = DI.draw(seed, (S, 3 * d), 1.0)
+    return qkv
+
+
+@pytest.mark.parametrize("S,H,Dh", [(200, 2, 128), (256, 4, 64), (64, 1, 128), (1, 2, 64), (333, 3, 128),
+                                    (129, 2, 64)])
+def test_attention_small(gpu_lib, S, H, Dh):
+    import torch
+    d = H * Dh
+    qkv = _qkv_for_attention(S, H, Dh, 31)
+    out = torch.zeros(S, d + 64, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.attention(dev_bf16(qkv), out, H, Dh)
+    ref = O.attention(qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:], H, Dh)
+    g = host(out)
+    assert_parity(g[:, :d], ref, f"attention S={S} H={H} Dh={Dh}")
+    assert np.all(g[:, d:] == 0)  # columns past H*Dh untouched
+
+
+def test_attention_sharp_scores(gpu_lib):
+    """Scores far from 0 (large |q|, |k|) exercise the running max."""
+    import torch
+    S, H, Dh = 300, 2, 128
+    d = H * Dh
+    qkv = _qkv_for_attention(S, H, Dh, 32)
+    qkv[:, :2 * d] = DI.round_bf16((qkv[:, :2 * d] * 3.0).astype(np.float32))
+    out = torch.empty(S, d, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.attention(dev_bf16(qkv), out, H, Dh)
+    ref = O.attention(qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:], H, Dh)
+    assert_parity(host(out), ref, "attention sharp")
+
+
+@pytest.mark.parametrize("S,H", [(4608, 24), (16384, 12)])
+def test_attention_full_size_sampled(gpu_lib, S, H):
+    import torch
+    Dh = 128
+    d = H * Dh
+    qkv = _qkv_for_attention(S, H, Dh, 33)
+    out = torch.empty(S, d, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.attention(dev_bf16(qkv), out, H, Dh)
+    rows = np.unique(np.concatenate([np.arange(0, S, S // 29), [S - 1, 127, 128, 511, 512]]))
+    ref = O.attention(qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:], H, Dh, q_rows=rows)
+    assert_parity(host(out)[rows], ref, f"attention S={S} sampled")
+
+
+# ------------------------------------------------------------ linear1 + GELU
+@pytest.mark.parametrize("S,d,mlp", [(300, 256, 1024), (4608, 3072, 12288), (97, 128, 192)])
+def test_linear1_gelu(gpu_lib, S, d, mlp):
+    import torch
+    u = DI.draw(41, (S, d), 1.0)
+    w1 = DI.draw(42, (3 * d + mlp, d), 0.02)
+    b1 = DI.draw(43, (3 * d + mlp,), 0.02)
+    qkv = torch.empty(S, 3 * d, dtype=torch.bfloat16, device="cuda")
+    cat = torch.zeros(S, d + mlp, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.linear1_gelu(dev_bf16(u), dev_bf16(w1), dev_bf16(b1), qkv, cat, mlp)
+    rows = np.arange(S) if S <= 512 else np.unique(np.concatenate([np.arange(0, S, 61), [S - 1]]))
+    z = O.linear(u[rows], w1, b1)
+    assert_parity(host(qkv)[rows], z[:, :3 * d], f"linear1 qkv S={S}")
+    c = host(cat)[rows]
+    assert_parity(c[:, d:], O.gelu_tanh(z[:, 3 * d:]), f"linear1 gelu S={S}")
+    assert np.all(c[:, :d] == 0)  # attention columns untouched
+
+
+# ------------------------------------------------------------ linear2 + gated residual
+@pytest.mark.parametrize("S,d,mlp", [(300, 256, 1024), (4608, 3072, 12288), (97, 128, 192), (16384, 1536, 8960)])
+def test_linear2_gated_residual(gpu_lib, S, d, mlp):
+    cat = DI.draw(51, (S, d + mlp), 1.0)
+    w2 = DI.draw(52, (d, d + mlp), 0.02)
+    b2 = DI.draw(53, (d,), 0.02)
+    x = DI.draw(54, (S, d), 1.0)
+    gate = _vec(55, d, 0.5)
+    xt = dev_bf16(x)
+    y = gpu_lib.linear2_gated_residual(dev_bf16(cat), dev_bf16(w2), dev_bf16(b2), xt, dev_f32(gate),
+                                       dev_bf16(np.zeros((S, d), np.float32)))
+    rows = np.arange(S) if S <= 512 else np.unique(np.concatenate([np.arange(0, S, 97), [S - 1]]))
+    h = O.linear(cat[rows], w2, b2)
+    yg = host(y)[rows]
+    assert_parity(yg, O.gated_residual(x[rows], gate, h), f"linear2 y S={S}")
+    # the branch alone (the residual hides branch errors in y)
+    hg = (yg - x[rows]) / gate[None, :]
+    assert_parity(hg, h, f"linear2 branch S={S}")
+
+
+def test_linear2_in_place(gpu_lib):
+    import torch
+    S, d, mlp = 200, 256, 512
+    cat = DI.draw(61, (S, d + mlp), 1.0)
+    w2 = DI.draw(62, (d, d + mlp), 0.02)
+    x = DI.draw(63, (S, d), 1.0)
+    gate = _vec(64, d, 0.5)
+    xt = dev_bf16(x)
+    gpu_lib.linear2_gated_residual(dev_bf16(cat), dev_bf16(w2), None, xt, dev_f32(gate), xt)
+    torch.cuda.synchronize()
+    assert_parity(host(xt), O.gated_residual(x, gate, O.linear(cat, w2)), "linear2 in place")
+
+
+def test_kernels_are_deterministic(gpu_lib):
+    import torch
+    S, d, mlp = 4608, 3072, 12288
+    u = dev_bf16(DI.draw(71, (S, d)))
+    w1 = dev_bf16(DI.draw(72, (3 * d + mlp, d), 0.02))
+    outs = []
+    for _ in range(2):
+        qkv = torch.empty(S, 3 * d, dtype=torch.bfloat16, device="cuda")
+        cat = torch.empty(S, d + mlp, dtype=torch.bfloat16, device="cuda")
+        gpu_lib.linear1_gelu(u, w1, None, qkv, cat, mlp)
+        o = torch.empty(S, d + mlp, dtype=torch.bfloat16, device="cuda")
+        gpu_lib.attention(qkv, o, 24, 128)
+        outs.append((qkv, cat[:, d:], o[:, :d]))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
