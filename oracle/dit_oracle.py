@@ -40,6 +40,18 @@ import numpy as np
 F64 = np.float64
 
 
+# ------------------------------------------------------------ bf16 storage
+def round_bf16(a):
+    """Round to the nearest bfloat16 value (ties to even), returned as float64.
+    The block takes and returns bf16 tensors (the Flux page, section 2, runs
+    the block in bf16), so a stack of blocks hands bf16 values from one
+    block to the next."""
+    f = np.ascontiguousarray(np.asarray(a, F64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(F64)
+
+
 # -------------------------------------------------------------- activations
 def silu(z):
     """SiLU(z) = z * sigmoid(z) = z / (1 + e^{-z}); feeds the modulation linear."""
@@ -214,16 +226,22 @@ def _attention_rows(q_rows, k, v, num_heads, head_dim):
     return attention(qfull, k, v, num_heads, head_dim, q_rows=np.arange(qfull.shape[0]))
 
 
-def stack_forward(shape, weights_list, x_in, temb_steps, pos, chain=False):
+def stack_forward(shape, weights_list, x_in, temb_steps, pos, chain=False, bf16_io=True):
     """Denoising-loop replay of a block stack: for each step s, run every block
     in order on the step input with temb_s; the step input is x_in, or the
-    previous step's output when ``chain`` is set.  Returns [n_steps, S, d]."""
+    previous step's output when ``chain`` is set.  With ``bf16_io`` each
+    block's output is handed to the next block (and to the next step) as a
+    bf16 tensor; the last block's output is returned unrounded.
+    Returns [n_steps, S, d]."""
     outs = []
     xs = np.asarray(x_in, F64)
+    nb = len(weights_list)
     for s in range(len(temb_steps)):
         cur = xs if (chain and s > 0) else np.asarray(x_in, F64)
-        for w in weights_list:
+        for b, w in enumerate(weights_list):
             cur = block_forward(shape, w, cur, temb_steps[s], pos)
+            if bf16_io and b + 1 < nb:
+                cur = round_bf16(cur)
         outs.append(cur)
-        xs = cur
+        xs = round_bf16(cur) if bf16_io else cur
     return np.stack(outs)

@@ -233,17 +233,28 @@ def pin_block(o):
     assert np.allclose(o.block_forward(sh, w, x, temb, pos, rows=rows), y[rows], rtol=1e-12, atol=1e-12)
 
 
+def pin_round_bf16(o):
+    a = RNG.standard_normal(4096) * np.exp(RNG.uniform(-20, 20, 4096))
+    a = np.concatenate([a, [0.0, 1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5]])
+    ref = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(o.round_bf16(a), ref)
+
+
 def pin_stack(o):
     sh, w, x, temb, pos = _small_block()
     w2 = DI.block_weights(sh, block=1, sigma=0.1)
     tembs = [temb, temb * 0.5]
     out = o.stack_forward(sh, [w, w2], x, tembs, pos)
+    rb = lambda a: torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).double().numpy()
     for s in range(2):
-        ref = o.block_forward(sh, w2, o.block_forward(sh, w, x, tembs[s], pos), tembs[s], pos)
+        ref = o.block_forward(sh, w2, rb(o.block_forward(sh, w, x, tembs[s], pos)), tembs[s], pos)
         assert np.allclose(out[s], ref, rtol=1e-12, atol=1e-12)
     ch = o.stack_forward(sh, [w, w2], x, tembs, pos, chain=True)
-    ref1 = o.block_forward(sh, w2, o.block_forward(sh, w, out[0], tembs[1], pos), tembs[1], pos)
+    ref1 = o.block_forward(sh, w2, rb(o.block_forward(sh, w, rb(out[0]), tembs[1], pos)), tembs[1], pos)
     assert np.allclose(ch[1], ref1, rtol=1e-12, atol=1e-12)
+    raw = o.stack_forward(sh, [w, w2], x, tembs, pos, bf16_io=False)
+    ref2 = o.block_forward(sh, w2, o.block_forward(sh, w, x, tembs[0], pos), tembs[0], pos)
+    assert np.allclose(raw[0], ref2, rtol=1e-12, atol=1e-12)
     # every gate zero (gate rows of W_mod and b_mod) -> the stack returns its input
     zw = []
     for wb in (w, w2):
@@ -256,7 +267,7 @@ def pin_stack(o):
 
 
 PINS = [pin_layer_norm, pin_modulate, pin_gated_residual, pin_silu, pin_gelu, pin_linear,
-        pin_modulation, pin_rms_norm, pin_rope, pin_attention, pin_block, pin_stack]
+        pin_modulation, pin_rms_norm, pin_rope, pin_attention, pin_block, pin_round_bf16, pin_stack]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -354,7 +365,14 @@ def _mut_silu_sigmoid(z):
     return 1.0 / (1.0 + np.exp(-z))
 
 
+def _mut_round_truncate(a):
+    f = np.ascontiguousarray(np.asarray(a, np.float64).astype(np.float32))
+    return (f.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+
+
 MUTANTS = [
+    ("round_bf16", _mut_round_truncate, pin_round_bf16),
+    ("round_bf16", _mut_round_truncate, pin_stack),
     ("gelu_tanh", _mut_gelu_no_cubic, pin_gelu),
     ("layer_norm", _mut_ln_unbiased, pin_layer_norm),
     ("layer_norm", _mut_ln_eps_outside, pin_layer_norm),
