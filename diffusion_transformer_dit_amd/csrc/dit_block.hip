@@ -158,9 +158,10 @@ extern "C" int dit_modulation(const dit_bf16* temb, const dit_bf16* w_mod, const
 
 extern "C" int dit_modulate_norm(const dit_bf16* x, const float* shift, const float* scale, dit_bf16* out,
                                  int64_t rows, int64_t cols, float eps, void* stream) {
-  if (!x || !shift || !scale || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   int rc = check_rows_cols(rows, cols);
   if (rc) return rc;
+  if (rows == 0) return DIT_OK;  // empty input: nothing to read or write
+  if (!x || !shift || !scale || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   if (!(eps >= 0.f)) return fail(DIT_ERR_INVALID_ARG, "eps must be >= 0");
   DIT_CHECK_HIP(dit::launch_modulate_norm(x, shift, scale, out, int(rows), int(cols), eps, as_stream(stream)), "modulate_norm");
   return DIT_OK;
@@ -168,18 +169,20 @@ extern "C" int dit_modulate_norm(const dit_bf16* x, const float* shift, const fl
 
 extern "C" int dit_gated_residual(const dit_bf16* x, const dit_bf16* h, const float* gate, dit_bf16* y,
                                   int64_t rows, int64_t cols, void* stream) {
-  if (!x || !h || !gate || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   int rc = check_rows_cols(rows, cols);
   if (rc) return rc;
+  if (rows == 0) return DIT_OK;
+  if (!x || !h || !gate || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   DIT_CHECK_HIP(dit::launch_gated_residual(x, h, gate, y, int(rows), int(cols), as_stream(stream)), "gated_residual");
   return DIT_OK;
 }
 
 extern "C" int dit_linear1_gelu(const dit_bf16* u, const dit_bf16* w1, const dit_bf16* b1, dit_bf16* qkv,
                                 dit_bf16* cat, int64_t seq_len, int64_t dim, int64_t mlp_hidden, void* stream) {
-  if (!u || !w1 || !qkv || !cat) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   int rc = check_linear(seq_len, dim, mlp_hidden);
   if (rc) return rc;
+  if (seq_len == 0) return DIT_OK;
+  if (!u || !w1 || !qkv || !cat) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   DIT_CHECK_HIP(dit::launch_linear1(u, w1, b1, qkv, cat, int(seq_len), int(dim), int(mlp_hidden), as_stream(stream)), "linear1");
   return DIT_OK;
 }
@@ -187,9 +190,10 @@ extern "C" int dit_linear1_gelu(const dit_bf16* u, const dit_bf16* w1, const dit
 extern "C" int dit_qk_rmsnorm_rope(dit_bf16* qkv, const float* q_norm_w, const float* k_norm_w,
                                    const float* rope_cos, const float* rope_sin, int64_t seq_len,
                                    int64_t num_heads, int64_t head_dim, float eps, void* stream) {
-  if (!qkv || !q_norm_w || !k_norm_w || !rope_cos || !rope_sin) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   int rc = check_dims(seq_len, num_heads * head_dim, num_heads, head_dim, 64, 8);
   if (rc) return rc;
+  if (seq_len == 0) return DIT_OK;
+  if (!qkv || !q_norm_w || !k_norm_w || !rope_cos || !rope_sin) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   if (!(eps >= 0.f)) return fail(DIT_ERR_INVALID_ARG, "eps must be >= 0");
   DIT_CHECK_HIP(dit::launch_qk_rmsnorm_rope(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, int(seq_len),
                                             int(num_heads), int(head_dim), eps, as_stream(stream)), "qk_rmsnorm_rope");
@@ -198,9 +202,10 @@ extern "C" int dit_qk_rmsnorm_rope(dit_bf16* qkv, const float* q_norm_w, const f
 
 extern "C" int dit_attention(const dit_bf16* qkv, dit_bf16* out, int64_t seq_len, int64_t num_heads,
                              int64_t head_dim, int64_t ld_out, void* stream) {
-  if (!qkv || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   int rc = check_dims(seq_len, num_heads * head_dim, num_heads, head_dim, 64, 8);
   if (rc) return rc;
+  if (seq_len == 0) return DIT_OK;
+  if (!qkv || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   if (ld_out < num_heads * head_dim || ld_out % 4 != 0 || ld_out > kMaxInt)
     return fail(DIT_ERR_INVALID_ARG, "ld_out=%lld must be >= H*Dh and a multiple of 4", (long long)ld_out);
   DIT_CHECK_HIP(dit::launch_attention(qkv, out, int(seq_len), int(num_heads), int(head_dim), int(ld_out),
@@ -211,9 +216,10 @@ extern "C" int dit_attention(const dit_bf16* qkv, dit_bf16* out, int64_t seq_len
 extern "C" int dit_linear2_gated_residual(const dit_bf16* cat, const dit_bf16* w2, const dit_bf16* b2,
                                           const dit_bf16* x, const float* gate, dit_bf16* y, int64_t seq_len,
                                           int64_t dim, int64_t mlp_hidden, void* stream) {
-  if (!cat || !w2 || !x || !gate || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   int rc = check_linear(seq_len, dim, mlp_hidden);
   if (rc) return rc;
+  if (seq_len == 0) return DIT_OK;
+  if (!cat || !w2 || !x || !gate || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   DIT_CHECK_HIP(dit::launch_linear2(cat, w2, b2, x, gate, y, int(seq_len), int(dim), int(mlp_hidden),
                                     as_stream(stream)), "linear2");
   return DIT_OK;

@@ -22,7 +22,9 @@
  *   - Every call returns DIT_OK (0) or an error code.  Arguments are checked
  *     before any HIP call; on error nothing is enqueued and dit_last_error()
  *     returns a message (thread-local).  HIP launch failures give DIT_ERR_HIP.
- *   - Supported shapes: any seq_len >= 1 (ragged tails are handled);
+ *   - Empty inputs (rows or seq_len 0) are valid no-ops; their tensor
+ *     pointers may then be NULL.
+ *   - Supported shapes: any seq_len >= 0 (ragged tails are handled);
  *     dim % 64 == 0; head_dim in {64, 128} with num_heads*head_dim == dim;
  *     mlp_hidden % 64 == 0; temb_dim % 8 == 0.  Others give
  *     DIT_ERR_UNSUPPORTED.

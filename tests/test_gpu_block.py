@@ -53,23 +53,46 @@ BLOCK_SHAPES = [
 
 @pytest.mark.parametrize("shape", BLOCK_SHAPES, ids=[s.name for s in BLOCK_SHAPES])
 def test_block_forward(gpu_lib, shape):
+    """Block output y, and every stage of the branch, read back from the
+    workspace (u, q/k after RMSNorm+RoPE, v, attention output, GELU output,
+    and h = linear2 of the GPU's own concat buffer with gate 1, x 0)."""
+    import torch
     B = gpu_lib
     blk = DevBlock(B, shape, norm_weights="random" if shape.seq_len < 1000 else "ones")
     x, temb = DI.block_activations(shape)
     pos, rc, rs = rope_dev(B, shape)
     cfg = cfg_of(B, shape)
-    y = B.block_forward(cfg, blk.dev, dev_bf16(x), dev_bf16(temb), rc, rs)
+    ws = B.alloc_workspace(B.block_workspace_bytes(cfg))
+    y = B.block_forward(cfg, blk.dev, dev_bf16(x), dev_bf16(temb), rc, rs, workspace=ws)
+    torch.cuda.synchronize()
     rows = sample_rows(shape.seq_len, extra=(shape.text_tokens - 1, shape.text_tokens))
     rows = rows[(rows >= 0) & (rows < shape.seq_len)]
-    ref, inter = O.block_forward(shape, blk.w, x, temb, pos, rows=rows, return_intermediates=True)
-    yg = host(y)[rows]
-    assert_parity(yg, ref, f"block y {shape.name}")
-    # the branch before the residual: h = (y - x) / gate
-    gate = inter["gate"]
-    ok = np.abs(gate) > 0.05
-    hg = (yg - x[rows])[:, ok] / gate[ok][None, :]
-    print(f"[info] {shape.name}: branch compared on {ok.sum()} of {gate.size} channels")
-    assert_parity(hg, inter["h"][:, ok], f"block branch h {shape.name}")
+    ref, it = O.block_forward(shape, blk.w, x, temb, pos, rows=rows, return_intermediates=True)
+    assert_parity(host(y)[rows], ref, f"block y {shape.name}")
+
+    S, d, mlp = shape.seq_len, shape.dim, shape.mlp_hidden
+    a = lambda n: (n + 255) // 256 * 256
+    off_u = a(3 * d * 4)
+    off_qkv = off_u + a(S * d * 2)
+    off_cat = off_qkv + a(S * 3 * d * 2)
+    mod = ws[:3 * d * 4].view(torch.float32)
+    u = ws[off_u:off_u + S * d * 2].view(torch.bfloat16).view(S, d)
+    qkv = ws[off_qkv:off_qkv + S * 3 * d * 2].view(torch.bfloat16).view(S, 3 * d)
+    cat = ws[off_cat:off_cat + S * (d + mlp) * 2].view(torch.bfloat16).view(S, d + mlp)
+    assert_parity(host(mod), np.concatenate([it["shift"], it["scale"], it["gate"]]), "mod", quantum=None)
+    assert_parity(host(u)[rows], it["u"], f"u {shape.name}")
+    qg = host(qkv)[rows]
+    assert_parity(qg[:, :d], it["q"], f"q {shape.name}")
+    assert_parity(qg[:, d:2 * d], it["k"], f"k {shape.name}")
+    assert_parity(qg[:, 2 * d:], it["v"], f"v {shape.name}")
+    cg = host(cat)[rows]
+    assert_parity(cg[:, :d], it["o"], f"attention out {shape.name}")
+    assert_parity(cg[:, d:], it["a"], f"gelu out {shape.name}")
+    w = blk.dev.tensors
+    hb = B.linear2_gated_residual(cat, w[4], w[5], torch.zeros(S, d, dtype=torch.bfloat16, device="cuda"),
+                                  torch.ones(d, dtype=torch.float32, device="cuda"),
+                                  torch.empty(S, d, dtype=torch.bfloat16, device="cuda"))
+    assert_parity(host(hb)[rows], it["h"], f"branch h {shape.name}")
 
 
 def test_block_forward_in_place_and_deterministic(gpu_lib):
@@ -116,42 +139,68 @@ def _stack_inputs(B, shape, n_blocks, n_steps):
     return blocks, x, tembs
 
 
-@pytest.mark.parametrize("chain", [False, True])
-def test_stack_replay_matches_oracle(gpu_lib, chain):
+def _replay(B, shape, blocks, x, tembs, rc, rs, chain=False):
     import torch
-    B = gpu_lib
-    shape = STACK_TINY
-    n_blocks, n_steps = 8, 3
-    blocks, x, tembs = _stack_inputs(B, shape, n_blocks, n_steps)
-    pos, rc, rs = rope_dev(B, shape)
     cfg = cfg_of(B, shape, B.DIT_STACK_CHAIN if chain else 0)
     ws = B.alloc_workspace(B.stack_workspace_bytes(cfg))
-    out = torch.empty(n_steps, shape.seq_len, shape.dim, dtype=torch.bfloat16, device="cuda")
+    n = tembs.shape[0]
+    out = torch.empty(n, shape.seq_len, shape.dim, dtype=torch.bfloat16, device="cuda")
     st = B.Stack()
     st.replay(cfg, [b.dev for b in blocks], dev_bf16(x), dev_bf16(tembs), rc, rs, out, ws)
+    torch.cuda.synchronize()
+    st.close()
+    return host(out)
+
+
+@pytest.mark.parametrize("chain", [False, True])
+def test_stack_replay_per_block_parity(gpu_lib, chain):
+    """Inside the replayed graph every block matches the oracle on the same
+    bf16 input: the output of the k-block stack is compared with the oracle's
+    block k applied to the GPU's (k-1)-block output, for every k."""
+    B = gpu_lib
+    shape = STACK_TINY
+    n_blocks, n_steps = 6, 2
+    blocks, x, tembs = _stack_inputs(B, shape, n_blocks, n_steps)
+    pos, rc, rs = rope_dev(B, shape)
+    prev = None
+    for k in range(1, n_blocks + 1):
+        out = _replay(B, shape, blocks[:k], x, tembs, rc, rs, chain)
+        for s in range(n_steps):
+            if k == 1:
+                xin = x if (s == 0 or not chain) else out[s - 1]
+            else:
+                xin = prev[s]
+            ref = O.block_forward(shape, blocks[k - 1].w, xin, tembs[s], pos)
+            if chain and s > 0 and k > 1:
+                continue  # its input (step s-1 of the full stack) is not this stack's output
+            assert_parity(out[s], ref, f"stack block {k} step {s} chain={chain}")
+        prev = out
+    # free-running comparison with the oracle stack (bf16 between blocks): drift report
     ref = O.stack_forward(shape, [b.w for b in blocks], x, tembs, pos, chain=chain)
     for s in range(n_steps):
-        assert_parity(host(out[s]), ref[s], f"stack step {s} chain={chain}")
-    st.close()
+        assert_parity(out[s], ref[s], f"stack free-running step {s} chain={chain} (drift report)",
+                      check_max_abs=False)
 
 
-def test_stack_57_blocks_reduced_depth(gpu_lib):
-    """57 blocks at the tiny shape, 2 steps, against the oracle (drift report)."""
-    import torch
+def test_stack_57_blocks(gpu_lib):
+    """57 blocks at the tiny shape, 2 steps: the last block inside the 57-deep
+    graph against the oracle on the same input (56-block output), plus the
+    free-running drift against the oracle stack (cosine asserted, max-abs
+    reported)."""
     B = gpu_lib
     shape = STACK_TINY
     n_blocks, n_steps = 57, 2
     blocks, x, tembs = _stack_inputs(B, shape, n_blocks, n_steps)
     pos, rc, rs = rope_dev(B, shape)
-    cfg = cfg_of(B, shape)
-    ws = B.alloc_workspace(B.stack_workspace_bytes(cfg))
-    out = torch.empty(n_steps, shape.seq_len, shape.dim, dtype=torch.bfloat16, device="cuda")
-    st = B.Stack()
-    st.replay(cfg, [b.dev for b in blocks], dev_bf16(x), dev_bf16(tembs), rc, rs, out, ws)
+    out56 = _replay(B, shape, blocks[:56], x, tembs, rc, rs)
+    out57 = _replay(B, shape, blocks, x, tembs, rc, rs)
+    for s in range(n_steps):
+        ref = O.block_forward(shape, blocks[56].w, out56[s], tembs[s], pos)
+        assert_parity(out57[s], ref, f"57-block stack, block 57 step {s}")
     ref = O.stack_forward(shape, [b.w for b in blocks], x, tembs, pos)
     for s in range(n_steps):
-        assert_parity(host(out[s]), ref[s], f"57-block stack step {s}")
-    st.close()
+        assert_parity(out57[s], ref[s], f"57-block stack free-running step {s} (drift report)",
+                      check_max_abs=False)
 
 
 def test_stack_replay_equals_eager_bitwise(gpu_lib):
