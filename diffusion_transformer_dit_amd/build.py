@@ -56,6 +56,10 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # resolve every symbol now: a kernel whose host stub was not emitted
+    # shows up here as an undefined symbol instead of at first use
+    import ctypes
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")

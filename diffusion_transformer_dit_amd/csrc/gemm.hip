@@ -7,38 +7,68 @@
 // 3.2) finds these GEMMs dominating the block's timeline before and after
 // fusion; the elementwise work around them is what its section 1.1 fuses.
 //
-// Design: one workgroup of 4 wavefronts owns a BM x BN output tile; K is
-// walked in BK = 64 slices staged through LDS (double buffered, 16-byte
-// chunks, XOR-swizzled so that both the 16-byte stores and the MFMA operand
-// reads are bank-conflict free).  Each wave computes a WM x WN sub-tile with
-// v_mfma_f32_16x16x32_bf16, fp32 accumulators; the next slice's global loads
-// are in flight while the current slice is multiplied.  Tiles are numbered
-// so that the tiles resident on one XCD (blocks are dealt round-robin over
-// the 8 XCDs) form a compact 2D patch sharing A and B panels in that XCD's L2.
+// Design: one workgroup of 4 wavefronts owns a BM x BN output tile.  K is
+// walked in BK = 32 slices through a ring of NSTAGE LDS buffers filled by
+// direct global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes
+// land in LDS without passing through registers), issued NSTAGE-1 slices
+// ahead of the slice being multiplied; explicit vmcnt waits and a bare
+// s_barrier hand a slice to the MFMAs.  Rows of a slice are 64 bytes (four
+// 16-byte chunks); chunk positions are XOR-swizzled by row so that the MFMA
+// operand reads are free of bank conflicts for 32- and 64-bank LDS.  Each
+// wave computes a WM x WN sub-tile with v_mfma_f32_16x16x32_bf16 and fp32
+// accumulators.  Tiles are numbered so that the tiles one XCD runs at a time
+// (blocks are dealt round-robin to the 8 XCDs) form a compact patch sharing
+// A and B panels in that XCD's L2.
 #include "dit_common.hpp"
 #include "launch.hpp"
 
 namespace dit {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 64;
+  static constexpr int BM = BM_, BN = BN_, BK = 32, NSTAGE = NSTAGE_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 16, FN = WN / 16;
-  static constexpr int A_LD = BM * 8 / NT;  // 16-byte chunks per thread per slice
-  static constexpr int B_LD = BN * 8 / NT;
-  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int ROW_BYTES = BK * 2;               // 64
+  static constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
   static constexpr int STAGE = A_BYTES + B_BYTES;
+  // one wave-load = 64 lanes x 16 bytes = 16 rows of a slice
+  static constexpr int A_WL = BM / 16, B_WL = BN / 16, WL = A_WL + B_WL;
+  static constexpr int L_MAX = (WL + NW - 1) / NW;       // wave-loads per wave per slice
+  static constexpr int L_MIN = WL / NW;
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
-  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile rows must split over threads");
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "tile must be a multiple of 16 rows");
+  static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "LDS ring too large");
+  static_assert(L_MIN >= 1, "every wave issues at least one load per slice");
 };
 
-// Byte offset of 16-byte chunk `c` (0..7) of row `r` inside an LDS slice whose
-// rows are 64 bf16 (128 bytes): chunk positions are XOR-swizzled by row.
-__device__ __forceinline__ uint32_t lds_off(int r, int c) {
-  return uint32_t(r) * 128u + (uint32_t(c ^ (r & 7)) << 4);
+// Swizzle of 16-byte chunk positions inside a 64-byte row.  For the rows a
+// ds_read_b128 phase touches (8 consecutive rows with 32 banks, 16 with 64
+// banks) the 4-bank groups are all distinct.
+__device__ __forceinline__ int row_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+// s_waitcnt vmcnt(VM) lgkmcnt(LGKM), expcnt unconstrained (gfx9 encoding;
+// LGKM = 15 leaves lgkmcnt unconstrained).
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_cnt() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from global memory straight into LDS; lane i writes
+// lds_block + 16 i (lds_block must be the same for the whole wavefront).
+__device__ __forceinline__ void load_lds_16(const bf16_t* src, unsigned char* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_block, 16, 0, 0);
 }
 
 struct EpiLinear1 {
@@ -103,7 +133,7 @@ template <class C, class Epi>
 __global__ void __launch_bounds__(C::NT, 1)
 gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, int M, int N,
                     int K, Epi epi) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -113,41 +143,40 @@ gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, 
   tile_coords<4>(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
 
-  // global -> LDS chunk assignment: chunk q = tid + i*NT, row q/8, column chunk q%8.
-  const int lc = tid & 7;
-  const int lr = tid >> 3;
-  constexpr int RSTEP = C::NT / 8;
-  const bf16_t* ga[C::A_LD];
-  const bf16_t* gb[C::B_LD];
+  // Direct-to-LDS loads.  Wave w issues wave-loads j = w, w + NW, ...; lane i
+  // of wave-load j writes LDS bytes [16 i, 16 i + 16) of the j-th 1 KB block
+  // of the slice, i.e. row 16 j' + i/4 (j' = j inside A or B), chunk position
+  // i % 4, which holds global chunk (i % 4) ^ swz(row) of that row.
+  const int lrow = lane >> 2;                       // row inside the 16-row block
+  const int lchunk = (lane & 3) ^ row_swz(lrow);    // global chunk this lane fetches
+  const bf16_t* gsrc[C::L_MAX];
+  uint32_t ldst[C::L_MAX];
+  int nload = 0;
 #pragma unroll
-  for (int i = 0; i < C::A_LD; ++i) {
-    const int r = min(m0 + lr + i * RSTEP, M - 1);  // rows past M are clamped; never stored
-    ga[i] = A + size_t(r) * K + lc * 8;
+  for (int i = 0; i < C::L_MAX; ++i) {
+    const int j = wave + i * C::NW;
+    gsrc[i] = A;
+    ldst[i] = 0;
+    if (j < C::WL) {
+      nload = i + 1;
+      if (j < C::A_WL) {
+        const int r = min(m0 + 16 * j + lrow, M - 1);  // rows past M are clamped; never stored
+        gsrc[i] = A + size_t(r) * K + lchunk * 8;
+        ldst[i] = uint32_t(j) * 1024u;
+      } else {
+        const int jb = j - C::A_WL;
+        const int r = min(n0 + 16 * jb + lrow, N - 1);
+        gsrc[i] = B + size_t(r) * K + lchunk * 8;
+        ldst[i] = uint32_t(C::A_BYTES) + uint32_t(jb) * 1024u;
+      }
+    }
   }
+  auto issue = [&](int kt, int stage) {
+    unsigned char* base = smem + stage * C::STAGE;
 #pragma unroll
-  for (int i = 0; i < C::B_LD; ++i) {
-    const int r = min(n0 + lr + i * RSTEP, N - 1);
-    gb[i] = B + size_t(r) * K + lc * 8;
-  }
-  uint32_t la[C::A_LD], lb[C::B_LD];
-#pragma unroll
-  for (int i = 0; i < C::A_LD; ++i) la[i] = lds_off(lr + i * RSTEP, lc);
-#pragma unroll
-  for (int i = 0; i < C::B_LD; ++i) lb[i] = C::A_BYTES + lds_off(lr + i * RSTEP, lc);
-
-  u32x4 ra[C::A_LD], rb[C::B_LD];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ga[i] + kt * C::BK);
-#pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4*>(gb[i] + kt * C::BK);
-  };
-  auto lstore = [&](int stage) {
-    unsigned char* s = smem + stage * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) *reinterpret_cast<u32x4*>(s + la[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) *reinterpret_cast<u32x4*>(s + lb[i]) = rb[i];
+    for (int i = 0; i < C::L_MAX; ++i)
+      if (i < nload)
+        load_lds_16(gsrc[i] + kt * C::BK, base + ldst[i]);
   };
 
   f32x4 acc[C::FM][C::FN];
@@ -156,40 +185,64 @@ gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, 
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // operand read offsets: lane holds row (lane & 15) of a 16-row fragment and
-  // the 8 K-values of chunk (lane >> 4) of the current 32-wide K step.
+  // MFMA operand reads: lane holds row (lane & 15) of a 16-row fragment and
+  // the 8 K-values of chunk (lane >> 4) of the 32-wide slice.
   const int fr = lane & 15;
   const int fk = lane >> 4;
-  const uint32_t a_row = uint32_t(wm * C::WM + fr) * 128u;
-  const uint32_t b_row = C::A_BYTES + uint32_t(wn * C::WN + fr) * 128u;
+  const uint32_t swz = uint32_t((fk ^ row_swz(fr)) << 4);
+  const uint32_t a_off = uint32_t(wm * C::WM + fr) * C::ROW_BYTES + swz;
+  const uint32_t b_off = C::A_BYTES + uint32_t(wn * C::WN + fr) * C::ROW_BYTES + swz;
 
-  const int KT = K / C::BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const unsigned char* s = smem + cur * C::STAGE;
+  bf16x8 fa[C::FM + C::FN], fb[C::FM + C::FN];  // two fragment sets (ping-pong)
+  auto read_frags = [&](int stage, bf16x8* f) {
+    const unsigned char* s = smem + stage * C::STAGE;
 #pragma unroll
-    for (int ks = 0; ks < C::BK / 32; ++ks) {
-      const uint32_t sw = uint32_t(((ks * 4 + fk) ^ (fr & 7)) << 4);
-      bf16x8 a[C::FM], b[C::FN];
+    for (int i = 0; i < C::FM; ++i) f[i] = *reinterpret_cast<const bf16x8*>(s + a_off + i * 16 * C::ROW_BYTES);
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(s + a_row + i * 16 * 128 + sw);
+    for (int j = 0; j < C::FN; ++j)
+      f[C::FM + j] = *reinterpret_cast<const bf16x8*>(s + b_off + j * 16 * C::ROW_BYTES);
+  };
+  auto mfmas = [&](const bf16x8* f) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(s + b_row + j * 16 * 128 + sw);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[i], f[C::FM + j], acc[i][j], 0, 0, 0);
+  };
+  // Wait until slice `next` has landed in LDS for every wave, with `ahead`
+  // later slices allowed to stay in flight, and until this wave's operand reads
+  // of the previous slice are complete; then every wave passes the barrier.
+  auto handoff = [&](int ahead) {
+    if (ahead >= 2) wait_cnt<2 * C::L_MIN, 0>();
+    else if (ahead == 1) wait_cnt<C::L_MIN, 0>();
+    else wait_cnt<0, 0>();
+    block_barrier();
+  };
+
+  const int KT = K / C::BK;  // even: K is a multiple of 64
+  // prologue: slices 0 .. NSTAGE-2 in flight; slice s lives in buffer s % NSTAGE
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) lstore(cur ^ 1);
-    __syncthreads();
+  for (int s = 0; s < C::NSTAGE - 1; ++s)
+    if (s < KT) issue(s, s);
+  handoff(min(C::NSTAGE - 2, KT - 1));
+  if (C::NSTAGE - 1 < KT) issue(C::NSTAGE - 1, C::NSTAGE - 1);
+  read_frags(0, fa);
+  // Iteration kt < KT-1: hand over slice kt+1, refill the buffer of slice kt
+  // (its operands are already in registers) with slice kt+NSTAGE, read slice
+  // kt+1's operands into the other fragment set while slice kt's MFMAs run.
+  auto step = [&](int kt, bf16x8* cur, bf16x8* nxt) {
+    handoff(min(C::NSTAGE - 2, KT - 2 - kt));
+    if (kt + C::NSTAGE < KT) issue(kt + C::NSTAGE, kt % C::NSTAGE);
+    read_frags((kt + 1) % C::NSTAGE, nxt);
+    mfmas(cur);
+  };
+  for (int kt = 0; kt < KT - 2; kt += 2) {
+    step(kt, fa, fb);
+    step(kt + 1, fb, fa);
   }
+  step(KT - 2, fa, fb);
+  wait_cnt<63, 0>();
+  mfmas(fb);
 
   // C fragment layout (16x16): lane holds column (lane & 15), rows 4*(lane>>4) + i.
 #pragma unroll
@@ -200,9 +253,9 @@ gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, 
 }
 
 // ------------------------------------------------------------------ tile choice
-using T288x192 = TileCfg<288, 192, 2, 2>;
-using T256 = TileCfg<256, 256, 2, 2>;
-using T128 = TileCfg<128, 128, 2, 2>;
+using T288x192 = TileCfg<288, 192, 2, 2, 4>;
+using T256 = TileCfg<256, 256, 2, 2, 4>;
+using T128 = TileCfg<128, 128, 2, 2, 4>;
 
 static int num_cus() {
   static int n = 0;
