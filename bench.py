@@ -81,6 +81,80 @@ def time_launches(fn, iters, warm=2):
     return s.elapsed_time(e) / iters
 
 
+KERNEL_NAMES = ("modulation", "modulate_norm", "linear1_gelu", "qk_rmsnorm_rope", "attention",
+                "linear2_gated_residual", "gated_residual", "copy")
+
+
+def kernel_phase(B, g, dev, blocks, x_in, temb, rc, rs, it, only=None):
+    """Times each kernel of the block with HIP events around `it` back-to-back
+    launches on the current stream (one block's buffers; the memory-bound
+    kernels rotate over 12 buffer sets, > the 256 MB last-level cache).
+    Returns ({name: ms per launch}, cache-warm ms of modulate_norm)."""
+    import torch
+    want = lambda n: (n != "copy") if only is None else (n in only)
+
+    def randn(shape, sigma):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * sigma).to(torch.bfloat16)
+
+    nb = len(blocks)
+    w0 = blocks[0]
+    u = torch.empty(S, D, dtype=torch.bfloat16, device=dev)
+    qkv = torch.empty(S, 3 * D, dtype=torch.bfloat16, device=dev)
+    cat = torch.empty(S, N2, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(S, D, dtype=torch.bfloat16, device=dev)
+    mod = B.modulation(temb[0], w0.tensors[0], w0.tensors[1])
+    B.modulate_norm(x_in, mod[:D], mod[D:2 * D], 1e-6, out=u)
+    B.linear1_gelu(u, w0.tensors[2], w0.tensors[3], qkv, cat, MLP)
+    B.qk_rmsnorm_rope(qkv, w0.tensors[6], w0.tensors[7], rc, rs, H, DH)
+    k = {}
+    if want("copy"):
+        # calibration for byte counters: a plain copy of a known size (256 MiB read + 256 MiB written)
+        src = torch.empty(128 * 1024 * 1024, dtype=torch.bfloat16, device=dev).normal_(generator=g)
+        dst = torch.empty_like(src)
+        k["copy"] = time_launches(lambda i: dst.copy_(src), min(it, 5))
+        del src, dst
+    if want("linear1_gelu"):
+        k["linear1_gelu"] = time_launches(
+            lambda i: B.linear1_gelu(u, w0.tensors[2], w0.tensors[3], qkv, cat, MLP), it)
+    if want("qk_rmsnorm_rope"):
+        k["qk_rmsnorm_rope"] = time_launches(
+            lambda i: B.qk_rmsnorm_rope(qkv, w0.tensors[6], w0.tensors[7], rc, rs, H, DH), it)
+        B.linear1_gelu(u, w0.tensors[2], w0.tensors[3], qkv, cat, MLP)
+        B.qk_rmsnorm_rope(qkv, w0.tensors[6], w0.tensors[7], rc, rs, H, DH)
+    if want("attention"):
+        k["attention"] = time_launches(lambda i: B.attention(qkv, cat, H, DH), it)
+    gate = mod[2 * D:]
+    if want("linear2_gated_residual"):
+        k["linear2_gated_residual"] = time_launches(
+            lambda i: B.linear2_gated_residual(cat, w0.tensors[4], w0.tensors[5], x_in, gate, y), it)
+    if want("modulation"):
+        # over distinct weights (each 56.6 MB; they are never cache resident together)
+        k["modulation"] = time_launches(
+            lambda i: B.modulation(temb[0], blocks[i % nb].tensors[0], blocks[i % nb].tensors[1], out=mod), it)
+    k_warm_norm = None
+    if want("modulate_norm") or want("gated_residual"):
+        nrot = 12
+        xs = [randn((S, D), 1.0) for _ in range(nrot)]
+        hs = [randn((S, D), 1.0) for _ in range(nrot)]
+        us = [torch.empty(S, D, dtype=torch.bfloat16, device=dev) for _ in range(nrot)]
+        shift = torch.randn(D, generator=g, device=dev) * 0.1
+        scale = torch.randn(D, generator=g, device=dev) * 0.1
+        gvec = torch.randn(D, generator=g, device=dev) * 0.1
+        norm_iters = max(it, 4 * nrot)
+        if want("modulate_norm"):
+            k["modulate_norm"] = time_launches(
+                lambda i: B.modulate_norm(xs[i % nrot], shift, scale, 1e-6, out=us[i % nrot]), norm_iters)
+            k_warm_norm = time_launches(lambda i: B.modulate_norm(xs[0], shift, scale, 1e-6, out=us[0]),
+                                        norm_iters)
+        if want("gated_residual"):
+            k["gated_residual"] = time_launches(
+                lambda i: B.gated_residual(xs[i % nrot], hs[i % nrot], gvec, out=us[i % nrot]), norm_iters)
+    torch.cuda.synchronize()
+    for name, ms in k.items():
+        log(f"kernel {name}: {ms * 1000:.1f} us")
+    return k, k_warm_norm
+
+
 def cpu_baseline():
     """The oracle (numpy float64) on one full Flux-shape block on the host cores."""
     import numpy as np
@@ -112,6 +186,9 @@ def main():
     ap.add_argument("--blocks", type=int, default=57)
     ap.add_argument("--kernel-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels-only", default=None,
+                    help="comma list of kernels (%s): time only these, no stack replay (for profiler runs)"
+                         % ",".join(KERNEL_NAMES))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -129,6 +206,24 @@ def main():
 
     def randn(shape, sigma):
         return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * sigma).to(torch.bfloat16)
+
+    if args.kernels_only:
+        only = set(args.kernels_only.split(","))
+        bad = only - set(KERNEL_NAMES)
+        if bad:
+            print(f"unknown kernels: {sorted(bad)}", file=sys.stderr)
+            return 2
+        nb = 1 if only != {"modulation"} and "modulation" not in only else 8
+        blocks = [B.BlockWeights(randn((3 * D, D), 0.02), randn((3 * D,), 0.02), randn((N1, D), 0.02),
+                                 randn((N1,), 0.02), randn((D, N2), 0.02), randn((D,), 0.02),
+                                 torch.ones(DH, device=dev), torch.ones(DH, device=dev)) for _ in range(nb)]
+        x_in = randn((S, D), 1.0)
+        temb = randn((1, D), 1.0)
+        pos = torch.from_numpy(DI.positions(DI.FLUX)).to(dev)
+        rc, rs = B.rope_table(pos, list(DI.FLUX.rope_axes_dims), DH)
+        k, _ = kernel_phase(B, g, dev, blocks, x_in, temb, rc, rs, args.kernel_iters, only)
+        print(json.dumps({"kernels_us": {n: round(v * 1e3, 2) for n, v in k.items()}}), flush=True)
+        return 0
 
     nb = args.blocks
     log(f"allocating {nb} Flux blocks ({nb * (3 * D * D + N1 * D + D * N2) * 2 / 1e9:.1f} GB of weights)")
@@ -168,47 +263,7 @@ def main():
     assert torch.isfinite(out[args.warmup:n_total].float()).all(), "non-finite output"
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, {ms_block:.4f} ms/block (wall {wall:.3f} s)")
 
-    # ---- per-kernel timing on the same stream, one block's worth of buffers
-    w0 = blocks[0]
-    u = torch.empty(S, D, dtype=torch.bfloat16, device=dev)
-    qkv = torch.empty(S, 3 * D, dtype=torch.bfloat16, device=dev)
-    cat = torch.empty(S, N2, dtype=torch.bfloat16, device=dev)
-    y = torch.empty(S, D, dtype=torch.bfloat16, device=dev)
-    mod = B.modulation(temb[0], w0.tensors[0], w0.tensors[1])
-    B.modulate_norm(x_in, mod[:D], mod[D:2 * D], 1e-6, out=u)
-    it = args.kernel_iters
-    k = {}
-    k["linear1_gelu"] = time_launches(lambda i: B.linear1_gelu(u, w0.tensors[2], w0.tensors[3], qkv, cat, MLP), it)
-    k["qk_rmsnorm_rope"] = time_launches(
-        lambda i: B.qk_rmsnorm_rope(qkv, w0.tensors[6], w0.tensors[7], rc, rs, H, DH), it)
-    B.linear1_gelu(u, w0.tensors[2], w0.tensors[3], qkv, cat, MLP)
-    B.qk_rmsnorm_rope(qkv, w0.tensors[6], w0.tensors[7], rc, rs, H, DH)
-    k["attention"] = time_launches(lambda i: B.attention(qkv, cat, H, DH), it)
-    gate = mod[2 * D:]
-    k["linear2_gated_residual"] = time_launches(
-        lambda i: B.linear2_gated_residual(cat, w0.tensors[4], w0.tensors[5], x_in, gate, y), it)
-    # modulation GEMV over the 57 distinct weights (each 56.6 MB; never cache resident together)
-    k["modulation"] = time_launches(
-        lambda i: B.modulation(temb[0], blocks[i % nb].tensors[0], blocks[i % nb].tensors[1], out=mod), it)
-    # memory-bound chain with buffer rotation: 12 sets x 56.6 MB > 256 MB MALL
-    nrot = 12
-    xs = [randn((S, D), 1.0) for _ in range(nrot)]
-    hs = [randn((S, D), 1.0) for _ in range(nrot)]
-    us = [torch.empty(S, D, dtype=torch.bfloat16, device=dev) for _ in range(nrot)]
-    shift = (torch.randn(D, generator=g, device=dev) * 0.1)
-    scale = (torch.randn(D, generator=g, device=dev) * 0.1)
-    gvec = (torch.randn(D, generator=g, device=dev) * 0.1)
-    norm_iters = max(it, 4 * nrot)
-    k["modulate_norm"] = time_launches(
-        lambda i: B.modulate_norm(xs[i % nrot], shift, scale, 1e-6, out=us[i % nrot]), norm_iters)
-    k["gated_residual"] = time_launches(
-        lambda i: B.gated_residual(xs[i % nrot], hs[i % nrot], gvec, out=us[i % nrot]), norm_iters)
-    # cache-warm single buffer, reported as a footnote only
-    k_warm_norm = time_launches(lambda i: B.modulate_norm(xs[0], shift, scale, 1e-6, out=us[0]), norm_iters)
-    torch.cuda.synchronize()
-    for name, ms in k.items():
-        log(f"kernel {name}: {ms * 1000:.1f} us")
-
+    k, k_warm_norm = kernel_phase(B, g, dev, blocks, x_in, temb, rc, rs, args.kernel_iters)
     tf = lambda flop, ms: flop / (ms * 1e-3) / 1e12
     gbs = lambda byt, ms: byt / (ms * 1e-3) / 1e9
     kernels = {

@@ -7,18 +7,22 @@
 // 3.2) finds these GEMMs dominating the block's timeline before and after
 // fusion; the elementwise work around them is what its section 1.1 fuses.
 //
-// Design: one workgroup of 4 wavefronts owns a BM x BN output tile.  K is
-// walked in BK = 32 slices through a ring of NSTAGE LDS buffers filled by
-// direct global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes
-// land in LDS without passing through registers), issued NSTAGE-1 slices
-// ahead of the slice being multiplied; explicit vmcnt waits and a bare
-// s_barrier hand a slice to the MFMAs.  Rows of a slice are 64 bytes (four
-// 16-byte chunks); chunk positions are XOR-swizzled by row so that the MFMA
-// operand reads are free of bank conflicts for 32- and 64-bank LDS.  Each
-// wave computes a WM x WN sub-tile with v_mfma_f32_16x16x32_bf16 and fp32
-// accumulators.  Tiles are numbered so that the tiles one XCD runs at a time
-// (blocks are dealt round-robin to the 8 XCDs) form a compact patch sharing
-// A and B panels in that XCD's L2.
+// Design: one workgroup of 8 wavefronts owns a BM x BN output tile; two
+// groups of 4 waves each own half of it.  K is walked in BK = 32 slices
+// through a ring of 4 LDS buffers filled by direct global->LDS loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land in LDS without passing
+// through registers), issued 3 slices ahead.  The two groups run half a slice
+// apart ("ping-pong"): between two workgroup barriers one group multiplies its
+// operands with v_mfma_f32_16x16x32_bf16 while the other group issues its
+// share of the refill and reads its next operands from LDS, so each SIMD (one
+// wave of each group) always has MFMA work while the other wave waits on
+// memory.  Rows of a slice are 64 bytes (four 16-byte chunks); chunk
+// positions are XOR-swizzled by row so that the operand reads are free of
+// bank conflicts.  Accumulation is fp32.  Tiles are numbered so that the
+// tiles one XCD runs at a time (blocks are dealt round-robin to the 8 XCDs)
+// form a compact patch sharing A and B panels in that XCD's L2.
+#include <type_traits>
+
 #include "dit_common.hpp"
 #include "launch.hpp"
 
@@ -36,12 +40,16 @@ struct TileCfg {
   static constexpr int STAGE = A_BYTES + B_BYTES;
   // one wave-load = 64 lanes x 16 bytes = 16 rows of a slice
   static constexpr int A_WL = BM / 16, B_WL = BN / 16, WL = A_WL + B_WL;
-  static constexpr int L_MAX = (WL + NW - 1) / NW;       // wave-loads per wave per slice
-  static constexpr int L_MIN = WL / NW;
+  static constexpr int L = (WL + NW - 1) / NW;           // wave-loads per wave per slice
+  // waves with fewer real loads issue their spare ones into a 1 KB trash slot,
+  // so that every wave has exactly L loads in flight per slice
+  static constexpr int TRASH = NSTAGE * STAGE;
+  static constexpr int LDS_BYTES = TRASH + ((WL % NW) ? 1024 : 0);
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "tile must be a multiple of 16 rows");
-  static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "LDS ring too large");
-  static_assert(L_MIN >= 1, "every wave issues at least one load per slice");
+  static_assert(NSTAGE == 4, "the pipeline is written for a 4-slice ring");
+  static_assert(NW == 8, "two groups of four waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
 };
 
 // Swizzle of 16-byte chunk positions inside a 64-byte row.  For the rows a
@@ -130,10 +138,10 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
 }
 
 template <class C, class Epi>
-__global__ void __launch_bounds__(C::NT, 1)
+__global__ void __launch_bounds__(C::NT, C::NW / 4)
 gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, int M, int N,
                     int K, Epi epi) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -149,34 +157,31 @@ gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, 
   // i % 4, which holds global chunk (i % 4) ^ swz(row) of that row.
   const int lrow = lane >> 2;                       // row inside the 16-row block
   const int lchunk = (lane & 3) ^ row_swz(lrow);    // global chunk this lane fetches
-  const bf16_t* gsrc[C::L_MAX];
-  uint32_t ldst[C::L_MAX];
-  int nload = 0;
+  const bf16_t* gsrc[C::L];
+  uint32_t ldst[C::L];  // LDS byte offset inside a slice buffer, or TRASH for a spare load
 #pragma unroll
-  for (int i = 0; i < C::L_MAX; ++i) {
+  for (int i = 0; i < C::L; ++i) {
     const int j = wave + i * C::NW;
-    gsrc[i] = A;
-    ldst[i] = 0;
-    if (j < C::WL) {
-      nload = i + 1;
-      if (j < C::A_WL) {
-        const int r = min(m0 + 16 * j + lrow, M - 1);  // rows past M are clamped; never stored
-        gsrc[i] = A + size_t(r) * K + lchunk * 8;
-        ldst[i] = uint32_t(j) * 1024u;
-      } else {
-        const int jb = j - C::A_WL;
-        const int r = min(n0 + 16 * jb + lrow, N - 1);
-        gsrc[i] = B + size_t(r) * K + lchunk * 8;
-        ldst[i] = uint32_t(C::A_BYTES) + uint32_t(jb) * 1024u;
-      }
+    if (j < C::A_WL) {
+      const int r = min(m0 + 16 * j + lrow, M - 1);  // rows past M are clamped; never stored
+      gsrc[i] = A + size_t(r) * K + lchunk * 8;
+      ldst[i] = uint32_t(j) * 1024u;
+    } else if (j < C::WL) {
+      const int jb = j - C::A_WL;
+      const int r = min(n0 + 16 * jb + lrow, N - 1);
+      gsrc[i] = B + size_t(r) * K + lchunk * 8;
+      ldst[i] = uint32_t(C::A_BYTES) + uint32_t(jb) * 1024u;
+    } else {
+      gsrc[i] = gsrc[0];  // any valid address; lands in the trash slot
+      ldst[i] = C::TRASH;
     }
   }
+  // the trash slot is shared by all stages: its offset does not move with the stage
   auto issue = [&](int kt, int stage) {
-    unsigned char* base = smem + stage * C::STAGE;
+    const uint32_t sbase = uint32_t(stage) * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < C::L_MAX; ++i)
-      if (i < nload)
-        load_lds_16(gsrc[i] + kt * C::BK, base + ldst[i]);
+    for (int i = 0; i < C::L; ++i)
+      load_lds_16(gsrc[i] + kt * C::BK, smem + (ldst[i] == uint32_t(C::TRASH) ? ldst[i] : sbase + ldst[i]));
   };
 
   f32x4 acc[C::FM][C::FN];
@@ -193,56 +198,65 @@ gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, 
   const uint32_t a_off = uint32_t(wm * C::WM + fr) * C::ROW_BYTES + swz;
   const uint32_t b_off = C::A_BYTES + uint32_t(wn * C::WN + fr) * C::ROW_BYTES + swz;
 
-  bf16x8 fa[C::FM + C::FN], fb[C::FM + C::FN];  // two fragment sets (ping-pong)
-  auto read_frags = [&](int stage, bf16x8* f) {
+  bf16x8 frag[C::FM + C::FN];
+  auto read_frags = [&](int stage) {
     const unsigned char* s = smem + stage * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) f[i] = *reinterpret_cast<const bf16x8*>(s + a_off + i * 16 * C::ROW_BYTES);
+    for (int i = 0; i < C::FM; ++i) frag[i] = *reinterpret_cast<const bf16x8*>(s + a_off + i * 16 * C::ROW_BYTES);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
-      f[C::FM + j] = *reinterpret_cast<const bf16x8*>(s + b_off + j * 16 * C::ROW_BYTES);
+      frag[C::FM + j] = *reinterpret_cast<const bf16x8*>(s + b_off + j * 16 * C::ROW_BYTES);
   };
-  auto mfmas = [&](const bf16x8* f) {
+  auto mfmas = [&]() {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[i], f[C::FM + j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag[i], frag[C::FM + j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
   };
-  // Wait until slice `next` has landed in LDS for every wave, with `ahead`
-  // later slices allowed to stay in flight, and until this wave's operand reads
-  // of the previous slice are complete; then every wave passes the barrier.
-  auto handoff = [&](int ahead) {
-    if (ahead >= 2) wait_cnt<2 * C::L_MIN, 0>();
-    else if (ahead == 1) wait_cnt<C::L_MIN, 0>();
+  // Workgroup barrier after this wave's loads of all but the `ahead` most
+  // recent slices have landed and its LDS reads are complete.
+  auto sync = [&](int ahead) {
+    if (ahead >= 2) wait_cnt<2 * C::L, 0>();
+    else if (ahead == 1) wait_cnt<C::L, 0>();
     else wait_cnt<0, 0>();
     block_barrier();
   };
 
-  const int KT = K / C::BK;  // even: K is a multiple of 64
-  // prologue: slices 0 .. NSTAGE-2 in flight; slice s lives in buffer s % NSTAGE
-#pragma unroll
-  for (int s = 0; s < C::NSTAGE - 1; ++s)
-    if (s < KT) issue(s, s);
-  handoff(min(C::NSTAGE - 2, KT - 1));
-  if (C::NSTAGE - 1 < KT) issue(C::NSTAGE - 1, C::NSTAGE - 1);
-  read_frags(0, fa);
-  // Iteration kt < KT-1: hand over slice kt+1, refill the buffer of slice kt
-  // (its operands are already in registers) with slice kt+NSTAGE, read slice
-  // kt+1's operands into the other fragment set while slice kt's MFMAs run.
-  auto step = [&](int kt, bf16x8* cur, bf16x8* nxt) {
-    handoff(min(C::NSTAGE - 2, KT - 2 - kt));
-    if (kt + C::NSTAGE < KT) issue(kt + C::NSTAGE, kt % C::NSTAGE);
-    read_frags((kt + 1) % C::NSTAGE, nxt);
-    mfmas(cur);
-  };
-  for (int kt = 0; kt < KT - 2; kt += 2) {
-    step(kt, fa, fb);
-    step(kt + 1, fb, fa);
+  const int KT = K / C::BK;  // >= 2: K is a multiple of 64
+  const int group = wave >> 2;
+  // prologue: every wave issues its share of slices 0..2; slice s lives in buffer s % 4
+  issue(0, 0);
+  issue(1, 1);
+  if (KT > 2) issue(2, 2);
+  // Iteration k, two phases.  Phase 1: group 0 refills (slice k+3 into the
+  // buffer of slice k-1, which both groups have finished reading) and reads
+  // slice k; group 1 multiplies slice k-1.  Phase 2: group 0 multiplies
+  // slice k; group 1 refills and reads slice k.  Before a group reads slice
+  // k, every wave's loads of slice k have landed (barrier of phase 1).
+  for (int k = 0; k <= KT; ++k) {
+    const int ahead = min(2, KT - 1 - k);
+    sync(ahead);
+    if (group == 0) {
+      if (k < KT) {
+        if (k + 3 < KT) issue(k + 3, (k + 3) & 3);
+        read_frags(k & 3);
+      }
+    } else if (k >= 1) {
+      mfmas();
+    }
+    sync(ahead);
+    if (k < KT) {
+      if (group == 0) {
+        mfmas();
+      } else {
+        if (k + 3 < KT) issue(k + 3, (k + 3) & 3);
+        read_frags(k & 3);
+      }
+    }
   }
-  step(KT - 2, fa, fb);
-  wait_cnt<63, 0>();
-  mfmas(fb);
 
   // C fragment layout (16x16): lane holds column (lane & 15), rows 4*(lane>>4) + i.
 #pragma unroll
@@ -253,9 +267,9 @@ gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, 
 }
 
 // ------------------------------------------------------------------ tile choice
-using T288x192 = TileCfg<288, 192, 2, 2, 4>;
-using T256 = TileCfg<256, 256, 2, 2, 4>;
-using T128 = TileCfg<128, 128, 2, 2, 4>;
+using T288x192 = TileCfg<288, 192, 2, 4, 4>;  // 8 waves of 144 x 48; groups own 144-row halves
+using T256 = TileCfg<256, 256, 4, 2, 4>;      // 8 waves of 64 x 128; groups own 128-row halves
+using T128 = TileCfg<128, 128, 4, 2, 4>;      // 8 waves of 32 x 64
 
 static int num_cus() {
   static int n = 0;
@@ -273,12 +287,14 @@ void prepare_device() { (void)num_cus(); }
 
 enum TileKind { K288x192 = 0, K256 = 1, K128 = 2 };
 
-// Pick the tile that minimises rounds-of-workgroups x tile area (a proxy for
-// the time of the busiest CU); small tiles pay a fixed efficiency penalty.
+// Pick the tile that minimises rounds-of-workgroups x tile area / efficiency
+// (a proxy for the time of the busiest CU).
 static TileKind choose_tile(int M, int N) {
   const int cus = num_cus();
   struct Opt { TileKind k; int bm, bn; double eff; } opts[] = {
-      {K288x192, 288, 192, 1.0}, {K256, 256, 256, 1.0}, {K128, 128, 128, 0.75}};
+      // per-tile efficiency measured at the Flux shape (288x192 waves hold a
+      // thinner 144 x 48 sub-tile and run at 0.87 of the 256x256 rate)
+      {K288x192, 288, 192, 0.87}, {K256, 256, 256, 1.0}, {K128, 128, 128, 0.6}};
   TileKind best = K128;
   double best_cost = 1e300;
   for (const Opt& o : opts) {
