@@ -42,7 +42,7 @@ __device__ __forceinline__ uint32_t bf_at(const u32x4& v, int e) {
 }
 
 template <int DH>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, int S, int H,
                      int ld_out, float c_log2) {
   using C = AttCfg<DH>;
@@ -129,79 +129,81 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
     const unsigned char* sK = smem + cur * C::STAGE;
     const unsigned char* sV = sK + C::K_BYTES;
 
-    // S^T for keys [32*kb, 32*kb+32) of the tile
-    f32x16 sacc[2];
+    // The tile is processed as two halves of 32 keys: S^T for keys
+    // [32*kb, 32*kb+32), online softmax, then O^T += V^T P^T for those keys.
+    const int key0 = jt * ATT_BN;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sacc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      const int key = kb * 32 + ql;
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+      {
+        const int key = kb * 32 + ql;
 #pragma unroll
-      for (int s = 0; s < DH / 16; ++s) {
-        const int c = 2 * s + hh;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + key * (DH * 2) + ((c ^ (key & 7)) << 4));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+        for (int s = 0; s < DH / 16; ++s) {
+          const int c = 2 * s + hh;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + key * (DH * 2) + ((c ^ (key & 7)) << 4));
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc, 0, 0, 0);
+        }
       }
-    }
-    // accumulator row of register i: key 32*kb + 8*(i/4) + 4*hh + (i%4)
-    const int key0 = jt * ATT_BN;
-    if (key0 + ATT_BN > S) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      // accumulator row of register i: key 32*kb + 8*(i/4) + 4*hh + (i%4)
+      if (key0 + ATT_BN > S) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= S) sacc[kb][i] = -INFINITY;
-    }
-    float mx = sacc[0][0];
+          if (key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= S) sacc[i] = -INFINITY;
+      }
+      float mx = sacc[0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // Lazy rescale: the running max only moves (and O, l are rescaled) when
+      // a score exceeds it by more than 2^8 in exp2 units for some lane of the
+      // wave; otherwise the stale max stays, which is exact because numerator
+      // and denominator use the same max and 2^8 cannot overflow fp32 sums.
+      if (__builtin_amdgcn_ballot_w64((mx - m_run) * c_log2 > 8.0f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2_fast((m_run - m_new) * c_log2);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2_fast((m_run - m_new) * c_log2);
-    const float mc = m_new * c_log2;
-    float psum = 0.f;
-    bf16x8 pf[4];
+        for (int b = 0; b < DH / 32; ++b)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+          for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+      }
+      const float mc = m_run * c_log2;
+      bf16x8 pf[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          p[j] = exp2_fast(fmaf(sacc[kb][8 * half + j], c_log2, -mc));
-          psum += p[j];
+          p[j] = exp2_fast(fmaf(sacc[8 * half + j], c_log2, -mc));
+          l_run += p[j];
         }
         u32x4 pk = pack8(p);
-        pf[2 * kb + half] = __builtin_bit_cast(bf16x8, pk);
+        pf[half] = __builtin_bit_cast(bf16x8, pk);
       }
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+      // O^T += V^T P^T over the two 16-key steps m of this half: lane supplies
+      // keys 16m + 4hh + (0..3) and 16m + 8 + 4hh + (0..3), i.e. 8-byte units
+      // 4m+hh and 4m+2+hh of the V^T row.
 #pragma unroll
-    for (int b = 0; b < DH / 32; ++b)
+      for (int b = 0; b < DH / 32; ++b) {
+        const int dim = b * 32 + ql;
+        const unsigned char* row = sV + dim * (ATT_BN * 2);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
-
-    // O^T += V^T P^T over the 4 16-key steps m: lane supplies keys
-    // 16m + 4hh + (0..3) and 16m + 8 + 4hh + (0..3), i.e. 8-byte units 4m+hh, 4m+2+hh.
-#pragma unroll
-    for (int b = 0; b < DH / 32; ++b) {
-      const int dim = b * 32 + ql;
-      const unsigned char* row = sV + dim * (ATT_BN * 2);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int u1 = 4 * m + hh, u2 = 4 * m + 2 + hh;
-        u32x4 av;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(row + ((u1 ^ (dim & 15)) << 3));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(row + ((u2 ^ (dim & 15)) << 3));
-        av[0] = lo[0];
-        av[1] = lo[1];
-        av[2] = hi[0];
-        av[3] = hi[1];
-        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pf[m],
-                                                          oacc[b], 0, 0, 0);
+        for (int mh = 0; mh < 2; ++mh) {
+          const int m = 2 * kb + mh;
+          const int u1 = 4 * m + hh, u2 = 4 * m + 2 + hh;
+          u32x4 av;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(row + ((u1 ^ (dim & 15)) << 3));
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + ((u2 ^ (dim & 15)) << 3));
+          av[0] = lo[0];
+          av[1] = lo[1];
+          av[2] = hi[0];
+          av[3] = hi[1];
+          oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pf[mh],
+                                                            oacc[b], 0, 0, 0);
+        }
       }
     }
     if (jt + 1 < ntiles) lstore(cur ^ 1);

@@ -12,23 +12,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest, ties to even
-// (inputs here are finite).
+// bf16 <-> fp32.  Widening is exact; narrowing is one v_cvt_pk_bf16_f32
+// (round to nearest, ties to even) per pair of values.
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-__device__ __forceinline__ uint32_t f2bf_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return f2bf_bits(lo) | (f2bf_bits(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+__device__ __forceinline__ uint32_t f2bf_bits(float f) { return pack_bf2(f, 0.f) & 0xffffu; }
 
 // 8 bf16 held in a 16-byte vector -> 8 floats
 __device__ __forceinline__ void unpack8(const u32x4& v, float* f) {
