@@ -56,6 +56,8 @@ SIGNATURES = {
     "dit_stack_destroy": ([VP], ctypes.c_int),
     "dit_stack_workspace_bytes": ([VP], SZ),
     "dit_stack_replay": ([VP, VP, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
+    "dit_stack_set_probe": ([VP, ctypes.c_uint32], ctypes.c_int),
+    "dit_stack_probe_ms": ([VP, VP, ctypes.c_int], ctypes.c_int),
     "dit_last_error": ([], ctypes.c_char_p),
     "dit_version": ([], ctypes.c_char_p),
 }
@@ -288,6 +290,23 @@ class Stack:
             self.close()
         except Exception:
             pass
+
+    KERNELS = ("modulation", "modulate_norm", "linear1", "qk_rmsnorm_rope", "attention", "linear2")
+
+    def set_probe(self, kernels):
+        """Time the named block kernels inside every replay (before the first replay)."""
+        mask = 0
+        for k in kernels:
+            mask |= 1 << self.KERNELS.index(k)
+        _check(_lib.dit_stack_set_probe(self.handle, mask))
+        self._probe = tuple(kernels)
+
+    def probe_ms(self, n_blocks):
+        """{kernel: [mean ms per block]} over the probed steps since the previous
+        read (synchronises the device; restarts the accumulation)."""
+        buf = (ctypes.c_float * (n_blocks * 6))()
+        _check(_lib.dit_stack_probe_ms(self.handle, ctypes.cast(buf, VP), n_blocks))
+        return {k: [buf[b * 6 + self.KERNELS.index(k)] for b in range(n_blocks)] for k in self._probe}
 
     def replay(self, cfg, blocks, x_in, temb_steps, rope_cos, rope_sin, out, workspace, stream=None):
         _need(x_in, BF16, "x_in", 2)

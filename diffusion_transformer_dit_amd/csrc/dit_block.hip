@@ -106,23 +106,55 @@ WsLayout layout(const Dims& D) {
   return L;
 }
 
+// Optional timing probes.  Each probed kernel is bracketed by two one-thread
+// stamp kernels that read the device wall clock; the second adds the interval
+// to an accumulator.  Channel 6 brackets nothing: its interval is the probe's
+// own overhead, subtracted on the host.
+constexpr int kProbeChannels = 7;
+struct Probe {
+  uint32_t mask = 0;                   // bit i: kernel i of the block (0..5)
+  unsigned long long* ch = nullptr;    // [kProbeChannels][2] for this block
+};
+
 // The six launches of one block on `st`.  x and y may alias.
 int enqueue_block(const Dims& D, const dit_block_config* cfg, const dit_block_weights* w,
                   const dit_bf16* x, const dit_bf16* temb, const float* rcos, const float* rsin,
-                  dit_bf16* y, unsigned char* ws, hipStream_t st) {
+                  dit_bf16* y, unsigned char* ws, hipStream_t st, const Probe& pr = Probe()) {
   const WsLayout L = layout(D);
   float* mod = reinterpret_cast<float*>(ws + L.mod);
   dit_bf16* u = reinterpret_cast<dit_bf16*>(ws + L.u);
   dit_bf16* qkv = reinterpret_cast<dit_bf16*>(ws + L.qkv);
   dit_bf16* cat = reinterpret_cast<dit_bf16*>(ws + L.cat);
+  auto pre = [&](int k) -> hipError_t {
+    return (pr.mask >> k & 1u) ? dit::launch_probe_stamp(pr.ch + 2 * k, 0, st) : hipSuccess;
+  };
+  auto post = [&](int k) -> hipError_t {
+    return (pr.mask >> k & 1u) ? dit::launch_probe_stamp(pr.ch + 2 * k, 1, st) : hipSuccess;
+  };
+  if (pr.mask) {
+    DIT_CHECK_HIP(dit::launch_probe_stamp(pr.ch + 12, 0, st), "probe");
+    DIT_CHECK_HIP(dit::launch_probe_stamp(pr.ch + 12, 1, st), "probe");
+  }
+  DIT_CHECK_HIP(pre(0), "probe");
   DIT_CHECK_HIP(dit::launch_modulation(temb, w->w_mod, w->b_mod, mod, 3 * D.d, D.tdim, st), "modulation");
+  DIT_CHECK_HIP(post(0), "probe");
   if (D.S == 0) return DIT_OK;
+  DIT_CHECK_HIP(pre(1), "probe");
   DIT_CHECK_HIP(dit::launch_modulate_norm(x, mod, mod + D.d, u, D.S, D.d, cfg->ln_eps, st), "modulate_norm");
+  DIT_CHECK_HIP(post(1), "probe");
+  DIT_CHECK_HIP(pre(2), "probe");
   DIT_CHECK_HIP(dit::launch_linear1(u, w->w1, w->b1, qkv, cat, D.S, D.d, D.mlp, st), "linear1");
+  DIT_CHECK_HIP(post(2), "probe");
+  DIT_CHECK_HIP(pre(3), "probe");
   DIT_CHECK_HIP(dit::launch_qk_rmsnorm_rope(qkv, w->q_norm_w, w->k_norm_w, rcos, rsin, D.S, D.H, D.Dh,
                                             cfg->qk_eps, st), "qk_rmsnorm_rope");
+  DIT_CHECK_HIP(post(3), "probe");
+  DIT_CHECK_HIP(pre(4), "probe");
   DIT_CHECK_HIP(dit::launch_attention(qkv, cat, D.S, D.H, D.Dh, D.d + D.mlp, st), "attention");
+  DIT_CHECK_HIP(post(4), "probe");
+  DIT_CHECK_HIP(pre(5), "probe");
   DIT_CHECK_HIP(dit::launch_linear2(cat, w->w2, w->b2, x, mod + 2 * D.d, y, D.S, D.d, D.mlp, st), "linear2");
+  DIT_CHECK_HIP(post(5), "probe");
   return DIT_OK;
 }
 
@@ -272,12 +304,17 @@ struct dit_stack {
   hipGraphExec_t exec = nullptr;
   hipStream_t cap = nullptr;
   std::vector<uintptr_t> key;
+  uint32_t probe_mask = 0;
+  int probe_blocks = 0;
+  long long probe_replays = 0;         // probed graph launches since the last read
+  int wall_khz = 0;                    // device wall-clock rate
+  unsigned long long* probe_buf = nullptr;  // device [n_blocks][kProbeChannels][2]
 };
 
 namespace {
 std::vector<uintptr_t> make_key(const dit_block_config* cfg, const dit_block_weights* blocks, int n_blocks,
                                 const dit_bf16* x_in, const float* rcos, const float* rsin, void* ws,
-                                size_t ws_bytes) {
+                                size_t ws_bytes, uint32_t probe_mask) {
   std::vector<uintptr_t> k;
   k.push_back(uintptr_t(cfg->seq_len));
   k.push_back(uintptr_t(cfg->dim));
@@ -297,6 +334,7 @@ std::vector<uintptr_t> make_key(const dit_block_config* cfg, const dit_block_wei
   k.push_back(uintptr_t(rsin));
   k.push_back(uintptr_t(ws));
   k.push_back(uintptr_t(ws_bytes));
+  k.push_back(uintptr_t(probe_mask));
   for (int b = 0; b < n_blocks; ++b) {
     const dit_block_weights& w = blocks[b];
     for (const void* p : {(const void*)w.w_mod, (const void*)w.b_mod, (const void*)w.w1, (const void*)w.b1,
@@ -316,6 +354,7 @@ extern "C" int dit_stack_create(dit_stack** out) {
 
 extern "C" int dit_stack_destroy(dit_stack* st) {
   if (!st) return DIT_OK;
+  if (st->probe_buf) hipFree(st->probe_buf);
   if (st->exec) hipGraphExecDestroy(st->exec);
   if (st->graph) hipGraphDestroy(st->graph);
   if (st->cap) hipStreamDestroy(st->cap);
@@ -355,17 +394,37 @@ extern "C" int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, cons
   dit_bf16* tbuf = reinterpret_cast<dit_bf16*>(ws + L.tbuf);
   const size_t act_bytes = size_t(D.S) * D.d * 2;
 
-  std::vector<uintptr_t> key = make_key(cfg, blocks, n_blocks, x_in, rope_cos, rope_sin, workspace, ws_bytes);
+  std::vector<uintptr_t> key =
+      make_key(cfg, blocks, n_blocks, x_in, rope_cos, rope_sin, workspace, ws_bytes, st->probe_mask);
   if (st->exec && key != st->key)
     return fail(DIT_ERR_GRAPH_KEY, "stack was captured for another config / pointer set; destroy and re-create it");
   if (!st->exec) {
     dit::prepare_device();  // device queries happen before capture
     if (!st->cap) DIT_CHECK_HIP(hipStreamCreateWithFlags(&st->cap, hipStreamNonBlocking), "hipStreamCreate");
+    if (st->probe_mask) {
+      int dev = 0;
+      DIT_CHECK_HIP(hipGetDevice(&dev), "hipGetDevice");
+      DIT_CHECK_HIP(hipDeviceGetAttribute(&st->wall_khz, hipDeviceAttributeWallClockRate, dev),
+                    "hipDeviceGetAttribute");
+      if (st->wall_khz <= 0) return fail(DIT_ERR_HIP, "device reports no wall-clock rate");
+      const size_t bytes = size_t(n_blocks) * kProbeChannels * 2 * sizeof(unsigned long long);
+      if (st->probe_buf) hipFree(st->probe_buf);
+      st->probe_buf = nullptr;
+      DIT_CHECK_HIP(hipMalloc(&st->probe_buf, bytes), "hipMalloc");
+      DIT_CHECK_HIP(hipMemset(st->probe_buf, 0, bytes), "hipMemset");
+      st->probe_blocks = n_blocks;
+      st->probe_replays = 0;
+    }
     DIT_CHECK_HIP(hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
     int brc = DIT_OK;
     for (int b = 0; b < n_blocks && brc == DIT_OK; ++b) {
       const dit_bf16* xin = (b == 0 && !chain) ? x_in : xbuf;
-      brc = enqueue_block(D, cfg, &blocks[b], xin, tbuf, rope_cos, rope_sin, xbuf, ws, st->cap);
+      Probe pr;
+      if (st->probe_mask) {
+        pr.mask = st->probe_mask;
+        pr.ch = st->probe_buf + size_t(b) * kProbeChannels * 2;
+      }
+      brc = enqueue_block(D, cfg, &blocks[b], xin, tbuf, rope_cos, rope_sin, xbuf, ws, st->cap, pr);
     }
     hipGraph_t g = nullptr;
     hipError_t e = hipStreamEndCapture(st->cap, &g);
@@ -390,8 +449,40 @@ extern "C" int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, cons
     DIT_CHECK_HIP(hipMemcpyAsync(tbuf, temb_steps + size_t(step) * D.tdim, size_t(D.tdim) * 2,
                                  hipMemcpyDeviceToDevice, s), "copy temb");
     DIT_CHECK_HIP(hipGraphLaunch(st->exec, s), "hipGraphLaunch");
+    if (st->probe_mask) ++st->probe_replays;
     DIT_CHECK_HIP(hipMemcpyAsync(out + size_t(step) * D.S * D.d, xbuf, act_bytes, hipMemcpyDeviceToDevice, s),
                   "copy out");
+  }
+  return DIT_OK;
+}
+
+extern "C" int dit_stack_set_probe(dit_stack* st, uint32_t kernel_mask) {
+  if (!st) return fail(DIT_ERR_INVALID_ARG, "stack is NULL");
+  if (kernel_mask >> 6) return fail(DIT_ERR_INVALID_ARG, "kernel_mask=0x%x has bits above 5", kernel_mask);
+  if (st->exec) return fail(DIT_ERR_GRAPH_KEY, "probes must be set before the first replay");
+  st->probe_mask = kernel_mask;
+  return DIT_OK;
+}
+
+extern "C" int dit_stack_probe_ms(dit_stack* st, float* ms, int n_blocks) {
+  if (!st || !ms) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if (!st->exec || !st->probe_mask || st->probe_replays == 0)
+    return fail(DIT_ERR_INVALID_ARG, "no probed replay has run since the last read");
+  if (n_blocks != st->probe_blocks) return fail(DIT_ERR_INVALID_ARG, "n_blocks=%d, stack has %d", n_blocks, st->probe_blocks);
+  const size_t n = size_t(n_blocks) * kProbeChannels * 2;
+  std::vector<unsigned long long> h(n);
+  DIT_CHECK_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  DIT_CHECK_HIP(hipMemcpy(h.data(), st->probe_buf, n * sizeof(unsigned long long), hipMemcpyDeviceToHost),
+                "hipMemcpy");
+  DIT_CHECK_HIP(hipMemset(st->probe_buf, 0, n * sizeof(unsigned long long)), "hipMemset");
+  const double per_tick_ms = 1.0 / double(st->wall_khz) / double(st->probe_replays);
+  st->probe_replays = 0;
+  for (int b = 0; b < n_blocks; ++b) {
+    const unsigned long long* c = h.data() + size_t(b) * kProbeChannels * 2;
+    const double overhead = double(c[2 * 6 + 1]);
+    for (int k = 0; k < 6; ++k)
+      ms[size_t(b) * 6 + k] =
+          (st->probe_mask >> k & 1u) ? float((double(c[2 * k + 1]) - overhead) * per_tick_ms) : -1.f;
   }
   return DIT_OK;
 }

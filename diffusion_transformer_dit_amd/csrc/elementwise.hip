@@ -376,4 +376,21 @@ hipError_t launch_rope_table(const int32_t* pos, int S, int n_axes, const int32_
   return hipGetLastError();
 }
 
+// Timing probe: one thread reads the constant-rate wall clock.  finish == 0
+// stores the stamp in ch[0]; finish != 0 adds (now - ch[0]) to ch[1].  Nodes of
+// a captured stream run in order, so the read-modify-write needs no atomics.
+__global__ void probe_stamp_kernel(unsigned long long* ch, int finish) {
+  if (threadIdx.x != 0) return;
+  const unsigned long long t = wall_clock64();
+  if (finish)
+    ch[1] += t - ch[0];
+  else
+    ch[0] = t;
+}
+
+hipError_t launch_probe_stamp(unsigned long long* ch, int finish, hipStream_t st) {
+  probe_stamp_kernel<<<1, 64, 0, st>>>(ch, finish);
+  return hipGetLastError();
+}
+
 }  // namespace dit

@@ -35,4 +35,7 @@ hipError_t launch_linear2(const bf16_t* cat, const bf16_t* w2, const bf16_t* b2,
 hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
                             hipStream_t st);
 
+// timing probe channel ch[2]: finish == 0 stamps ch[0], else ch[1] += now - ch[0]
+hipError_t launch_probe_stamp(unsigned long long* ch, int finish, hipStream_t st);
+
 }  // namespace dit

@@ -179,6 +179,28 @@ int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, const dit_block
                      int n_steps, const float* rope_cos, const float* rope_sin, dit_bf16* out,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* Timing probes (diagnostics for benchmarks; must be set before the first
+ * replay, i.e. before the graph is captured; DIT_ERR_GRAPH_KEY after).  For
+ * every block and every kernel i (0 modulation, 1 LayerNorm+modulate,
+ * 2 linear1, 3 QK RMSNorm+RoPE, 4 attention, 5 linear2) with bit i of
+ * kernel_mask set, the captured graph brackets that launch with two
+ * one-thread kernels that read the device wall clock (hipDeviceAttribute-
+ * WallClockRate) and accumulate the interval in a small device buffer owned
+ * by the stack; a bracket around nothing, once per block, measures the
+ * probe's own overhead.  The kernels being timed and their results are
+ * unchanged; the graph gains 2 + 2*popcount(mask) tiny nodes per block.
+ * kernel_mask bits above 5 -> DIT_ERR_INVALID_ARG. */
+int dit_stack_set_probe(dit_stack* st, uint32_t kernel_mask);
+
+/* Synchronises the device, then writes ms[b*6 + i] = mean duration in
+ * milliseconds of kernel i of block b over the probed replay steps since
+ * the previous call (or since capture), with the probe overhead subtracted
+ * (so one dispatch gap remains in each figure); -1 for kernels not probed.
+ * Restarts the accumulation.  ms is a HOST array of n_blocks*6 floats;
+ * n_blocks must match the captured stack.  No probed step since the last
+ * read, or a mismatched n_blocks -> DIT_ERR_INVALID_ARG. */
+int dit_stack_probe_ms(dit_stack* st, float* ms, int n_blocks);
+
 /* ---- diagnostics ------------------------------------------------------------ */
 
 const char* dit_last_error(void);  /* message for the last non-OK return on this thread */

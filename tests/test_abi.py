@@ -111,3 +111,16 @@ def test_stack_argument_checks(lib):
     assert rep(h, 1, 1, need - 256) == B.DIT_ERR_WORKSPACE
     assert lib.dit_stack_destroy(h) == B.DIT_OK
     assert lib.dit_stack_destroy(None) == B.DIT_OK
+
+
+def test_stack_probe_argument_checks(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    h = ctypes.c_void_p()
+    assert lib.dit_stack_create(ctypes.byref(h)) == B.DIT_OK
+    assert lib.dit_stack_set_probe(None, 1) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_stack_set_probe(h, 1 << 6) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_stack_set_probe(h, 0x3F) == B.DIT_OK
+    buf = (ctypes.c_float * 6)()
+    # no probed replay has run yet
+    assert lib.dit_stack_probe_ms(h, ctypes.cast(buf, ctypes.c_void_p), 1) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_stack_destroy(h) == B.DIT_OK

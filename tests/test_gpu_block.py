@@ -269,3 +269,33 @@ def test_stack_graph_key_mismatch(gpu_lib):
     assert e.value.code == B.DIT_ERR_GRAPH_KEY
     torch.cuda.synchronize()
     st.close()
+
+
+def test_stack_probes_time_kernels_without_changing_results(gpu_lib):
+    import torch
+    B = gpu_lib
+    shape = STACK_TINY
+    blocks, x, tembs = _stack_inputs(B, shape, 3, 2)
+    _, rc, rs = rope_dev(B, shape)
+    cfg = cfg_of(B, shape)
+    outs = []
+    for probe in (False, True):
+        ws = B.alloc_workspace(B.stack_workspace_bytes(cfg))
+        out = torch.empty(2, shape.seq_len, shape.dim, dtype=torch.bfloat16, device="cuda")
+        st = B.Stack()
+        if probe:
+            st.set_probe(B.Stack.KERNELS)
+        st.replay(cfg, [b.dev for b in blocks], dev_bf16(x), dev_bf16(tembs), rc, rs, out, ws)
+        torch.cuda.synchronize()
+        if probe:
+            pm = st.probe_ms(3)
+            assert set(pm) == set(B.Stack.KERNELS)
+            for k, v in pm.items():
+                assert len(v) == 3 and all(t > 0 for t in v), (k, v)
+            with pytest.raises(B.DitError):
+                st.probe_ms(3)  # nothing replayed since the last read
+            with pytest.raises(B.DitError):
+                st.set_probe(["attention"])  # after capture
+        st.close()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
