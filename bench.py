@@ -82,6 +82,35 @@ def time_launches(fn, iters, warm=2):
     return s.elapsed_time(e) / iters
 
 
+def time_graph(fn, iters, replays=3):
+    """Mean ms per launch of `iters` launches fn(0..iters-1) captured into one
+    graph and replayed: launch gaps are the graph's, not the Python loop's
+    (short kernels would otherwise be timed at the host's launch rate)."""
+    import torch
+    fn(0)
+    fn(1 % iters)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(iters):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / (replays * iters)
+    del g
+    return ms
+
+
 KERNEL_NAMES = ("modulation", "block_modulate_norm", "modulate_norm", "linear1_gelu", "qk_rmsnorm_rope",
                 "attention", "linear2_gated_residual", "gated_residual", "copy")
 
@@ -128,8 +157,8 @@ def block_sequence_times(B, blocks, x_in, temb, rc, rs, iters, only=None):
 def hbm_kernel_times(B, g, dev, it, only=None):
     """HBM rates of the memory-bound kernels at the chain shape: each launch
     works on one of 12 buffer sets (12 x 56.6 MB > the 256 MB last-level
-    cache), so the data comes from HBM.  Returns ({name: ms}, cache-warm ms
-    of modulate_norm)."""
+    cache), so the data comes from HBM; the launches are captured in a graph
+    and replayed.  Returns ({name: ms}, cache-warm ms of modulate_norm)."""
     import torch
     want = lambda n: only is None or n in only
     randn = lambda shape: torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
@@ -150,11 +179,11 @@ def hbm_kernel_times(B, g, dev, it, only=None):
         gvec = torch.randn(D, generator=g, device=dev) * 0.1
         n = max(it, 4 * nrot)
         if want("modulate_norm"):
-            k["modulate_norm"] = time_launches(
+            k["modulate_norm"] = time_graph(
                 lambda i: B.modulate_norm(xs[i % nrot], shift, scale, 1e-6, out=us[i % nrot]), n)
-            warm = time_launches(lambda i: B.modulate_norm(xs[0], shift, scale, 1e-6, out=us[0]), n)
+            warm = time_graph(lambda i: B.modulate_norm(xs[0], shift, scale, 1e-6, out=us[0]), n)
         if want("gated_residual"):
-            k["gated_residual"] = time_launches(
+            k["gated_residual"] = time_graph(
                 lambda i: B.gated_residual(xs[i % nrot], hs[i % nrot], gvec, out=us[i % nrot]), n)
     torch.cuda.synchronize()
     return k, warm
