@@ -5,20 +5,23 @@
 // softmax kernel.
 //
 // One workgroup = 4 wavefronts = 128 queries of one head; each wave owns 32
-// queries.  Keys/values stream through LDS in tiles of 64 tokens (double
-// buffered; the next tile's global loads are in flight during the current
-// tile's math).  Per tile and wave:
+// queries.  K and V stream through LDS in tiles of 64 tokens, double
+// buffered, filled by direct global->LDS loads (global_load_lds_dwordx4) that
+// are issued one tile ahead.  Both tiles keep the token-major layout of qkv
+// (rows of Dh bf16) with 16-byte chunks XOR-swizzled by row.  Per tile and
+// wave, in two halves of 32 keys:
 //   S^T = K Q^T   with v_mfma_f32_32x32x16_bf16 (Q stays in registers), so
-//                 every lane holds scores of ONE query: the row max / sum need
-//                 one cross-lane step (lanes l and l^32) instead of a 32-lane
-//                 reduction;
-//   online softmax in fp32 with exp2 and the 1/sqrt(Dh)*log2(e) scale folded;
+//                 every lane holds scores of ONE query: the row max needs one
+//                 exchange between lanes l and l^32 (v_permlane32_swap);
+//   online softmax in fp32 with exp2 and the 1/sqrt(Dh)*log2(e) scale folded
+//                 into one FMA; P is packed to bf16 (v_cvt_pk_bf16_f32);
 //   O^T += V^T P^T, where the P^T operand comes straight from the S^T
-//                 accumulator registers (rounded to bf16) and V^T is read from
-//                 an LDS copy of V stored transposed (8-byte units of 4 keys,
-//                 XOR-swizzled).  The key order inside each 16-key MFMA step
-//                 is permuted identically on both operands, which leaves the
-//                 contraction unchanged.
+//                 accumulator registers and the V^T operand is read from the
+//                 token-major V tile with ds_read_b64_tr_b16 (a transposing
+//                 LDS read: lane i of a 16-lane group receives element i of
+//                 four consecutive rows).  The key order inside each 16-key
+//                 MFMA step is permuted identically on both operands, which
+//                 leaves the contraction unchanged.
 #include "dit_common.hpp"
 #include "launch.hpp"
 
@@ -29,30 +32,57 @@ constexpr int ATT_BN = 64;   // keys per tile
 
 template <int DH>
 struct AttCfg {
-  static constexpr int K_BYTES = ATT_BN * DH * 2;  // K tile, rows of DH bf16
-  static constexpr int V_BYTES = ATT_BN * DH * 2;  // V^T tile, rows of ATT_BN bf16
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int KCH = DH / 8;                    // 16-byte chunks per K row
-  static constexpr int K_LD = ATT_BN * KCH / 256;       // K chunks per thread
-  static constexpr int V_GROUPS = (DH / 8) * (ATT_BN / 4);  // (8 dims x 4 keys) groups
+  static constexpr int ROW = DH * 2;                // bytes per token row
+  static constexpr int TILE = ATT_BN * ROW;         // one K or V tile
+  static constexpr int STAGE = 2 * TILE;            // K tile then V tile
+  static constexpr int KCH = DH / 8;                // 16-byte chunks per row
+  static constexpr int LPW = ATT_BN * KCH / 64 / 4;  // 1 KB wave-loads per wave per tile
+  static_assert(KCH == 8 || KCH == 16, "head_dim 64 or 128");
 };
 
-__device__ __forceinline__ uint32_t bf_at(const u32x4& v, int e) {
-  return (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu);
+// Chunk swizzles.  K is read 16 rows x one chunk per 256 bytes of LDS banks,
+// so the 16 rows of a read phase must land on 16 distinct chunk positions;
+// V is read 4 rows x one 64-byte group, so the 4 rows must land on distinct
+// 64-byte bank groups.
+template <int KCH>
+__device__ __forceinline__ int k_swz(int row) { return KCH == 16 ? (row & 15) : ((row >> 1) & 7); }
+template <int KCH>
+__device__ __forceinline__ int v_swz(int row) { return KCH == 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
+
+__device__ __forceinline__ void load_lds_16(const bf16_t* src, unsigned char* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_block, 16, 0, 0);
 }
+__device__ __forceinline__ u32x2 read_tr16(const unsigned char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p));
+}
+// max / sum of the values held by lanes l and l^32
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 template <int DH>
 __global__ void __launch_bounds__(256, 2)
 attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, int S, int H,
                      int ld_out, float c_log2) {
   using C = AttCfg<DH>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
+  constexpr int KCH = C::KCH;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int head = blockIdx.y;
   const int d = H * DH;
-  const size_t ld = size_t(3) * d;
+  const int ld = 3 * d;
   const bf16_t* Qg = qkv + head * DH;
   const bf16_t* Kg = qkv + d + head * DH;
   const bf16_t* Vg = qkv + 2 * d + head * DH;
@@ -68,48 +98,58 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
   for (int s = 0; s < DH / 16; ++s)
     qf[s] = *reinterpret_cast<const bf16x8*>(Qg + size_t(qc) * ld + 16 * s + 8 * hh);
 
-  // ---- K/V tile loaders
-  u32x4 rk[C::K_LD];
-  u32x4 rv[4];
-  const int vu = tid & 15;        // key group (keys 4*vu .. 4*vu+3)
-  const int ve = tid >> 4;        // dim group (dims 8*ve .. 8*ve+7)
-  const bool v_active = ve < DH / 8;
-  auto gload = [&](int t0) {
+  // ---- tile loads: wave-load w of a tile fills LDS chunks [64w, 64w + 64);
+  // chunk p holds row p / KCH, global chunk (p % KCH) ^ swz(row).
+  int koff[C::LPW], voff[C::LPW];
 #pragma unroll
-    for (int i = 0; i < C::K_LD; ++i) {
-      const int qd = tid + i * 256;
-      const int key = qd / C::KCH, c = qd % C::KCH;
-      const int tok = min(t0 + key, S - 1);
-      rk[i] = *reinterpret_cast<const u32x4*>(Kg + size_t(tok) * ld + 8 * c);
-    }
-    if (v_active) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int tok = min(t0 + 4 * vu + kk, S - 1);
-        rv[kk] = *reinterpret_cast<const u32x4*>(Vg + size_t(tok) * ld + 8 * ve);
-      }
-    }
-  };
-  auto lstore = [&](int stage) {
+  for (int i = 0; i < C::LPW; ++i) {
+    const int p = (wave * C::LPW + i) * 64 + lane;
+    const int row = p / KCH, cp = p % KCH;
+    koff[i] = row * ld + 8 * (cp ^ k_swz<KCH>(row));
+    voff[i] = row * ld + 8 * (cp ^ v_swz<KCH>(row));
+  }
+  auto issue = [&](int t0, int stage) {
     unsigned char* sK = smem + stage * C::STAGE;
-    unsigned char* sV = sK + C::K_BYTES;
+    unsigned char* sV = sK + C::TILE;
+    const bf16_t* kb = Kg + size_t(t0) * ld;
+    const bf16_t* vb = Vg + size_t(t0) * ld;
+    if (t0 + ATT_BN <= S) {
 #pragma unroll
-    for (int i = 0; i < C::K_LD; ++i) {
-      const int qd = tid + i * 256;
-      const int key = qd / C::KCH, c = qd % C::KCH;
-      *reinterpret_cast<u32x4*>(sK + key * (DH * 2) + ((c ^ (key & 7)) << 4)) = rk[i];
-    }
-    if (v_active) {
+      for (int i = 0; i < C::LPW; ++i) {
+        const int w = wave * C::LPW + i;
+        load_lds_16(kb + koff[i], sK + w * 1024);
+        load_lds_16(vb + voff[i], sV + w * 1024);
+      }
+    } else {
+      // ragged last tile: rows past the sequence re-read its last token
+      // (their scores are masked to -inf below)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dim = 8 * ve + e;
-        u32x2 w;
-        w[0] = bf_at(rv[0], e) | (bf_at(rv[1], e) << 16);
-        w[1] = bf_at(rv[2], e) | (bf_at(rv[3], e) << 16);
-        *reinterpret_cast<u32x2*>(sV + dim * (ATT_BN * 2) + ((vu ^ (dim & 15)) << 3)) = w;
+      for (int i = 0; i < C::LPW; ++i) {
+        const int w = wave * C::LPW + i;
+        const int row = (w * 64 + lane) / KCH;
+        const int back = (row - min(row, S - 1 - t0)) * ld;
+        load_lds_16(kb + koff[i] - back, sK + w * 1024);
+        load_lds_16(vb + voff[i] - back, sV + w * 1024);
       }
     }
   };
+
+  // LDS read offsets of this lane (bytes within a stage).
+  // K (A operand of S^T): row kb*32 + ql, chunk 2s + hh.
+  int kaddr[DH / 16];
+#pragma unroll
+  for (int s = 0; s < DH / 16; ++s) kaddr[s] = ql * C::ROW + (((2 * s + hh) ^ k_swz<KCH>(ql)) << 4);
+  // V (A operand of O^T via the transposing read): lane j of 16-lane group g
+  // points at row 4*(g >> 1) + (j >> 2) (+ 16m, + 8 for the second read) and
+  // dims 32b + 16*(g & 1) + 4*(j & 3).
+  const int g = lane >> 4, j = lane & 15;
+  const int vrow = 4 * (g >> 1) + (j >> 2);
+  int vaddr[DH / 32];
+#pragma unroll
+  for (int b = 0; b < DH / 32; ++b) {
+    const int dim = 32 * b + 16 * (g & 1) + 4 * (j & 3);
+    vaddr[b] = C::TILE + vrow * C::ROW + (((dim >> 3) ^ v_swz<KCH>(vrow)) << 4) + 2 * (dim & 7);
+  }
 
   f32x16 oacc[DH / 32];
 #pragma unroll
@@ -120,32 +160,26 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
   float l_run = 0.f;     // this lane's share of the running softmax denominator
 
   const int ntiles = (S + ATT_BN - 1) / ATT_BN;
-  gload(0);
-  lstore(0);
+  issue(0, 0);
+  wait_all();
   __syncthreads();
   for (int jt = 0; jt < ntiles; ++jt) {
     const int cur = jt & 1;
-    if (jt + 1 < ntiles) gload((jt + 1) * ATT_BN);
-    const unsigned char* sK = smem + cur * C::STAGE;
-    const unsigned char* sV = sK + C::K_BYTES;
-
-    // The tile is processed as two halves of 32 keys: S^T for keys
-    // [32*kb, 32*kb+32), online softmax, then O^T += V^T P^T for those keys.
+    if (jt + 1 < ntiles) issue((jt + 1) * ATT_BN, cur ^ 1);
+    const unsigned char* st = smem + cur * C::STAGE;
     const int key0 = jt * ATT_BN;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 kf[DH / 16];
+#pragma unroll
+      for (int s = 0; s < DH / 16; ++s)
+        kf[s] = *reinterpret_cast<const bf16x8*>(st + kb * 32 * C::ROW + kaddr[s]);
       f32x16 sacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-      {
-        const int key = kb * 32 + ql;
 #pragma unroll
-        for (int s = 0; s < DH / 16; ++s) {
-          const int c = 2 * s + hh;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + key * (DH * 2) + ((c ^ (key & 7)) << 4));
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc, 0, 0, 0);
-        }
-      }
+      for (int s = 0; s < DH / 16; ++s)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
       // accumulator row of register i: key 32*kb + 8*(i/4) + 4*hh + (i%4)
       if (key0 + ATT_BN > S) {
 #pragma unroll
@@ -155,7 +189,7 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
       float mx = sacc[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = xor32_max(mx);
       // Lazy rescale: the running max only moves (and O, l are rescaled) when
       // a score exceeds it by more than 2^8 in exp2 units for some lane of the
       // wave; otherwise the stale max stays, which is exact because numerator
@@ -174,29 +208,27 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
       bf16x8 pf[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        float p[8];
+        u32x4 pk;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = exp2_fast(fmaf(sacc[8 * half + j], c_log2, -mc));
-          l_run += p[j];
+        for (int t = 0; t < 4; ++t) {
+          const float e0 = exp2_fast(fmaf(sacc[8 * half + 2 * t], c_log2, -mc));
+          const float e1 = exp2_fast(fmaf(sacc[8 * half + 2 * t + 1], c_log2, -mc));
+          l_run += e0;
+          l_run += e1;
+          pk[t] = pack_bf2(e0, e1);
         }
-        u32x4 pk = pack8(p);
         pf[half] = __builtin_bit_cast(bf16x8, pk);
       }
-      // O^T += V^T P^T over the two 16-key steps m of this half: lane supplies
-      // keys 16m + 4hh + (0..3) and 16m + 8 + 4hh + (0..3), i.e. 8-byte units
-      // 4m+hh and 4m+2+hh of the V^T row.
+      // O^T += V^T P^T over the two 16-key steps of this half; step m covers
+      // keys 16m + 4hh + (0..3) and 16m + 8 + 4hh + (0..3) of the tile.
 #pragma unroll
-      for (int b = 0; b < DH / 32; ++b) {
-        const int dim = b * 32 + ql;
-        const unsigned char* row = sV + dim * (ATT_BN * 2);
+      for (int mh = 0; mh < 2; ++mh) {
+        const int m = 2 * kb + mh;
 #pragma unroll
-        for (int mh = 0; mh < 2; ++mh) {
-          const int m = 2 * kb + mh;
-          const int u1 = 4 * m + hh, u2 = 4 * m + 2 + hh;
+        for (int b = 0; b < DH / 32; ++b) {
+          const u32x2 lo = read_tr16(st + vaddr[b] + (16 * m) * C::ROW);
+          const u32x2 hi = read_tr16(st + vaddr[b] + (16 * m + 8) * C::ROW);
           u32x4 av;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row + ((u1 ^ (dim & 15)) << 3));
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + ((u2 ^ (dim & 15)) << 3));
           av[0] = lo[0];
           av[1] = lo[1];
           av[2] = hi[0];
@@ -206,23 +238,23 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
         }
       }
     }
-    if (jt + 1 < ntiles) lstore(cur ^ 1);
+    wait_all();
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = xor32_sum(l_run);
   const float inv = 1.0f / l_tot;
   if (q < S) {
     bf16_t* orow = out + size_t(q) * ld_out + head * DH;
 #pragma unroll
     for (int b = 0; b < DH / 32; ++b)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // registers 4g..4g+3 hold dims b*32 + 8g + 4hh + (0..3)
+      for (int gg = 0; gg < 4; ++gg) {
+        // registers 4gg..4gg+3 hold dims b*32 + 8gg + 4hh + (0..3)
         u32x2 w;
-        w[0] = pack_bf2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
-        w[1] = pack_bf2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * g + 4 * hh) = w;
+        w[0] = pack_bf2(oacc[b][4 * gg] * inv, oacc[b][4 * gg + 1] * inv);
+        w[1] = pack_bf2(oacc[b][4 * gg + 2] * inv, oacc[b][4 * gg + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * gg + 4 * hh) = w;
       }
   }
 }
