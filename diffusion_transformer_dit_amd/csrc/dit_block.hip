@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -81,11 +82,23 @@ int dims_of(const dit_block_config* cfg, Dims* out) {
   return DIT_OK;
 }
 
+// Tensor pointers must be 16-byte aligned (the kernels use 16-byte vector and
+// direct-to-LDS accesses); NULL entries are skipped (optional tensors).
+int check_aligned(std::initializer_list<const void*> ps) {
+  int i = 0;
+  for (const void* p : ps) {
+    if (p && reinterpret_cast<uintptr_t>(p) % 16 != 0)
+      return fail(DIT_ERR_INVALID_ARG, "tensor pointer %d (%p) is not 16-byte aligned", i, p);
+    ++i;
+  }
+  return DIT_OK;
+}
+
 int check_weights(const dit_block_weights* w) {
   if (!w) return fail(DIT_ERR_INVALID_ARG, "weights is NULL");
   if (!w->w_mod || !w->w1 || !w->w2 || !w->q_norm_w || !w->k_norm_w)
     return fail(DIT_ERR_INVALID_ARG, "a required weight pointer is NULL");
-  return DIT_OK;
+  return check_aligned({w->w_mod, w->b_mod, w->w1, w->b1, w->w2, w->b2, w->q_norm_w, w->k_norm_w});
 }
 
 struct WsLayout {
@@ -183,6 +196,8 @@ extern "C" int dit_modulation(const dit_bf16* temb, const dit_bf16* w_mod, const
   if (!temb || !w_mod || !mod) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   if (dim <= 0 || temb_dim <= 0) return fail(DIT_ERR_INVALID_ARG, "dim=%lld temb_dim=%lld", (long long)dim, (long long)temb_dim);
   if (temb_dim % 8 != 0 || temb_dim > kMaxRowCols) return fail(DIT_ERR_UNSUPPORTED, "temb_dim=%lld", (long long)temb_dim);
+  int rc = check_aligned({temb, w_mod, b_mod, mod});
+  if (rc) return rc;
   if (3 * dim > kMaxInt) return fail(DIT_ERR_UNSUPPORTED, "dim too large");
   DIT_CHECK_HIP(dit::launch_modulation(temb, w_mod, b_mod, mod, int(3 * dim), int(temb_dim), as_stream(stream)), "modulation");
   return DIT_OK;
@@ -194,6 +209,7 @@ extern "C" int dit_modulate_norm(const dit_bf16* x, const float* shift, const fl
   if (rc) return rc;
   if (rows == 0) return DIT_OK;  // empty input: nothing to read or write
   if (!x || !shift || !scale || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({x, shift, scale, out}))) return rc;
   if (!(eps >= 0.f)) return fail(DIT_ERR_INVALID_ARG, "eps must be >= 0");
   DIT_CHECK_HIP(dit::launch_modulate_norm(x, shift, scale, out, int(rows), int(cols), eps, as_stream(stream)), "modulate_norm");
   return DIT_OK;
@@ -205,6 +221,7 @@ extern "C" int dit_gated_residual(const dit_bf16* x, const dit_bf16* h, const fl
   if (rc) return rc;
   if (rows == 0) return DIT_OK;
   if (!x || !h || !gate || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({x, h, gate, y}))) return rc;
   DIT_CHECK_HIP(dit::launch_gated_residual(x, h, gate, y, int(rows), int(cols), as_stream(stream)), "gated_residual");
   return DIT_OK;
 }
@@ -215,6 +232,7 @@ extern "C" int dit_linear1_gelu(const dit_bf16* u, const dit_bf16* w1, const dit
   if (rc) return rc;
   if (seq_len == 0) return DIT_OK;
   if (!u || !w1 || !qkv || !cat) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({u, w1, b1, qkv, cat}))) return rc;
   DIT_CHECK_HIP(dit::launch_linear1(u, w1, b1, qkv, cat, int(seq_len), int(dim), int(mlp_hidden), as_stream(stream)), "linear1");
   return DIT_OK;
 }
@@ -226,6 +244,7 @@ extern "C" int dit_qk_rmsnorm_rope(dit_bf16* qkv, const float* q_norm_w, const f
   if (rc) return rc;
   if (seq_len == 0) return DIT_OK;
   if (!qkv || !q_norm_w || !k_norm_w || !rope_cos || !rope_sin) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({qkv, q_norm_w, k_norm_w, rope_cos, rope_sin}))) return rc;
   if (!(eps >= 0.f)) return fail(DIT_ERR_INVALID_ARG, "eps must be >= 0");
   DIT_CHECK_HIP(dit::launch_qk_rmsnorm_rope(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, int(seq_len),
                                             int(num_heads), int(head_dim), eps, as_stream(stream)), "qk_rmsnorm_rope");
@@ -238,6 +257,7 @@ extern "C" int dit_attention(const dit_bf16* qkv, dit_bf16* out, int64_t seq_len
   if (rc) return rc;
   if (seq_len == 0) return DIT_OK;
   if (!qkv || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({qkv, out}))) return rc;
   if (ld_out < num_heads * head_dim || ld_out % 4 != 0 || ld_out > kMaxInt)
     return fail(DIT_ERR_INVALID_ARG, "ld_out=%lld must be >= H*Dh and a multiple of 4", (long long)ld_out);
   DIT_CHECK_HIP(dit::launch_attention(qkv, out, int(seq_len), int(num_heads), int(head_dim), int(ld_out),
@@ -252,6 +272,7 @@ extern "C" int dit_linear2_gated_residual(const dit_bf16* cat, const dit_bf16* w
   if (rc) return rc;
   if (seq_len == 0) return DIT_OK;
   if (!cat || !w2 || !x || !gate || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({cat, w2, b2, x, gate, y}))) return rc;
   DIT_CHECK_HIP(dit::launch_linear2(cat, w2, b2, x, gate, y, int(seq_len), int(dim), int(mlp_hidden),
                                     as_stream(stream)), "linear2");
   return DIT_OK;
@@ -270,6 +291,7 @@ extern "C" int dit_rope_table(const int32_t* positions, int64_t seq_len, int32_t
     sum += axes_dims[a];
   }
   if (sum != head_dim) return fail(DIT_ERR_INVALID_ARG, "axes_dims sum to %lld, head_dim is %lld", (long long)sum, (long long)head_dim);
+  if (int rc = check_aligned({rope_cos, rope_sin})) return rc;
   DIT_CHECK_HIP(dit::launch_rope_table(positions, int(seq_len), n_axes, axes_dims, int(head_dim), base, rope_cos,
                                        rope_sin, as_stream(stream)), "rope_table");
   return DIT_OK;
@@ -290,6 +312,7 @@ extern "C" int dit_block_forward(const dit_block_config* cfg, const dit_block_we
   if (rc) return rc;
   if ((rc = check_weights(w))) return rc;
   if (!x || !temb || !rope_cos || !rope_sin || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({x, temb, rope_cos, rope_sin, y}))) return rc;
   const WsLayout L = layout(D);
   if (!workspace || ws_bytes < L.block_end)
     return fail(DIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.block_end);
@@ -381,6 +404,7 @@ extern "C" int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, cons
   for (int b = 0; b < n_blocks; ++b)
     if ((rc = check_weights(&blocks[b]))) return rc;
   if (!x_in || !temb_steps || !rope_cos || !rope_sin || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({x_in, temb_steps, rope_cos, rope_sin, out}))) return rc;
   const WsLayout L = layout(D);
   if (!workspace || ws_bytes < L.stack_end)
     return fail(DIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.stack_end);

@@ -52,10 +52,12 @@ struct TileCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
 };
 
-// Swizzle of 16-byte chunk positions inside a 64-byte row.  For the rows a
-// ds_read_b128 phase touches (8 consecutive rows with 32 banks, 16 with 64
-// banks) the 4-bank groups are all distinct.
-__device__ __forceinline__ int row_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+// Swizzle of 16-byte chunk positions inside a 64-byte row: chunk c of row r
+// sits at position c ^ ((r >> 1) & 3).  A fragment read (row = lane & 15,
+// chunk = lane >> 4) then touches every bank once per LDS cycle; measured
+// with SQ_LDS_BANK_CONFLICT, other XOR patterns (including one that also
+// folds in bit 3 of the row) leave one conflict cycle per two.
+__device__ __forceinline__ int row_swz(int r) { return (r >> 1) & 3; }
 
 // s_waitcnt vmcnt(VM) lgkmcnt(LGKM), expcnt unconstrained (gfx9 encoding;
 // LGKM = 15 leaves lgkmcnt unconstrained).
@@ -79,23 +81,39 @@ __device__ __forceinline__ void load_lds_16(const bf16_t* src, unsigned char* ld
   __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_block, 16, 0, 0);
 }
 
+// Epilogues act on 4 consecutive columns of one output row (the layout of
+// the transposed MFMA product, see the kernel): col(col0) loads what depends
+// only on the columns, store() finishes and writes one row's 4 values.
+struct Cols4 {
+  f32x4 a, b;
+};
+__device__ __forceinline__ f32x4 load_bf4(const bf16_t* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  return f32x4{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
+}
+__device__ __forceinline__ void store_bf4(bf16_t* p, const f32x4& v) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+}
+
 struct EpiLinear1 {
   const bf16_t* bias;
   bf16_t* qkv;
   bf16_t* cat;
   int M, N, split, d, ld_qkv, ld_cat;
-  __device__ __forceinline__ void operator()(int row0, int col, const f32x4& v) const {
-    if (col >= N) return;
-    const float b = bias ? bf2f(bias[col]) : 0.f;
-    if (col < split) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (row0 + i < M) qkv[size_t(row0 + i) * ld_qkv + col] = bf16_t(f2bf_bits(v[i] + b));
+  __device__ __forceinline__ Cols4 col(int col0) const {
+    Cols4 c;
+    c.a = (bias && col0 < N) ? load_bf4(bias + col0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    return c;
+  }
+  __device__ __forceinline__ void store(int row, int col0, const Cols4& c, const f32x4& v) const {
+    if (row >= M || col0 >= N) return;  // N and split are multiples of 64
+    f32x4 z = v + c.a;
+    if (col0 < split) {
+      store_bf4(qkv + size_t(row) * ld_qkv + col0, z);
     } else {
-      const int cc = d + (col - split);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (row0 + i < M) cat[size_t(row0 + i) * ld_cat + cc] = bf16_t(f2bf_bits(gelu_tanh(v[i] + b)));
+      for (int i = 0; i < 4; ++i) z[i] = gelu_tanh(z[i]);
+      store_bf4(cat + size_t(row) * ld_cat + d + (col0 - split), z);
     }
   }
 };
@@ -106,17 +124,20 @@ struct EpiLinear2 {
   const float* gate;
   bf16_t* y;
   int M, N;
-  __device__ __forceinline__ void operator()(int row0, int col, const f32x4& v) const {
-    if (col >= N) return;
-    const float b = bias ? bf2f(bias[col]) : 0.f;
-    const float g = gate[col];
+  __device__ __forceinline__ Cols4 col(int col0) const {
+    Cols4 c;
+    c.a = (bias && col0 < N) ? load_bf4(bias + col0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    c.b = col0 < N ? *reinterpret_cast<const f32x4*>(gate + col0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    return c;
+  }
+  __device__ __forceinline__ void store(int row, int col0, const Cols4& c, const f32x4& v) const {
+    if (row >= M || col0 >= N) return;
+    const size_t o = size_t(row) * N + col0;
+    const f32x4 xv = load_bf4(x + o);
+    f32x4 z;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (row0 + i < M) {
-        const size_t o = size_t(row0 + i) * N + col;
-        y[o] = bf16_t(f2bf_bits(bf2f(x[o]) + g * (v[i] + b)));
-      }
-    }
+    for (int i = 0; i < 4; ++i) z[i] = fmaf(c.b[i], v[i] + c.a[i], xv[i]);
+    store_bf4(y + o, z);
   }
 };
 
@@ -213,7 +234,7 @@ gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, 
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag[i], frag[C::FM + j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag[C::FM + j], frag[i], acc[i][j], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
   };
   // Workgroup barrier after this wave's loads of all but the `ahead` most
@@ -258,12 +279,16 @@ gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, 
     }
   }
 
-  // C fragment layout (16x16): lane holds column (lane & 15), rows 4*(lane>>4) + i.
+  // The MFMAs compute the transposed product C^T = B A^T per 16x16 block, so
+  // lane l holds row (l & 15) of the block and its 4 consecutive columns
+  // 4*(l >> 4) + (0..3): one 8-byte store per block and lane.
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+  for (int j = 0; j < C::FN; ++j) {
+    const int col0 = n0 + wn * C::WN + j * 16 + 4 * fk;
+    const Cols4 c = epi.col(col0);
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-      epi(m0 + wm * C::WM + i * 16 + 4 * fk, n0 + wn * C::WN + j * 16 + fr, acc[i][j]);
+    for (int i = 0; i < C::FM; ++i) epi.store(m0 + wm * C::WM + i * 16 + fr, col0, c, acc[i][j]);
+  }
 }
 
 // ------------------------------------------------------------------ tile choice

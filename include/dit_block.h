@@ -15,6 +15,8 @@
  *     row-major.  Activations are token-major [S, features] with heads in
  *     contiguous column blocks; weights use the [out, in] layout.
  *   - dit_bf16 holds raw bfloat16 bits.  Vectors marked float are fp32.
+ *   - Device tensor pointers must be 16-byte aligned (every allocation from
+ *     the HIP or PyTorch allocators is); others give DIT_ERR_INVALID_ARG.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on `stream` and returns; none
  *     synchronises the host, and none allocates device memory.  The caller

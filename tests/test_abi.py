@@ -77,6 +77,24 @@ def test_invalid_arguments_are_rejected_before_hip(lib):
     assert "sum" in lib.dit_last_error().decode()
 
 
+def test_misaligned_tensor_pointers_are_rejected(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    P, Q = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)  # Q: 8-byte aligned only
+    assert lib.dit_modulate_norm(Q, P, P, P, 4, 64, 1e-6, None) == B.DIT_ERR_INVALID_ARG
+    assert "aligned" in lib.dit_last_error().decode()
+    assert lib.dit_gated_residual(P, P, Q, P, 4, 64, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_linear1_gelu(P, P, Q, P, P, 64, 128, 128, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_linear2_gated_residual(P, P, P, P, P, Q, 64, 128, 128, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_attention(P, Q, 64, 2, 64, 128, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_qk_rmsnorm_rope(P, P, P, Q, P, 64, 2, 64, 1e-6, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_modulation(P, Q, None, P, 64, 64, None) == B.DIT_ERR_INVALID_ARG
+    c = cfg()
+    w = B.BlockWeightsC(0x1000, 0, 0x1008, 0, 0x1000, 0, 0x1000, 0x1000)
+    need = B.block_workspace_bytes(c)
+    assert lib.dit_block_forward(ctypes.byref(c), ctypes.byref(w), P, P, P, P, P, P, need, None) \
+        == B.DIT_ERR_INVALID_ARG
+
+
 def test_block_forward_argument_checks(lib):
     from diffusion_transformer_dit_amd import binding as B
     P = ctypes.c_void_p(0x1000)
