@@ -6,15 +6,17 @@
 //
 // One workgroup = 4 wavefronts = 128 queries of one head; each wave owns 32
 // queries.  K and V stream through LDS in tiles of 64 tokens, double
-// buffered, filled by direct global->LDS loads (global_load_lds_dwordx4) that
-// are issued one tile ahead.  Both tiles keep the token-major layout of qkv
-// (rows of Dh bf16) with 16-byte chunks XOR-swizzled by row.  Per tile and
-// wave, in two halves of 32 keys:
+// buffered, filled by direct buffer->LDS loads (buffer_load_dwordx4 ... lds,
+// no VALU address work per load) issued one tile ahead.  Both tiles keep the
+// token-major layout of qkv (rows of Dh bf16) with 16-byte chunks
+// XOR-swizzled by row.  Per tile and wave, in two halves of 32 keys:
 //   S^T = K Q^T   with v_mfma_f32_32x32x16_bf16 (Q stays in registers), so
-//                 every lane holds scores of ONE query: the row max needs one
+//                 every lane holds scores of ONE query: a row max needs one
 //                 exchange between lanes l and l^32 (v_permlane32_swap);
 //   online softmax in fp32 with exp2 and the 1/sqrt(Dh)*log2(e) scale folded
-//                 into one FMA; P is packed to bf16 (v_cvt_pk_bf16_f32);
+//                 into one FMA, against a running max that is only
+//                 recomputed when the probabilities grow past 2^8; P is
+//                 packed to bf16 (v_cvt_pk_bf16_f32);
 //   O^T += V^T P^T, where the P^T operand comes straight from the S^T
 //                 accumulator registers and the V^T operand is read from the
 //                 token-major V tile with ds_read_b64_tr_b16 (a transposing
@@ -53,8 +55,14 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
 
-__device__ __forceinline__ void load_lds_16(const bf16_t* src, unsigned char* lds_block) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_block, 16, 0, 0);
+// Buffer descriptor over `bytes` bytes from `base` (raw, 32-bit data format):
+// loads at offsets past the range read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+// 16 bytes per lane from a buffer straight into LDS: lane i writes lds_block + 16 i
+__device__ __forceinline__ void buffer_load_lds_16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_block, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_block, 16, voff, 0, 0, 0);
 }
 __device__ __forceinline__ u32x2 read_tr16(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p));
@@ -63,6 +71,15 @@ __device__ __forceinline__ u32x2 read_tr16(const unsigned char* p) {
 __device__ __forceinline__ float xor32_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// pairwise sum of 16 values (a tree of depth 4 instead of a serial chain)
+__device__ __forceinline__ float sum16(const float* e) {
+  float s8[8], s4[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s8[i] = e[2 * i] + e[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s4[i] = s8[2 * i] + s8[2 * i + 1];
+  return (s4[0] + s4[1]) + (s4[2] + s4[3]);
 }
 __device__ __forceinline__ float xor32_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -79,13 +96,11 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS targets stay scalar
   const int head = blockIdx.y;
   const int d = H * DH;
   const int ld = 3 * d;
   const bf16_t* Qg = qkv + head * DH;
-  const bf16_t* Kg = qkv + d + head * DH;
-  const bf16_t* Vg = qkv + 2 * d + head * DH;
 
   const int ql = lane & 31;  // query column of this lane
   const int hh = lane >> 5;  // lane half
@@ -100,37 +115,27 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
 
   // ---- tile loads: wave-load w of a tile fills LDS chunks [64w, 64w + 64);
   // chunk p holds row p / KCH, global chunk (p % KCH) ^ swz(row).
+  // Byte offsets of this lane's chunks inside a tile (rows = tokens of the
+  // tile).  Each tile gets a descriptor whose range ends with the sequence,
+  // so the rows of a ragged last tile past S read as zero: their scores are
+  // masked to -inf and their V rows meet zero probabilities.
   int koff[C::LPW], voff[C::LPW];
 #pragma unroll
   for (int i = 0; i < C::LPW; ++i) {
     const int p = (wave * C::LPW + i) * 64 + lane;
     const int row = p / KCH, cp = p % KCH;
-    koff[i] = row * ld + 8 * (cp ^ k_swz<KCH>(row));
-    voff[i] = row * ld + 8 * (cp ^ v_swz<KCH>(row));
+    koff[i] = (row * ld + d + head * DH + 8 * (cp ^ k_swz<KCH>(row))) * 2;
+    voff[i] = (row * ld + 2 * d + head * DH + 8 * (cp ^ v_swz<KCH>(row))) * 2;
   }
   auto issue = [&](int t0, int stage) {
     unsigned char* sK = smem + stage * C::STAGE;
     unsigned char* sV = sK + C::TILE;
-    const bf16_t* kb = Kg + size_t(t0) * ld;
-    const bf16_t* vb = Vg + size_t(t0) * ld;
-    if (t0 + ATT_BN <= S) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(qkv + size_t(t0) * ld, uint32_t(S - t0) * uint32_t(ld) * 2u);
 #pragma unroll
-      for (int i = 0; i < C::LPW; ++i) {
-        const int w = wave * C::LPW + i;
-        load_lds_16(kb + koff[i], sK + w * 1024);
-        load_lds_16(vb + voff[i], sV + w * 1024);
-      }
-    } else {
-      // ragged last tile: rows past the sequence re-read its last token
-      // (their scores are masked to -inf below)
-#pragma unroll
-      for (int i = 0; i < C::LPW; ++i) {
-        const int w = wave * C::LPW + i;
-        const int row = (w * 64 + lane) / KCH;
-        const int back = (row - min(row, S - 1 - t0)) * ld;
-        load_lds_16(kb + koff[i] - back, sK + w * 1024);
-        load_lds_16(vb + voff[i] - back, sV + w * 1024);
-      }
+    for (int i = 0; i < C::LPW; ++i) {
+      const int w = wave * C::LPW + i;
+      buffer_load_lds_16(r, sK + w * 1024, koff[i]);
+      buffer_load_lds_16(r, sV + w * 1024, voff[i]);
     }
   };
 
@@ -186,15 +191,21 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
         for (int i = 0; i < 16; ++i)
           if (key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= S) sacc[i] = -INFINITY;
       }
-      float mx = sacc[0];
+      // Exponentials against the running max; the max of the scores is only
+      // taken when some lane's 16 probabilities sum past 2^8 (or overflow),
+      // i.e. a score rose well above the running max (always on the first
+      // tile).  Keeping a stale max is exact: numerator and denominator share
+      // it, and values up to 2^8 cannot overflow the fp32 sums.
+      float e[16];
+      float mc = m_run * c_log2;
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-      mx = xor32_max(mx);
-      // Lazy rescale: the running max only moves (and O, l are rescaled) when
-      // a score exceeds it by more than 2^8 in exp2 units for some lane of the
-      // wave; otherwise the stale max stays, which is exact because numerator
-      // and denominator use the same max and 2^8 cannot overflow fp32 sums.
-      if (__builtin_amdgcn_ballot_w64((mx - m_run) * c_log2 > 8.0f)) {
+      for (int i = 0; i < 16; ++i) e[i] = exp2_fast(fmaf(sacc[i], c_log2, -mc));
+      float hs = sum16(e);
+      if (__builtin_amdgcn_ballot_w64(!(hs <= 256.0f))) {
+        float mx = sacc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+        mx = xor32_max(mx);
         const float m_new = fmaxf(m_run, mx);
         const float alpha = exp2_fast((m_run - m_new) * c_log2);
         m_run = m_new;
@@ -203,20 +214,18 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
         for (int b = 0; b < DH / 32; ++b)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+        mc = m_run * c_log2;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) e[i] = exp2_fast(fmaf(sacc[i], c_log2, -mc));
+        hs = sum16(e);
       }
-      const float mc = m_run * c_log2;
+      l_run += hs;
       bf16x8 pf[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         u32x4 pk;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float e0 = exp2_fast(fmaf(sacc[8 * half + 2 * t], c_log2, -mc));
-          const float e1 = exp2_fast(fmaf(sacc[8 * half + 2 * t + 1], c_log2, -mc));
-          l_run += e0;
-          l_run += e1;
-          pk[t] = pack_bf2(e0, e1);
-        }
+        for (int t = 0; t < 4; ++t) pk[t] = pack_bf2(e[8 * half + 2 * t], e[8 * half + 2 * t + 1]);
         pf[half] = __builtin_bit_cast(bf16x8, pk);
       }
       // O^T += V^T P^T over the two 16-key steps of this half; step m covers
