@@ -155,13 +155,23 @@ int enqueue_block(const Dims& D, const dit_block_config* cfg, const dit_block_we
   DIT_CHECK_HIP(pre(1), "probe");
   DIT_CHECK_HIP(dit::launch_modulate_norm(x, mod, mod + D.d, u, D.S, D.d, cfg->ln_eps, st), "modulate_norm");
   DIT_CHECK_HIP(post(1), "probe");
-  DIT_CHECK_HIP(pre(2), "probe");
-  DIT_CHECK_HIP(dit::launch_linear1(u, w->w1, w->b1, qkv, cat, D.S, D.d, D.mlp, st), "linear1");
-  DIT_CHECK_HIP(post(2), "probe");
-  DIT_CHECK_HIP(pre(3), "probe");
-  DIT_CHECK_HIP(dit::launch_qk_rmsnorm_rope(qkv, w->q_norm_w, w->k_norm_w, rcos, rsin, D.S, D.H, D.Dh,
-                                            cfg->qk_eps, st), "qk_rmsnorm_rope");
-  DIT_CHECK_HIP(post(3), "probe");
+  if (dit::linear1_fuses_qk(D.S, D.d, D.mlp, D.Dh)) {
+    // the q/k RMSNorm + RoPE runs in linear1's epilogue (kernel 3 is empty)
+    DIT_CHECK_HIP(pre(2), "probe");
+    DIT_CHECK_HIP(dit::launch_linear1_qk(u, w->w1, w->b1, qkv, cat, D.S, D.d, D.mlp, w->q_norm_w, w->k_norm_w,
+                                         rcos, rsin, cfg->qk_eps, st), "linear1_qk");
+    DIT_CHECK_HIP(post(2), "probe");
+    DIT_CHECK_HIP(pre(3), "probe");
+    DIT_CHECK_HIP(post(3), "probe");
+  } else {
+    DIT_CHECK_HIP(pre(2), "probe");
+    DIT_CHECK_HIP(dit::launch_linear1(u, w->w1, w->b1, qkv, cat, D.S, D.d, D.mlp, st), "linear1");
+    DIT_CHECK_HIP(post(2), "probe");
+    DIT_CHECK_HIP(pre(3), "probe");
+    DIT_CHECK_HIP(dit::launch_qk_rmsnorm_rope(qkv, w->q_norm_w, w->k_norm_w, rcos, rsin, D.S, D.H, D.Dh,
+                                              cfg->qk_eps, st), "qk_rmsnorm_rope");
+    DIT_CHECK_HIP(post(3), "probe");
+  }
   DIT_CHECK_HIP(pre(4), "probe");
   DIT_CHECK_HIP(dit::launch_attention(qkv, cat, D.S, D.H, D.Dh, D.d + D.mlp, st), "attention");
   DIT_CHECK_HIP(post(4), "probe");

@@ -96,6 +96,7 @@ __device__ __forceinline__ void store_bf4(bf16_t* p, const f32x4& v) {
 }
 
 struct EpiLinear1 {
+  static constexpr bool kHeadNorm = false;
   const bf16_t* bias;
   bf16_t* qkv;
   bf16_t* cat;
@@ -118,7 +119,67 @@ struct EpiLinear1 {
   }
 };
 
+// linear1 whose q and k columns also get the per-head RMSNorm (weights qw,
+// kw over the 128 dims of a head) and the RoPE rotation of adjacent dim
+// pairs (tables [S, 64]) before they are stored: the whole head of a row is
+// in one wave when the wave owns 128 columns (the 256x256 tile).
+struct EpiLinear1QK : EpiLinear1 {
+  static constexpr bool kHeadNorm = true;
+  const float* qw;
+  const float* kw;
+  const float* rcos;
+  const float* rsin;
+  float eps;
+  // Rows row_base + 16 i (i < FM) of the 128-column head starting at column
+  // colw (< 2d); lane columns 4*fk + 16 j + (0..3) of block j.
+  template <int FM, int FN>
+  __device__ __forceinline__ void store_head(int row_base, int colw, int fk, const f32x4 (&acc)[FM][FN]) const {
+    static_assert(FN == 8, "one head of 128 columns per wave");
+    const float* w = colw < d ? qw : kw;
+    f32x4 wv[FN], bv[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int c = j * 16 + 4 * fk;  // column inside the head
+      wv[j] = *reinterpret_cast<const f32x4*>(w + c);
+      bv[j] = bias ? load_bf4(bias + colw + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = row_base + 16 * i;
+      const int rc = min(row, M - 1);
+      f32x4 z[FN];
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        z[j] = acc[i][j] + bv[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = fmaf(z[j][e], z[j][e], ss);
+      }
+      // the row's 128 values sit in lanes fr + 16 fk, fk = 0..3
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      const float r = __frsqrt_rn(ss * (1.0f / 128.0f) + eps);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int c = j * 16 + 4 * fk;
+        const f32x2 cs = *reinterpret_cast<const f32x2*>(rcos + size_t(rc) * 64 + c / 2);
+        const f32x2 sn = *reinterpret_cast<const f32x2*>(rsin + size_t(rc) * 64 + c / 2);
+        f32x4 n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) n[e] = z[j][e] * r * wv[j][e];
+        f32x4 o;
+        o[0] = n[0] * cs[0] - n[1] * sn[0];
+        o[1] = n[0] * sn[0] + n[1] * cs[0];
+        o[2] = n[2] * cs[1] - n[3] * sn[1];
+        o[3] = n[2] * sn[1] + n[3] * cs[1];
+        if (row < M) store_bf4(qkv + size_t(row) * ld_qkv + colw + c, o);
+      }
+    }
+  }
+};
+
 struct EpiLinear2 {
+  static constexpr bool kHeadNorm = false;
   const bf16_t* bias;
   const bf16_t* x;
   const float* gate;
@@ -282,6 +343,13 @@ gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, 
   // The MFMAs compute the transposed product C^T = B A^T per 16x16 block, so
   // lane l holds row (l & 15) of the block and its 4 consecutive columns
   // 4*(l >> 4) + (0..3): one 8-byte store per block and lane.
+  if constexpr (Epi::kHeadNorm && C::WN == 128) {
+    const int colw = n0 + wn * C::WN;  // a whole head: q or k columns get normalised and rotated
+    if (colw < 2 * epi.d) {
+      epi.template store_head<C::FM, C::FN>(m0 + wm * C::WM + fr, colw, fk, acc);
+      return;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) {
     const int col0 = n0 + wn * C::WN + j * 16 + 4 * fk;
@@ -357,6 +425,24 @@ hipError_t launch_linear1(const bf16_t* u, const bf16_t* w1, const bf16_t* b1, b
                           bf16_t* cat, int S, int d, int mlp, hipStream_t st) {
   EpiLinear1 e{b1, qkv, cat, S, 3 * d + mlp, 3 * d, d, 3 * d, d + mlp};
   return launch_gemm(u, w1, S, 3 * d + mlp, d, e, st);
+}
+
+bool linear1_fuses_qk(int S, int d, int mlp, int DH) {
+  return DH == 128 && S > 0 && choose_tile(S, 3 * d + mlp) == K256;
+}
+
+hipError_t launch_linear1_qk(const bf16_t* u, const bf16_t* w1, const bf16_t* b1, bf16_t* qkv, bf16_t* cat,
+                             int S, int d, int mlp, const float* qw, const float* kw, const float* rcos,
+                             const float* rsin, float eps, hipStream_t st) {
+  if (!linear1_fuses_qk(S, d, mlp, 128)) return hipErrorInvalidValue;
+  EpiLinear1QK e;
+  static_cast<EpiLinear1&>(e) = EpiLinear1{b1, qkv, cat, S, 3 * d + mlp, 3 * d, d, 3 * d, d + mlp};
+  e.qw = qw;
+  e.kw = kw;
+  e.rcos = rcos;
+  e.rsin = rsin;
+  e.eps = eps;
+  return launch_tile<T256>(u, w1, S, 3 * d + mlp, d, e, st);
 }
 
 hipError_t launch_linear2(const bf16_t* cat, const bf16_t* w2, const bf16_t* b2, const bf16_t* x,

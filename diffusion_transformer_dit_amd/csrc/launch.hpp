@@ -28,6 +28,12 @@ hipError_t launch_rope_table(const int32_t* pos, int S, int n_axes, const int32_
 // linear1: z = u W1^T + b1; cols < 3d -> qkv[S,3d]; cols >= 3d -> gelu -> cat[:, d + ...]
 hipError_t launch_linear1(const bf16_t* u, const bf16_t* w1, const bf16_t* b1, bf16_t* qkv,
                           bf16_t* cat, int S, int d, int mlp, hipStream_t st);
+// linear1 with the q/k RMSNorm + RoPE fused into its epilogue; only for the
+// shapes where linear1_fuses_qk() holds (head_dim 128, 256x256 tiles)
+bool linear1_fuses_qk(int S, int d, int mlp, int DH);
+hipError_t launch_linear1_qk(const bf16_t* u, const bf16_t* w1, const bf16_t* b1, bf16_t* qkv, bf16_t* cat,
+                             int S, int d, int mlp, const float* qw, const float* kw, const float* rcos,
+                             const float* rsin, float eps, hipStream_t st);
 // linear2: y = x + gate * (cat W2^T + b2)
 hipError_t launch_linear2(const bf16_t* cat, const bf16_t* w2, const bf16_t* b2, const bf16_t* x,
                           const float* gate, bf16_t* y, int S, int d, int mlp, hipStream_t st);
