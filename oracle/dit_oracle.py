@@ -25,7 +25,11 @@ Readings of what the pages leave open (all are documented with the tests):
     then RoPE on adjacent pairs (2j, 2j+1) with base 10000; the head dim is
     split in equal chunks, one per position axis, in axis order;
   * attention: no mask, scale 1/sqrt(head_dim), softmax over all tokens;
-  * GELU in its tanh form.
+  * GELU in its tanh form;
+  * chunked attention (the one-GPU math of ring attention): a chunk's
+    partial output is the softmax average over the chunk's keys alone, its
+    lse the natural log of the chunk's sum of exp(score); partials of
+    disjoint chunks are merged with weights exp(lse_c - lse).
 
 Parity status: every function below is pinned by the CPU tests in
 tests/test_oracle_pins.py against library routines, closed forms, invariants
@@ -174,6 +178,49 @@ def attention(q, k, v, num_heads, head_dim, q_rows=None):
             p = softmax_rows((q[rr, cs] @ kh.T) * scale)
             out[r0:r0 + len(rr), cs] = p @ vh
     return out
+
+
+# ------------------------------------------- chunked attention (one GPU)
+def attention_partial(q, k, v, num_heads, head_dim, kv_begin, kv_end, q_rows=None):
+    """Attention of the queries against the keys and values of tokens
+    [kv_begin, kv_end) only, with the chunk's log-sum-exp: the step one hop
+    of ring attention performs on its K/V shard (ChituDiffusion page,
+    sections 5 and 6.1: every hop yields a partial output and its lse, and
+    the hops are merged by lse).  Returns (o, lse): o [R, H*Dh] is the softmax
+    average over the chunk alone; lse [H, R] is ln sum_u exp(s_tu) over the
+    chunk with s = q.k / sqrt(Dh)."""
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)[kv_begin:kv_end]
+    v = np.asarray(v, F64)[kv_begin:kv_end]
+    rows = np.arange(q.shape[0]) if q_rows is None else np.asarray(q_rows)
+    out = np.empty((rows.shape[0], num_heads * head_dim), F64)
+    lse = np.empty((num_heads, rows.shape[0]), F64)
+    scale = 1.0 / np.sqrt(head_dim)
+    for h in range(num_heads):
+        cs = slice(h * head_dim, (h + 1) * head_dim)
+        s = (q[rows, cs] @ k[:, cs].T) * scale
+        mx = s.max(axis=1, keepdims=True)
+        e = np.exp(s - mx)
+        z = e.sum(axis=1, keepdims=True)
+        out[:, cs] = (e / z) @ v[:, cs]
+        lse[h] = (mx + np.log(z))[:, 0]
+    return out, lse
+
+
+def attention_merge(parts, num_heads, head_dim):
+    """Combine partial results (o_c, lse_c) of disjoint chunks: with
+    lse = ln sum_c exp(lse_c), o = sum_c exp(lse_c - lse) o_c, which is the
+    softmax average over the union of the chunks."""
+    lses = np.stack([np.asarray(l, F64) for _, l in parts])            # [C, H, R]
+    mx = lses.max(axis=0)
+    lse = mx + np.log(np.exp(lses - mx).sum(axis=0))                   # [H, R]
+    out = np.zeros_like(np.asarray(parts[0][0], F64))
+    for o_c, l_c in parts:
+        wgt = np.exp(np.asarray(l_c, F64) - lse)                       # [H, R]
+        for h in range(num_heads):
+            cs = slice(h * head_dim, (h + 1) * head_dim)
+            out[:, cs] += wgt[h][:, None] * np.asarray(o_c, F64)[:, cs]
+    return out, lse
 
 
 # ------------------------------------------------------------- whole block

@@ -190,6 +190,37 @@ def pin_attention(o):
     assert np.allclose(o.attention(q, k, v, H, Dh, q_rows=rows), o.attention(q, k, v, H, Dh)[rows], rtol=1e-13)
 
 
+def pin_attention_chunks(o):
+    # merging the chunks of any partition of the keys gives full attention
+    S, H, Dh = 29, 2, 8
+    q, k, v = (RNG.standard_normal((S, H * Dh)) * 1.5 for _ in range(3))
+    full = o.attention(q, k, v, H, Dh)
+    for bounds in ([0, 13, 29], [0, 1, 2, 10, 11, 29], [0, 4, 8, 12, 16, 20, 24, 28, 29]):
+        parts = [o.attention_partial(q, k, v, H, Dh, a, b) for a, b in zip(bounds[:-1], bounds[1:])]
+        merged, lse = o.attention_merge(parts, H, Dh)
+        assert np.allclose(merged, full, rtol=1e-12, atol=1e-12)
+        # the merged lse is the lse of the whole key range
+        assert np.allclose(lse, o.attention_partial(q, k, v, H, Dh, 0, S)[1], rtol=1e-13, atol=1e-13)
+    # lse against scipy on scores computed with plain loops
+    from scipy.special import logsumexp
+    _, lse = o.attention_partial(q, k, v, H, Dh, 5, 17)
+    for h in range(H):
+        for i in range(S):
+            sc = [sum(q[i, h * Dh + c] * k[j, h * Dh + c] for c in range(Dh)) / math.sqrt(Dh) for j in range(5, 17)]
+            assert abs(lse[h, i] - logsumexp(sc)) < 1e-12
+    # a one-key chunk returns that key's value row and its score
+    oc, lc = o.attention_partial(q, k, v, H, Dh, 6, 7)
+    assert np.allclose(oc, np.repeat(v[6:7], S, 0), atol=1e-14)
+    for h in range(H):
+        cs = slice(h * Dh, (h + 1) * Dh)
+        assert np.allclose(lc[h], q[:, cs] @ k[6, cs] / math.sqrt(Dh), rtol=1e-13)
+    # query rows restrict the output rows only
+    rows = np.array([28, 3])
+    oa, la = o.attention_partial(q, k, v, H, Dh, 2, 20)
+    ob, lb = o.attention_partial(q, k, v, H, Dh, 2, 20, q_rows=rows)
+    assert np.allclose(ob, oa[rows], rtol=1e-13) and np.allclose(lb, la[:, rows], rtol=1e-13)
+
+
 def torch_block(shape, w, x, temb, pos):
     """The block composed from PyTorch float64 library routines, RoPE done
     with complex numbers; an independent second writing of the same block."""
@@ -267,7 +298,8 @@ def pin_stack(o):
 
 
 PINS = [pin_layer_norm, pin_modulate, pin_gated_residual, pin_silu, pin_gelu, pin_linear,
-        pin_modulation, pin_rms_norm, pin_rope, pin_attention, pin_block, pin_round_bf16, pin_stack]
+        pin_modulation, pin_rms_norm, pin_rope, pin_attention, pin_attention_chunks, pin_block, pin_round_bf16,
+        pin_stack]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -370,6 +402,19 @@ def _mut_round_truncate(a):
     return (f.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
 
 
+def _mut_merge_plain_mean(parts, num_heads, head_dim):
+    out = sum(np.asarray(o_c, np.float64) for o_c, _ in parts) / len(parts)
+    lses = np.stack([np.asarray(l, np.float64) for _, l in parts])
+    return out, np.log(np.exp(lses).sum(0))
+
+
+def _mut_partial_lse_log2(q, k, v, num_heads, head_dim, kv_begin, kv_end, q_rows=None):
+    out, lse = _REAL_PARTIAL(q, k, v, num_heads, head_dim, kv_begin, kv_end, q_rows)
+    return out, lse / np.log(2.0)
+
+
+_REAL_PARTIAL = O.attention_partial
+
 MUTANTS = [
     ("round_bf16", _mut_round_truncate, pin_round_bf16),
     ("round_bf16", _mut_round_truncate, pin_stack),
@@ -383,6 +428,8 @@ MUTANTS = [
     ("rms_norm_heads", _mut_rms_whole_row, pin_rms_norm),
     ("gated_residual", _mut_gated_on_x, pin_gated_residual),
     ("silu", _mut_silu_sigmoid, pin_silu),
+    ("attention_merge", _mut_merge_plain_mean, pin_attention_chunks),
+    ("attention_partial", _mut_partial_lse_log2, pin_attention_chunks),
     # the same mistakes must also break the whole-block pin
     ("gelu_tanh", _mut_gelu_no_cubic, pin_block),
     ("rope_apply", _mut_rope_sign, pin_block),
