@@ -56,6 +56,8 @@ SIGNATURES = {
     "dit_stack_destroy": ([VP], ctypes.c_int),
     "dit_stack_workspace_bytes": ([VP], SZ),
     "dit_stack_replay": ([VP, VP, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
+    "dit_attention_partial": ([VP, I64, I64, I64, I64, I64, VP, VP, VP], ctypes.c_int),
+    "dit_attention_merge": ([VP, VP, I64, I64, I64, I64, VP, I64, VP], ctypes.c_int),
     "dit_stack_set_probe": ([VP, ctypes.c_uint32], ctypes.c_int),
     "dit_stack_probe_ms": ([VP, VP, ctypes.c_int], ctypes.c_int),
     "dit_last_error": ([], ctypes.c_char_p),
@@ -189,6 +191,37 @@ def attention(qkv, out, num_heads, head_dim, stream=None):
     if qkv.shape[1] != 3 * num_heads * head_dim or out.shape[0] != S:
         raise ValueError("shape mismatch")
     _check(_lib.dit_attention(_p(qkv), _p(out), S, num_heads, head_dim, out.shape[1], _stream(stream)))
+    return out
+
+
+def attention_partial(qkv, num_heads, head_dim, kv_begin, kv_end, o_part=None, lse=None, stream=None):
+    """(o_part [S, H*Dh] fp32, lse [H, S] fp32): attention of every query over keys [kv_begin, kv_end)."""
+    _need(qkv, BF16, "qkv", 2)
+    S = qkv.shape[0]
+    d = num_heads * head_dim
+    if qkv.shape[1] != 3 * d:
+        raise ValueError("shape mismatch")
+    o_part = torch.empty(S, d, dtype=F32T, device=qkv.device) if o_part is None else o_part
+    lse = torch.empty(num_heads, S, dtype=F32T, device=qkv.device) if lse is None else lse
+    _need(o_part, F32T, "o_part", 2)
+    _need(lse, F32T, "lse", 2)
+    if o_part.shape != (S, d) or lse.shape != (num_heads, S):
+        raise ValueError("output shape mismatch")
+    _check(_lib.dit_attention_partial(_p(qkv), S, num_heads, head_dim, kv_begin, kv_end, _p(o_part), _p(lse),
+                                      _stream(stream)))
+    return o_part, lse
+
+
+def attention_merge(o_parts, lses, out, num_heads, head_dim, stream=None):
+    """out[:, :H*Dh] <- lse-weighted merge of o_parts [C, S, H*Dh] fp32 with lses [C, H, S] fp32."""
+    _need(o_parts, F32T, "o_parts", 3)
+    _need(lses, F32T, "lses", 3)
+    _need(out, BF16, "out", 2)
+    C, S, d = o_parts.shape
+    if d != num_heads * head_dim or lses.shape != (C, num_heads, S) or out.shape[0] != S:
+        raise ValueError("shape mismatch")
+    _check(_lib.dit_attention_merge(_p(o_parts), _p(lses), C, S, num_heads, head_dim, _p(out), out.shape[1],
+                                    _stream(stream)))
     return out
 
 

@@ -87,10 +87,15 @@ __device__ __forceinline__ float xor32_sum(float v) {
 }
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-template <int DH>
+// PARTIAL: attend to keys [kv_begin, kv_end) only and write the chunk's
+// normalised output in fp32 to out_f32 [S, H*DH] and its log-sum-exp (natural
+// log) to lse [H, S], the per-hop step of ring attention; otherwise write
+// bf16 to out (row stride ld_out) over all keys.
+template <int DH, bool PARTIAL>
 __global__ void __launch_bounds__(256, 2)
-attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, int S, int H,
-                     int ld_out, float c_log2) {
+attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ out_f32,
+                     float* __restrict__ lse, int S, int H, int ld_out, float c_log2, int kv_begin,
+                     int kv_end) {
   using C = AttCfg<DH>;
   constexpr int KCH = C::KCH;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
@@ -116,8 +121,8 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
   // ---- tile loads: wave-load w of a tile fills LDS chunks [64w, 64w + 64);
   // chunk p holds row p / KCH, global chunk (p % KCH) ^ swz(row).
   // Byte offsets of this lane's chunks inside a tile (rows = tokens of the
-  // tile).  Each tile gets a descriptor whose range ends with the sequence,
-  // so the rows of a ragged last tile past S read as zero: their scores are
+  // tile).  Each tile gets a descriptor whose range ends with the key range,
+  // so the rows of a ragged last tile past it read as zero: their scores are
   // masked to -inf and their V rows meet zero probabilities.
   int koff[C::LPW], voff[C::LPW];
 #pragma unroll
@@ -130,7 +135,7 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
   auto issue = [&](int t0, int stage) {
     unsigned char* sK = smem + stage * C::STAGE;
     unsigned char* sV = sK + C::TILE;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(qkv + size_t(t0) * ld, uint32_t(S - t0) * uint32_t(ld) * 2u);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(qkv + size_t(t0) * ld, uint32_t(kv_end - t0) * uint32_t(ld) * 2u);
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int w = wave * C::LPW + i;
@@ -164,15 +169,15 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
   float m_run = -1e30f;  // running max of raw scores of this lane's query
   float l_run = 0.f;     // this lane's share of the running softmax denominator
 
-  const int ntiles = (S + ATT_BN - 1) / ATT_BN;
-  issue(0, 0);
+  const int ntiles = (kv_end - kv_begin + ATT_BN - 1) / ATT_BN;
+  issue(kv_begin, 0);
   wait_all();
   __syncthreads();
   for (int jt = 0; jt < ntiles; ++jt) {
     const int cur = jt & 1;
-    if (jt + 1 < ntiles) issue((jt + 1) * ATT_BN, cur ^ 1);
+    if (jt + 1 < ntiles) issue(kv_begin + (jt + 1) * ATT_BN, cur ^ 1);
     const unsigned char* st = smem + cur * C::STAGE;
-    const int key0 = jt * ATT_BN;
+    const int key0 = kv_begin + jt * ATT_BN;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       bf16x8 kf[DH / 16];
@@ -186,10 +191,10 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
       for (int s = 0; s < DH / 16; ++s)
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
       // accumulator row of register i: key 32*kb + 8*(i/4) + 4*hh + (i%4)
-      if (key0 + ATT_BN > S) {
+      if (key0 + ATT_BN > kv_end) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= S) sacc[i] = -INFINITY;
+          if (key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= kv_end) sacc[i] = -INFINITY;
       }
       // Exponentials against the running max; the max of the scores is only
       // taken when some lane's 16 probabilities sum past 2^8 (or overflow),
@@ -254,18 +259,64 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, i
   const float l_tot = xor32_sum(l_run);
   const float inv = 1.0f / l_tot;
   if (q < S) {
-    bf16_t* orow = out + size_t(q) * ld_out + head * DH;
+    if constexpr (PARTIAL) {
+      float* orow = out_f32 + size_t(q) * d + head * DH;
 #pragma unroll
-    for (int b = 0; b < DH / 32; ++b)
+      for (int b = 0; b < DH / 32; ++b)
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        // registers 4gg..4gg+3 hold dims b*32 + 8gg + 4hh + (0..3)
-        u32x2 w;
-        w[0] = pack_bf2(oacc[b][4 * gg] * inv, oacc[b][4 * gg + 1] * inv);
-        w[1] = pack_bf2(oacc[b][4 * gg + 2] * inv, oacc[b][4 * gg + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * gg + 4 * hh) = w;
-      }
+        for (int gg = 0; gg < 4; ++gg) {
+          // registers 4gg..4gg+3 hold dims b*32 + 8gg + 4hh + (0..3)
+          const f32x4 w = {oacc[b][4 * gg] * inv, oacc[b][4 * gg + 1] * inv, oacc[b][4 * gg + 2] * inv,
+                           oacc[b][4 * gg + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + b * 32 + 8 * gg + 4 * hh) = w;
+        }
+      // scores in exp2 units are s * log2(e)/sqrt(Dh): lse = (m c + log2 l) ln 2
+      if (hh == 0) lse[size_t(head) * S + q] = (m_run * c_log2 + __log2f(l_tot)) * 0.6931471805599453f;
+    } else {
+      bf16_t* orow = out + size_t(q) * ld_out + head * DH;
+#pragma unroll
+      for (int b = 0; b < DH / 32; ++b)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          // registers 4gg..4gg+3 hold dims b*32 + 8gg + 4hh + (0..3)
+          u32x2 w;
+          w[0] = pack_bf2(oacc[b][4 * gg] * inv, oacc[b][4 * gg + 1] * inv);
+          w[1] = pack_bf2(oacc[b][4 * gg + 2] * inv, oacc[b][4 * gg + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * gg + 4 * hh) = w;
+        }
+    }
   }
+}
+
+// Merge of the partial results of disjoint key chunks: with
+// lse = ln sum_c exp(lse_c), out = sum_c exp(lse_c - lse) o_c.  One thread
+// owns 4 consecutive dims of one (token, head); the chunk weights are
+// recomputed by each of the head's DH/4 threads.
+__global__ void __launch_bounds__(256)
+attention_merge_kernel(const float* __restrict__ o_parts, const float* __restrict__ lses, int n_chunks, int S,
+                       int H, int DH, bf16_t* __restrict__ out, int ld_out) {
+  const int d = H * DH;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)S * (d / 4);
+  if (gid >= total) return;
+  const int t = int(gid / (d / 4));
+  const int c4 = int(gid % (d / 4)) * 4;  // first of the 4 dims
+  const int h = c4 / DH;
+  float mx = -INFINITY;
+  for (int c = 0; c < n_chunks; ++c) mx = fmaxf(mx, lses[(size_t(c) * H + h) * S + t]);
+  float z = 0.f;
+  for (int c = 0; c < n_chunks; ++c) z += exp2_fast((lses[(size_t(c) * H + h) * S + t] - mx) * kLog2e);
+  const float lz = mx + __log2f(z) * 0.6931471805599453f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < n_chunks; ++c) {
+    const float w = exp2_fast((lses[(size_t(c) * H + h) * S + t] - lz) * kLog2e);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(o_parts + (size_t(c) * S + t) * d + c4);
+    acc += w * o;
+  }
+  u32x2 wv;
+  wv[0] = pack_bf2(acc[0], acc[1]);
+  wv[1] = pack_bf2(acc[2], acc[3]);
+  *reinterpret_cast<u32x2*>(out + size_t(t) * ld_out + c4) = wv;
 }
 
 hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
@@ -274,11 +325,34 @@ hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH
   dim3 grid((S + ATT_BM - 1) / ATT_BM, H), block(256);
   const float c = kLog2e / sqrtf(float(DH));
   if (DH == 128)
-    attention_fwd_kernel<128><<<grid, block, 0, st>>>(qkv, out, S, H, ld_out, c);
+    attention_fwd_kernel<128, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S);
   else if (DH == 64)
-    attention_fwd_kernel<64><<<grid, block, 0, st>>>(qkv, out, S, H, ld_out, c);
+    attention_fwd_kernel<64, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_partial(const bf16_t* qkv, int S, int H, int DH, int kv_begin, int kv_end,
+                                    float* o_part, float* lse, hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  dim3 grid((S + ATT_BM - 1) / ATT_BM, H), block(256);
+  const float c = kLog2e / sqrtf(float(DH));
+  if (DH == 128)
+    attention_fwd_kernel<128, true><<<grid, block, 0, st>>>(qkv, nullptr, o_part, lse, S, H, 0, c, kv_begin, kv_end);
+  else if (DH == 64)
+    attention_fwd_kernel<64, true><<<grid, block, 0, st>>>(qkv, nullptr, o_part, lse, S, H, 0, c, kv_begin, kv_end);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_merge(const float* o_parts, const float* lses, int n_chunks, int S, int H, int DH,
+                                  bf16_t* out, int ld_out, hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  const long long total = (long long)S * (H * DH / 4);
+  attention_merge_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(o_parts, lses, n_chunks, S, H, DH, out,
+                                                                           ld_out);
   return hipGetLastError();
 }
 

@@ -275,6 +275,39 @@ extern "C" int dit_attention(const dit_bf16* qkv, dit_bf16* out, int64_t seq_len
   return DIT_OK;
 }
 
+extern "C" int dit_attention_partial(const dit_bf16* qkv, int64_t seq_len, int64_t num_heads, int64_t head_dim,
+                                     int64_t kv_begin, int64_t kv_end, float* o_part, float* lse, void* stream) {
+  int rc = check_dims(seq_len, num_heads * head_dim, num_heads, head_dim, 64, 8);
+  if (rc) return rc;
+  if (seq_len == 0) return DIT_OK;
+  if (!qkv || !o_part || !lse) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({qkv, o_part}))) return rc;
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return fail(DIT_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (kv_begin < 0 || kv_end <= kv_begin || kv_end > seq_len)
+    return fail(DIT_ERR_INVALID_ARG, "key range [%lld, %lld) must be non-empty and inside [0, %lld)",
+                (long long)kv_begin, (long long)kv_end, (long long)seq_len);
+  DIT_CHECK_HIP(dit::launch_attention_partial(qkv, int(seq_len), int(num_heads), int(head_dim), int(kv_begin),
+                                              int(kv_end), o_part, lse, as_stream(stream)), "attention_partial");
+  return DIT_OK;
+}
+
+extern "C" int dit_attention_merge(const float* o_parts, const float* lses, int64_t n_chunks, int64_t seq_len,
+                                   int64_t num_heads, int64_t head_dim, dit_bf16* out, int64_t ld_out,
+                                   void* stream) {
+  int rc = check_dims(seq_len, num_heads * head_dim, num_heads, head_dim, 64, 8);
+  if (rc) return rc;
+  if (n_chunks < 1 || n_chunks > 64) return fail(DIT_ERR_INVALID_ARG, "n_chunks=%lld not in [1, 64]", (long long)n_chunks);
+  if (seq_len == 0) return DIT_OK;
+  if (!o_parts || !lses || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({o_parts, out}))) return rc;
+  if (reinterpret_cast<uintptr_t>(lses) % 4 != 0) return fail(DIT_ERR_INVALID_ARG, "lses must be 4-byte aligned");
+  if (ld_out < num_heads * head_dim || ld_out % 4 != 0 || ld_out > kMaxInt)
+    return fail(DIT_ERR_INVALID_ARG, "ld_out=%lld must be >= H*Dh and a multiple of 4", (long long)ld_out);
+  DIT_CHECK_HIP(dit::launch_attention_merge(o_parts, lses, int(n_chunks), int(seq_len), int(num_heads),
+                                            int(head_dim), out, int(ld_out), as_stream(stream)), "attention_merge");
+  return DIT_OK;
+}
+
 extern "C" int dit_linear2_gated_residual(const dit_bf16* cat, const dit_bf16* w2, const dit_bf16* b2,
                                           const dit_bf16* x, const float* gate, dit_bf16* y, int64_t seq_len,
                                           int64_t dim, int64_t mlp_hidden, void* stream) {

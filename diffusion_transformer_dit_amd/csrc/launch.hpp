@@ -40,6 +40,12 @@ hipError_t launch_linear2(const bf16_t* cat, const bf16_t* w2, const bf16_t* b2,
 // attention over qkv [S, 3*H*DH] -> out [S, ld_out] columns [0, H*DH)
 hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
                             hipStream_t st);
+// attention over keys [kv_begin, kv_end): o_part [S, H*DH] fp32, lse [H, S] fp32
+hipError_t launch_attention_partial(const bf16_t* qkv, int S, int H, int DH, int kv_begin, int kv_end,
+                                    float* o_part, float* lse, hipStream_t st);
+// out[t, :H*DH] (row stride ld_out) = lse-weighted sum of n_chunks partials
+hipError_t launch_attention_merge(const float* o_parts, const float* lses, int n_chunks, int S, int H, int DH,
+                                  bf16_t* out, int ld_out, hipStream_t st);
 
 // timing probe channel ch[2]: finish == 0 stamps ch[0], else ch[1] += now - ch[0]
 hipError_t launch_probe_stamp(unsigned long long* ch, int finish, hipStream_t st);

@@ -125,6 +125,29 @@ int dit_qk_rmsnorm_rope(dit_bf16* qkv, const float* q_norm_w, const float* k_nor
 int dit_attention(const dit_bf16* qkv, dit_bf16* out, int64_t seq_len, int64_t num_heads,
                   int64_t head_dim, int64_t ld_out, void* stream);
 
+/* Chunked attention, the one-device math of ring attention (page
+ * "ChituDiffusion: torch.compile and CUDA Graph on Flux.1-dev", sections 5
+ * and 6.1: every hop attends to one K/V shard, yields a partial output and
+ * its log-sum-exp, and the hops are merged by log-sum-exp).
+ *
+ * dit_attention_partial: queries of all seq_len tokens of qkv (layout as in
+ * dit_attention) against the keys and values of tokens [kv_begin, kv_end)
+ * only.  o_part [seq_len, H*Dh] fp32 receives the softmax average over the
+ * chunk; lse [H, seq_len] fp32 receives ln sum_u exp(q.k_u / sqrt(Dh)) over
+ * the chunk.  0 <= kv_begin < kv_end <= seq_len, else DIT_ERR_INVALID_ARG.
+ * lse is written as scalars and needs only 4-byte alignment. */
+int dit_attention_partial(const dit_bf16* qkv, int64_t seq_len, int64_t num_heads, int64_t head_dim,
+                          int64_t kv_begin, int64_t kv_end, float* o_part, float* lse, void* stream);
+
+/* dit_attention_merge: o_parts holds n_chunks consecutive [seq_len, H*Dh]
+ * fp32 partials of disjoint key chunks and lses their n_chunks consecutive
+ * [H, seq_len] log-sum-exps; writes out[t, h*Dh + i] (bf16, row stride
+ * ld_out) = sum_c exp(lse_c - lse) o_c with lse = ln sum_c exp(lse_c), i.e.
+ * attention over the union of the chunks.  1 <= n_chunks <= 64; lses needs
+ * only 4-byte alignment. */
+int dit_attention_merge(const float* o_parts, const float* lses, int64_t n_chunks, int64_t seq_len,
+                        int64_t num_heads, int64_t head_dim, dit_bf16* out, int64_t ld_out, void* stream);
+
 /* linear2 with fused gated residual: y = x + gate * (cat . W2^T + b2).
  * cat [S, d+mlp]; w2 [d, d+mlp]; b2 [d] or NULL; x, y [S, d] (y may equal x);
  * gate [d] fp32. */

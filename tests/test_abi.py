@@ -95,6 +95,20 @@ def test_misaligned_tensor_pointers_are_rejected(lib):
         == B.DIT_ERR_INVALID_ARG
 
 
+def test_chunked_attention_argument_checks(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    P, Q = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)
+    assert lib.dit_attention_partial(P, 64, 2, 64, 10, 10, P, P, None) == B.DIT_ERR_INVALID_ARG  # empty range
+    assert lib.dit_attention_partial(P, 64, 2, 64, 0, 65, P, P, None) == B.DIT_ERR_INVALID_ARG   # past the end
+    assert lib.dit_attention_partial(P, 64, 2, 64, 0, 64, Q, P, None) == B.DIT_ERR_INVALID_ARG   # misaligned
+    assert lib.dit_attention_partial(P, 64, 3, 96, 0, 64, P, P, None) == B.DIT_ERR_UNSUPPORTED
+    assert lib.dit_attention_partial(None, 0, 2, 64, 0, 1, None, None, None) == B.DIT_OK         # empty input
+    assert lib.dit_attention_merge(P, P, 0, 64, 2, 64, P, 128, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_attention_merge(P, P, 65, 64, 2, 64, P, 128, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_attention_merge(P, P, 2, 64, 2, 64, P, 100, None) == B.DIT_ERR_INVALID_ARG   # ld_out
+    assert "ld_out" in lib.dit_last_error().decode()
+
+
 def test_block_forward_argument_checks(lib):
     from diffusion_transformer_dit_amd import binding as B
     P = ctypes.c_void_p(0x1000)

@@ -166,6 +166,74 @@ def test_attention_full_size_sampled(gpu_lib, S, H):
     assert_parity(host(out)[rows], ref, f"attention S={S} sampled")
 
 
+# ------------------------------------------ chunked attention + LSE merge
+@pytest.mark.parametrize("S,H,Dh,bounds", [
+    (333, 3, 128, [0, 100, 333]),                 # ragged chunks
+    (333, 3, 128, [0, 1, 17, 18, 200, 333]),      # one-token chunks
+    (256, 4, 64, [0, 64, 128, 192, 256]),         # tile-aligned, Dh = 64
+    (129, 2, 64, [0, 65, 129]),
+])
+def test_attention_partial_and_merge(gpu_lib, S, H, Dh, bounds):
+    import torch
+    B = gpu_lib
+    d = H * Dh
+    qkv = _qkv_for_attention(S, H, Dh, 34)
+    qd = dev_bf16(qkv)
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    C = len(bounds) - 1
+    o_parts = torch.empty(C, S, d, dtype=torch.float32, device="cuda")
+    lses = torch.empty(C, H, S, dtype=torch.float32, device="cuda")
+    for c, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        B.attention_partial(qd, H, Dh, a, b, o_part=o_parts[c], lse=lses[c])
+    torch.cuda.synchronize()
+    for c, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        ro, rl = O.attention_partial(q, k, v, H, Dh, a, b)
+        assert_parity(host(o_parts[c]), ro, f"partial o [{a},{b})", quantum=None)
+        gl = host(lses[c])
+        assert np.max(np.abs(gl - rl)) <= 1e-3 * max(1.0, float(np.max(np.abs(rl)))), (a, b)
+    out = torch.zeros(S, d + 64, dtype=torch.bfloat16, device="cuda")
+    B.attention_merge(o_parts, lses, out, H, Dh)
+    ref = O.attention(q, k, v, H, Dh)
+    g = host(out)
+    assert_parity(g[:, :d], ref, f"merged attention S={S} chunks={C}")
+    assert np.all(g[:, d:] == 0)  # columns past H*Dh untouched
+
+
+def test_attention_chunked_flux_eight_chunks(gpu_lib):
+    """The pages' 8-way split of the Flux sequence (8 x 576 keys), merged on one GPU."""
+    import torch
+    B = gpu_lib
+    S, H, Dh, C = 4608, 24, 128, 8
+    d = H * Dh
+    qkv = _qkv_for_attention(S, H, Dh, 35)
+    qd = dev_bf16(qkv)
+    o_parts = torch.empty(C, S, d, dtype=torch.float32, device="cuda")
+    lses = torch.empty(C, H, S, dtype=torch.float32, device="cuda")
+    for c in range(C):
+        B.attention_partial(qd, H, Dh, c * 576, (c + 1) * 576, o_part=o_parts[c], lse=lses[c])
+    out = torch.empty(S, d, dtype=torch.bfloat16, device="cuda")
+    B.attention_merge(o_parts, lses, out, H, Dh)
+    full = torch.empty(S, d, dtype=torch.bfloat16, device="cuda")
+    B.attention(qd, full, H, Dh)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, S, S // 23), [S - 1, 575, 576]]))
+    ref = O.attention(qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:], H, Dh, q_rows=rows)
+    assert_parity(host(out)[rows], ref, "merged attention flux 8x576")
+    # and against the single-pass kernel on every row: two bf16 results, each
+    # within the bar of the exact one, differ by at most twice the bar
+    st = assert_parity(host(out), host(full), "merged vs single-pass attention", check_max_abs=False)
+    assert st["excess"] <= 2 * 2e-2 * st["rms"], st
+
+
+def test_attention_partial_rejects_bad_ranges(gpu_lib):
+    import torch
+    B = gpu_lib
+    qd = dev_bf16(_qkv_for_attention(64, 1, 64, 36))
+    for a, b in ((0, 0), (10, 5), (-1, 10), (0, 65)):
+        with pytest.raises(B.DitError):
+            B.attention_partial(qd, 1, 64, a, b)
+
+
 # ------------------------------------------------------------ linear1 + GELU
 @pytest.mark.parametrize("S,d,mlp", [(300, 256, 1024), (4608, 3072, 12288), (97, 128, 192)])
 def test_linear1_gelu(gpu_lib, S, d, mlp):
