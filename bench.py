@@ -201,6 +201,36 @@ def hbm_kernel_times(B, g, dev, it, only=None):
     return k, warm
 
 
+def chunked_attention_times(B, g, dev, reps=3):
+    """The one-GPU math of the pages' ring attention at the Flux shape: 8 key
+    chunks of 576 tokens (dit_attention_partial) merged by log-sum-exp
+    (dit_attention_merge), against the single-pass kernel; and the share of
+    one rank under an 8-way head split (3 heads x 4608 tokens)."""
+    import torch
+    C = 8
+    qkv = (torch.randn(S, 3 * D, generator=g, device=dev, dtype=torch.float32)).to(torch.bfloat16)
+    o_parts = torch.empty(C, S, D, dtype=torch.float32, device=dev)
+    lses = torch.empty(C, H, S, dtype=torch.float32, device=dev)
+    out = torch.empty(S, D, dtype=torch.bfloat16, device=dev)
+    ck = S // C
+
+    def partials(i):
+        for c in range(C):
+            B.attention_partial(qkv, H, DH, c * ck, (c + 1) * ck, o_part=o_parts[c], lse=lses[c])
+
+    res = {"chunks": C, "chunk_tokens": ck}
+    res["partials_ms"] = time_graph(partials, 1, reps)
+    res["merge_ms"] = time_graph(lambda i: B.attention_merge(o_parts, lses, out, H, DH), 4, reps)
+    res["single_pass_ms"] = time_graph(lambda i: B.attention(qkv, out, H, DH), 4, reps)
+    hq = 3
+    qkv3 = (torch.randn(S, 3 * hq * DH, generator=g, device=dev, dtype=torch.float32)).to(torch.bfloat16)
+    out3 = torch.empty(S, hq * DH, dtype=torch.bfloat16, device=dev)
+    res["ulysses_share_3heads_ms"] = time_graph(lambda i: B.attention(qkv3, out3, hq, DH), 8, reps)
+    del o_parts, lses, qkv, qkv3
+    torch.cuda.synchronize()
+    return res
+
+
 def kernel_phase(B, g, dev, blocks, x_in, temb, rc, rs, it, only=None):
     """Block-sequence times of the six block kernels plus the HBM-rate loops."""
     k = block_sequence_times(B, blocks, x_in, temb, rc, rs, it, only)
@@ -411,6 +441,20 @@ def main():
                     "this_ms_per_57_block_step": round(ms_block * 57, 2),
                     "note": "H20 figures cover 19 double- and 38 single-stream Flux blocks; context only"},
     }
+    ca = chunked_attention_times(B, g, dev)
+    merge_bytes = ca["chunks"] * (S * D * 4 + H * S * 4) + S * D * 2
+    result["chunked_attention"] = {
+        "workload": "Flux attention (S=4608, 24x128) as 8 key chunks of 576 merged by log-sum-exp",
+        "partials_us": round(ca["partials_ms"] * 1e3, 1),
+        "partials_tflops": round(tf(ATTN_FLOP, ca["partials_ms"]), 1),
+        "merge_us": round(ca["merge_ms"] * 1e3, 1),
+        "merge_gbs": round(gbs(merge_bytes, ca["merge_ms"]), 1),
+        "single_pass_us": round(ca["single_pass_ms"] * 1e3, 1),
+        "ulysses_share_3_heads_us": round(ca["ulysses_share_3heads_ms"] * 1e3, 1),
+        "note": "outside the graph of the stack; partials write fp32 outputs that the merge reads back",
+    }
+    log(f"chunked attention: 8 partials {ca['partials_ms'] * 1e3:.1f} us + merge {ca['merge_ms'] * 1e3:.1f} us, "
+        f"single pass {ca['single_pass_ms'] * 1e3:.1f} us, 3-head share {ca['ulysses_share_3heads_ms'] * 1e3:.1f} us")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one Flux block ...")
         result["cpu_baseline"] = cpu_baseline()
