@@ -112,7 +112,7 @@ def time_graph(fn, iters, replays=3):
 
 
 KERNEL_NAMES = ("modulation", "block_modulate_norm", "modulate_norm", "linear1_gelu", "qk_rmsnorm_rope",
-                "attention", "linear2_gated_residual", "gated_residual", "copy")
+                "attention", "linear2_gated_residual", "gated_residual", "copy", "block_forward")
 
 
 def block_sequence_times(B, blocks, x_in, temb, rc, rs, iters, only=None):
@@ -236,6 +236,15 @@ def kernel_phase(B, g, dev, blocks, x_in, temb, rc, rs, it, only=None):
     k = block_sequence_times(B, blocks, x_in, temb, rc, rs, it, only)
     k2, warm = hbm_kernel_times(B, g, dev, it, only)
     k.update(k2)
+    if only is not None and "block_forward" in only:
+        # whole eager block forwards: the kernels as the stack launches them
+        # (at this shape linear1 carries the q/k RMSNorm + RoPE epilogue)
+        import torch
+        cfg = B.make_config(S, D, H, DH, MLP)
+        ws = B.alloc_workspace(B.block_workspace_bytes(cfg))
+        y = torch.empty_like(x_in)
+        k["block_forward"] = time_launches(
+            lambda i: B.block_forward(cfg, blocks[i % len(blocks)], x_in, temb[0], rc, rs, y=y, workspace=ws), it)
     for name, ms in k.items():
         log(f"kernel {name}: {ms * 1000:.1f} us")
     return k, warm
