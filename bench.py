@@ -231,6 +231,45 @@ def chunked_attention_times(B, g, dev, reps=3):
     return res
 
 
+def other_block_times(B, g, dev, reps=3):
+    """One block forward of the other block kinds, captured in a graph and
+    replayed: the two-stream (MMDiT) block at the Flux shape (512 text + 4096
+    image tokens, each stream with its own weights) and the sequential block
+    at the video shape (S=16384, d=1536, 12x128, MLP 8960, 3D RoPE)."""
+    import torch
+    import dit_inputs as DI
+
+    def rnd(shape, sigma=0.02):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * sigma).to(torch.bfloat16)
+
+    def stream(d, mlp, dh):
+        one = torch.ones(dh, device=dev)
+        return B.StreamWeights(rnd((6 * d, d)), rnd((6 * d,)), rnd((3 * d, d)), rnd((3 * d,)), one, one,
+                               rnd((d, d)), rnd((d,)), rnd((mlp, d)), rnd((mlp,)), rnd((d, mlp)), rnd((d,)))
+
+    res = {}
+    for name, sh, n_txt in (("mmdit_double_block", DI.FLUX_DOUBLE, 512), ("sequential_video_block", DI.VIDEO, 0)):
+        d, mlp, dh = sh.dim, sh.mlp_hidden, sh.head_dim
+        cfg = B.make_config(sh.seq_len, d, sh.num_heads, dh, mlp)
+        ws = B.alloc_workspace(B.mmdit_block_workspace_bytes(cfg))
+        pos = torch.from_numpy(DI.positions(sh)).to(dev)
+        rc, rs = B.rope_table(pos, list(sh.rope_axes_dims), dh)
+        x = rnd((sh.seq_len, d), 1.0)
+        temb = rnd((d,), 1.0)
+        y = torch.empty_like(x)
+        wi = stream(d, mlp, dh)
+        wt = stream(d, mlp, dh) if n_txt else None
+        ms = time_graph(lambda i: B.mmdit_block_forward(cfg, n_txt, wt, wi, x, temb, rc, rs, y=y, workspace=ws),
+                        4, reps)
+        S = sh.seq_len
+        flop = 2.0 * S * d * (4 * d + 2 * mlp) + 4.0 * sh.num_heads * S * S * dh + 2 * 6.0 * d * d * (2 if n_txt else 1)
+        res[name] = dict(S=S, text_tokens=n_txt, dim=d, heads=sh.num_heads, mlp_hidden=mlp, ms=round(ms, 4),
+                         gflop=round(flop / 1e9, 1), tflops=round(flop / (ms * 1e-3) / 1e12, 1))
+        del ws, x, y, wi, wt
+    torch.cuda.synchronize()
+    return res
+
+
 def kernel_phase(B, g, dev, blocks, x_in, temb, rc, rs, it, only=None):
     """Block-sequence times of the six block kernels plus the HBM-rate loops."""
     k = block_sequence_times(B, blocks, x_in, temb, rc, rs, it, only)
@@ -464,6 +503,11 @@ def main():
     }
     log(f"chunked attention: 8 partials {ca['partials_ms'] * 1e3:.1f} us + merge {ca['merge_ms'] * 1e3:.1f} us, "
         f"single pass {ca['single_pass_ms'] * 1e3:.1f} us, 3-head share {ca['ulysses_share_3heads_ms'] * 1e3:.1f} us")
+    ob = other_block_times(B, g, dev)
+    for v in ob.values():
+        v["note"] = "one block forward captured in a graph and replayed (same weights each replay)"
+    result["other_blocks"] = ob
+    log("other blocks: " + ", ".join(f"{n} {v['ms']:.3f} ms ({v['tflops']} TFLOP/s)" for n, v in ob.items()))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one Flux block ...")
         result["cpu_baseline"] = cpu_baseline()

@@ -39,6 +39,14 @@ class BlockWeightsC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w_mod", "b_mod", "w1", "b1", "w2", "b2", "q_norm_w", "k_norm_w")]
 
 
+STREAM_FIELDS = ("w_mod", "b_mod", "w_qkv", "b_qkv", "q_norm_w", "k_norm_w", "w_o", "b_o",
+                 "w_fc1", "b_fc1", "w_fc2", "b_fc2")
+
+
+class StreamWeightsC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in STREAM_FIELDS]
+
+
 VP, I64, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 
 SIGNATURES = {
@@ -52,6 +60,9 @@ SIGNATURES = {
     "dit_rope_table": ([VP, I64, I32, VP, I64, F32, VP, VP, VP], ctypes.c_int),
     "dit_block_workspace_bytes": ([VP], SZ),
     "dit_block_forward": ([VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
+    "dit_mmdit_block_workspace_bytes": ([VP], SZ),
+    "dit_mmdit_block_forward": ([VP, I64, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
+    "dit_sequential_block_forward": ([VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
     "dit_stack_create": ([VP], ctypes.c_int),
     "dit_stack_destroy": ([VP], ctypes.c_int),
     "dit_stack_workspace_bytes": ([VP], SZ),
@@ -273,6 +284,66 @@ class BlockWeights:
         _need(k_norm_w, F32T, "k_norm_w", 1)
         self.tensors = (w_mod, b_mod, w1, b1, w2, b2, q_norm_w, k_norm_w)
         self.c = BlockWeightsC(*[None if t is None else t.data_ptr() for t in self.tensors])
+
+
+class StreamWeights:
+    """Device weights of one stream of a two-stream (or sequential) block."""
+
+    def __init__(self, w_mod, b_mod, w_qkv, b_qkv, q_norm_w, k_norm_w, w_o, b_o, w_fc1, b_fc1, w_fc2, b_fc2):
+        for t, n in ((w_mod, "w_mod"), (w_qkv, "w_qkv"), (w_o, "w_o"), (w_fc1, "w_fc1"), (w_fc2, "w_fc2")):
+            _need(t, BF16, n, 2)
+        for t, n in ((b_mod, "b_mod"), (b_qkv, "b_qkv"), (b_o, "b_o"), (b_fc1, "b_fc1"), (b_fc2, "b_fc2")):
+            if t is not None:
+                _need(t, BF16, n, 1)
+        _need(q_norm_w, F32T, "q_norm_w", 1)
+        _need(k_norm_w, F32T, "k_norm_w", 1)
+        self.tensors = (w_mod, b_mod, w_qkv, b_qkv, q_norm_w, k_norm_w, w_o, b_o, w_fc1, b_fc1, w_fc2, b_fc2)
+        self.c = StreamWeightsC(*[None if t is None else t.data_ptr() for t in self.tensors])
+
+
+def mmdit_block_workspace_bytes(cfg: BlockConfig) -> int:
+    return int(_lib.dit_mmdit_block_workspace_bytes(ctypes.byref(cfg)))
+
+
+def mmdit_block_forward(cfg, txt_len, txt: "StreamWeights | None", img: StreamWeights, x, temb, rope_cos,
+                        rope_sin, y=None, workspace=None, stream=None):
+    """One two-stream block forward: rows [0, txt_len) of x are the text
+    tokens, the rest the image tokens; y may be x (in place)."""
+    _need(x, BF16, "x", 2)
+    _need(temb, BF16, "temb", 1)
+    _need(rope_cos, F32T, "rope_cos", 2)
+    _need(rope_sin, F32T, "rope_sin", 2)
+    y = torch.empty_like(x) if y is None else y
+    _need(y, BF16, "y", 2)
+    if x.shape != (cfg.seq_len, cfg.dim) or y.shape != x.shape:
+        raise ValueError("x / y shape does not match the config")
+    if workspace is None:
+        workspace = alloc_workspace(mmdit_block_workspace_bytes(cfg), x.device)
+    _check(_lib.dit_mmdit_block_forward(ctypes.byref(cfg), int(txt_len),
+                                        None if txt is None else ctypes.byref(txt.c),
+                                        None if img is None else ctypes.byref(img.c), _p(x), _p(temb),
+                                        _p(rope_cos), _p(rope_sin), _p(y), _p(workspace), workspace.numel(),
+                                        _stream(stream)))
+    return y
+
+
+def sequential_block_forward(cfg, w: StreamWeights, x, temb, rope_cos, rope_sin, y=None, workspace=None,
+                             stream=None):
+    """One sequential (single-stream-sequence, Wan-style) block forward."""
+    _need(x, BF16, "x", 2)
+    _need(temb, BF16, "temb", 1)
+    _need(rope_cos, F32T, "rope_cos", 2)
+    _need(rope_sin, F32T, "rope_sin", 2)
+    y = torch.empty_like(x) if y is None else y
+    _need(y, BF16, "y", 2)
+    if x.shape != (cfg.seq_len, cfg.dim) or y.shape != x.shape:
+        raise ValueError("x / y shape does not match the config")
+    if workspace is None:
+        workspace = alloc_workspace(mmdit_block_workspace_bytes(cfg), x.device)
+    _check(_lib.dit_sequential_block_forward(ctypes.byref(cfg), ctypes.byref(w.c), _p(x), _p(temb), _p(rope_cos),
+                                             _p(rope_sin), _p(y), _p(workspace), workspace.numel(),
+                                             _stream(stream)))
+    return y
 
 
 def block_workspace_bytes(cfg: BlockConfig) -> int:

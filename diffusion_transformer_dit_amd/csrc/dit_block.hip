@@ -1,6 +1,6 @@
-// C ABI of libdit_block: argument checks, the block schedule (six launches)
-// and the captured block stack.  Host code only; the kernels live in
-// elementwise.hip, gemm.hip and attention.hip.
+// C ABI of libdit_block: argument checks, the block schedules (single-stream,
+// two-stream and sequential blocks) and the captured block stack.  Host code
+// only; the kernels live in elementwise.hip, gemm.hip and attention.hip.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -178,6 +178,112 @@ int enqueue_block(const Dims& D, const dit_block_config* cfg, const dit_block_we
   DIT_CHECK_HIP(pre(5), "probe");
   DIT_CHECK_HIP(dit::launch_linear2(cat, w->w2, w->b2, x, mod + 2 * D.d, y, D.S, D.d, D.mlp, st), "linear2");
   DIT_CHECK_HIP(post(5), "probe");
+  return DIT_OK;
+}
+
+// ---------------------------------------------- two-stream / sequential blocks
+int check_stream_weights(const dit_stream_weights* w, const char* which) {
+  if (!w) return fail(DIT_ERR_INVALID_ARG, "%s weights are NULL", which);
+  if (!w->w_mod || !w->w_qkv || !w->q_norm_w || !w->k_norm_w || !w->w_o || !w->w_fc1 || !w->w_fc2)
+    return fail(DIT_ERR_INVALID_ARG, "a required %s weight pointer is NULL", which);
+  return check_aligned({w->w_mod, w->b_mod, w->w_qkv, w->b_qkv, w->q_norm_w, w->k_norm_w, w->w_o, w->b_o,
+                        w->w_fc1, w->b_fc1, w->w_fc2, w->b_fc2});
+}
+
+struct MmLayout {
+  size_t mod, u, qkv, o, x1, h, end;
+};
+
+MmLayout mm_layout(const Dims& D) {
+  MmLayout L;
+  size_t o = 0;
+  L.mod = o; o = align256(o + size_t(2) * 6 * D.d * sizeof(float));
+  L.u = o;   o = align256(o + size_t(D.S) * D.d * 2);
+  L.qkv = o; o = align256(o + size_t(D.S) * 3 * D.d * 2);
+  L.o = o;   o = align256(o + size_t(D.S) * D.d * 2);
+  L.x1 = o;  o = align256(o + size_t(D.S) * D.d * 4);
+  L.h = o;   o = align256(o + size_t(D.S) * D.mlp * 2);
+  L.end = o;
+  return L;
+}
+
+// The launches of one two-stream block on `st`: stream 0 = text rows
+// [0, T), stream 1 = image rows [T, S); empty streams are skipped.  Each
+// linear is one grouped launch over both streams.  The residual between the
+// attention and MLP halves (x') stays fp32.  x and y may alias.
+int enqueue_mmdit(const Dims& D, int T, const dit_block_config* cfg, const dit_stream_weights* wt,
+                  const dit_stream_weights* wi, const dit_bf16* x, const dit_bf16* temb, const float* rcos,
+                  const float* rsin, dit_bf16* y, unsigned char* ws, hipStream_t st) {
+  const MmLayout L = mm_layout(D);
+  const int d = D.d, mlp = D.mlp, half = D.Dh / 2;
+  float* mod0 = reinterpret_cast<float*>(ws + L.mod);
+  dit_bf16* u = reinterpret_cast<dit_bf16*>(ws + L.u);
+  dit_bf16* qkv = reinterpret_cast<dit_bf16*>(ws + L.qkv);
+  dit_bf16* o = reinterpret_cast<dit_bf16*>(ws + L.o);
+  float* x1 = reinterpret_cast<float*>(ws + L.x1);
+  dit_bf16* h = reinterpret_cast<dit_bf16*>(ws + L.h);
+  struct Stream {
+    const dit_stream_weights* w;
+    int r0, rows;
+    float* mod;
+  } ss[2];
+  int n = 0;
+  if (T > 0) ss[n++] = Stream{wt, 0, T, mod0};
+  if (D.S - T > 0) ss[n++] = Stream{wi, T, D.S - T, mod0 + 6 * d};
+  if (n == 0) return DIT_OK;
+  const size_t rd = size_t(d);
+  for (int i = 0; i < n; ++i)
+    DIT_CHECK_HIP(dit::launch_modulation(temb, ss[i].w->w_mod, ss[i].w->b_mod, ss[i].mod, 6 * d, D.tdim, st),
+                  "modulation");
+  for (int i = 0; i < n; ++i)
+    DIT_CHECK_HIP(dit::launch_modulate_norm(x + ss[i].r0 * rd, ss[i].mod, ss[i].mod + d, u + ss[i].r0 * rd,
+                                            ss[i].rows, d, cfg->ln_eps, st), "modulate_norm");
+  // q | k | v of both streams into one [S, 3d] buffer (text rows first)
+  dit::BiasActArgs qa[2];
+  dit::QKNormArgs qn[2];
+  for (int i = 0; i < n; ++i) {
+    const Stream& s = ss[i];
+    qa[i] = dit::BiasActArgs{u + s.r0 * rd, s.w->w_qkv, s.w->b_qkv, s.rows, 3 * d, d, 3 * d,
+                             qkv + s.r0 * 3 * rd, 3 * d, nullptr, 0, 0, d};
+    qn[i] = dit::QKNormArgs{s.w->q_norm_w, s.w->k_norm_w, rcos + size_t(s.r0) * half, rsin + size_t(s.r0) * half,
+                            cfg->qk_eps};
+  }
+  if (dit::bias_act_fuses_qk(qa, n, D.Dh)) {
+    DIT_CHECK_HIP(dit::launch_bias_act_qk_group(qa, qn, n, st), "qkv_qk");
+  } else {
+    DIT_CHECK_HIP(dit::launch_bias_act_group(qa, n, st), "qkv");
+    for (int i = 0; i < n; ++i)
+      DIT_CHECK_HIP(dit::launch_qk_rmsnorm_rope(qkv + ss[i].r0 * 3 * rd, qn[i].qw, qn[i].kw, qn[i].rcos, qn[i].rsin,
+                                                ss[i].rows, D.H, D.Dh, cfg->qk_eps, st), "qk_rmsnorm_rope");
+  }
+  DIT_CHECK_HIP(dit::launch_attention(qkv, o, D.S, D.H, D.Dh, d, st), "attention");
+  dit::GatedArgs ga[2];
+  float* x1s[2];
+  for (int i = 0; i < n; ++i) {
+    const Stream& s = ss[i];
+    ga[i] = dit::GatedArgs{o + s.r0 * rd, s.w->w_o, s.w->b_o, x + s.r0 * rd, s.mod + 2 * d, nullptr, s.rows, d, d};
+    x1s[i] = x1 + s.r0 * rd;
+  }
+  DIT_CHECK_HIP(dit::launch_gated_f32out_group(ga, x1s, n, st), "proj");
+  for (int i = 0; i < n; ++i)
+    DIT_CHECK_HIP(dit::launch_modulate_norm(static_cast<const float*>(x1s[i]), ss[i].mod + 3 * d,
+                                            ss[i].mod + 4 * d, u + ss[i].r0 * rd, ss[i].rows, d, cfg->ln_eps, st),
+                  "modulate_norm2");
+  dit::BiasActArgs fa[2];
+  for (int i = 0; i < n; ++i) {
+    const Stream& s = ss[i];
+    fa[i] = dit::BiasActArgs{u + s.r0 * rd, s.w->w_fc1, s.w->b_fc1, s.rows, mlp, d, 0, nullptr, 0,
+                             h + s.r0 * size_t(mlp), mlp, 0, 0};
+  }
+  DIT_CHECK_HIP(dit::launch_bias_act_group(fa, n, st), "fc1");
+  const float* x1c[2];
+  for (int i = 0; i < n; ++i) {
+    const Stream& s = ss[i];
+    ga[i] = dit::GatedArgs{h + s.r0 * size_t(mlp), s.w->w_fc2, s.w->b_fc2, nullptr, s.mod + 5 * d, y + s.r0 * rd,
+                           s.rows, d, mlp};
+    x1c[i] = x1s[i];
+  }
+  DIT_CHECK_HIP(dit::launch_gated_f32in_group(ga, x1c, n, st), "fc2");
   return DIT_OK;
 }
 
@@ -362,6 +468,42 @@ extern "C" int dit_block_forward(const dit_block_config* cfg, const dit_block_we
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(DIT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   return enqueue_block(D, cfg, w, x, temb, rope_cos, rope_sin, y, static_cast<unsigned char*>(workspace),
                        as_stream(stream));
+}
+
+// ================================================= two-stream / sequential blocks
+extern "C" size_t dit_mmdit_block_workspace_bytes(const dit_block_config* cfg) {
+  Dims D;
+  if (dims_of(cfg, &D)) return 0;
+  return mm_layout(D).end;
+}
+
+extern "C" int dit_mmdit_block_forward(const dit_block_config* cfg, int64_t txt_len, const dit_stream_weights* txt,
+                                       const dit_stream_weights* img, const dit_bf16* x, const dit_bf16* temb,
+                                       const float* rope_cos, const float* rope_sin, dit_bf16* y, void* workspace,
+                                       size_t ws_bytes, void* stream) {
+  Dims D;
+  int rc = dims_of(cfg, &D);
+  if (rc) return rc;
+  if (txt_len < 0 || txt_len > D.S)
+    return fail(DIT_ERR_INVALID_ARG, "txt_len=%lld outside [0, seq_len=%d]", (long long)txt_len, D.S);
+  const int T = int(txt_len);
+  if (T > 0 && (rc = check_stream_weights(txt, "text"))) return rc;
+  if (D.S - T > 0 && (rc = check_stream_weights(img, "image"))) return rc;
+  if (D.S == 0) return DIT_OK;
+  if (!x || !temb || !rope_cos || !rope_sin || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({x, temb, rope_cos, rope_sin, y}))) return rc;
+  const MmLayout L = mm_layout(D);
+  if (!workspace || ws_bytes < L.end) return fail(DIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.end);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(DIT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return enqueue_mmdit(D, T, cfg, txt, img, x, temb, rope_cos, rope_sin, y, static_cast<unsigned char*>(workspace),
+                       as_stream(stream));
+}
+
+extern "C" int dit_sequential_block_forward(const dit_block_config* cfg, const dit_stream_weights* w,
+                                            const dit_bf16* x, const dit_bf16* temb, const float* rope_cos,
+                                            const float* rope_sin, dit_bf16* y, void* workspace, size_t ws_bytes,
+                                            void* stream) {
+  return dit_mmdit_block_forward(cfg, 0, nullptr, w, x, temb, rope_cos, rope_sin, y, workspace, ws_bytes, stream);
 }
 
 // ============================================================== block stack

@@ -19,9 +19,35 @@ namespace dit {
 // keeps the per-column vectors (modulation / gate) in registers across them;
 // the next row's loads are issued before the current row is finished.
 // ------------------------------------------------------------------------
-template <int NCH>
+// 8 consecutive input values of a row: one 16-byte load of bf16, or two of fp32
+template <class TI>
+struct Chunk8;
+template <>
+struct Chunk8<bf16_t> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const bf16_t* row, int c) { v = reinterpret_cast<const u32x4*>(row)[c]; }
+  __device__ __forceinline__ void get(float* f) const { unpack8(v, f); }
+};
+template <>
+struct Chunk8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* row, int c) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(row) + 2 * c;
+    a = p[0];
+    b = p[1];
+  }
+  __device__ __forceinline__ void get(float* f) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = a[e];
+      f[4 + e] = b[e];
+    }
+  }
+};
+
+template <int NCH, class TI>
 __global__ void __launch_bounds__(256)
-ln_modulate_kernel(const bf16_t* __restrict__ x, const float* __restrict__ shift,
+ln_modulate_kernel(const TI* __restrict__ x, const float* __restrict__ shift,
                    const float* __restrict__ scale, bf16_t* __restrict__ out,
                    int rows, int cols, int rows_per_wave, float eps) {
   const int lane = threadIdx.x & 63;
@@ -50,18 +76,18 @@ ln_modulate_kernel(const bf16_t* __restrict__ x, const float* __restrict__ shift
   }
   const float inv_n = 1.0f / float(cols);
 
-  u32x4 cur[NCH], nxt[NCH];
+  Chunk8<TI> cur[NCH], nxt[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = lane + 64 * j;
-    if (c < nchunk) cur[j] = reinterpret_cast<const u32x4*>(x + size_t(r0) * cols)[c];
+    if (c < nchunk) cur[j].load(x + size_t(r0) * cols, c);
   }
   for (int r = r0; r < r1; ++r) {
     if (r + 1 < r1) {
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = lane + 64 * j;
-        if (c < nchunk) nxt[j] = reinterpret_cast<const u32x4*>(x + size_t(r + 1) * cols)[c];
+        if (c < nchunk) nxt[j].load(x + size_t(r + 1) * cols, c);
       }
     }
     float v[NCH][8];
@@ -70,7 +96,7 @@ ln_modulate_kernel(const bf16_t* __restrict__ x, const float* __restrict__ shift
     for (int j = 0; j < NCH; ++j) {
       const int c = lane + 64 * j;
       if (c < nchunk) {
-        unpack8(cur[j], v[j]);
+        cur[j].get(v[j]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s += v[j][e];
       } else {
@@ -294,8 +320,9 @@ static int rows_per_wave_for(int rows, int target_waves) {
   return rpw < 1 ? 1 : rpw;
 }
 
-hipError_t launch_modulate_norm(const bf16_t* x, const float* shift, const float* scale,
-                                bf16_t* out, int rows, int cols, float eps, hipStream_t st) {
+template <class TI>
+static hipError_t launch_ln_modulate(const TI* x, const float* shift, const float* scale, bf16_t* out, int rows,
+                                     int cols, float eps, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const int nch = (cols / 8 + 63) / 64;
   const int rpw = rows_per_wave_for(rows, 2048);
@@ -303,13 +330,23 @@ hipError_t launch_modulate_norm(const bf16_t* x, const float* shift, const float
   dim3 grid((waves + 3) / 4), block(256);
   switch (nch) {
 #define CASE(N) \
-  case N: ln_modulate_kernel<N><<<grid, block, 0, st>>>(x, shift, scale, out, rows, cols, rpw, eps); break;
+  case N: ln_modulate_kernel<N, TI><<<grid, block, 0, st>>>(x, shift, scale, out, rows, cols, rpw, eps); break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8) CASE(9) CASE(10) CASE(11) CASE(12)
     CASE(13) CASE(14) CASE(15) CASE(16)
 #undef CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_modulate_norm(const bf16_t* x, const float* shift, const float* scale,
+                                bf16_t* out, int rows, int cols, float eps, hipStream_t st) {
+  return launch_ln_modulate(x, shift, scale, out, rows, cols, eps, st);
+}
+
+hipError_t launch_modulate_norm(const float* x, const float* shift, const float* scale,
+                                bf16_t* out, int rows, int cols, float eps, hipStream_t st) {
+  return launch_ln_modulate(x, shift, scale, out, rows, cols, eps, st);
 }
 
 hipError_t launch_gated_residual(const bf16_t* x, const bf16_t* h, const float* gate, bf16_t* y,

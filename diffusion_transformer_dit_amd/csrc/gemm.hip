@@ -95,12 +95,16 @@ __device__ __forceinline__ void store_bf4(bf16_t* p, const f32x4& v) {
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
 }
 
+// Columns [0, split) of z = acc + bias go to qkv (row stride ld_qkv);
+// columns [split, N) go through GELU-tanh to cat at column gelu_col0 + (col -
+// split) (row stride ld_cat).  d is the width of q (and of k) for the head
+// norm of EpiLinear1QK.
 struct EpiLinear1 {
   static constexpr bool kHeadNorm = false;
   const bf16_t* bias;
   bf16_t* qkv;
   bf16_t* cat;
-  int M, N, split, d, ld_qkv, ld_cat;
+  int M, N, split, d, ld_qkv, ld_cat, gelu_col0;
   __device__ __forceinline__ Cols4 col(int col0) const {
     Cols4 c;
     c.a = (bias && col0 < N) ? load_bf4(bias + col0) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -114,7 +118,7 @@ struct EpiLinear1 {
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[i] = gelu_tanh(z[i]);
-      store_bf4(cat + size_t(row) * ld_cat + d + (col0 - split), z);
+      store_bf4(cat + size_t(row) * ld_cat + gelu_col0 + (col0 - split), z);
     }
   }
 };
@@ -202,14 +206,70 @@ struct EpiLinear2 {
   }
 };
 
-// Map the linear block id to a (tile_m, tile_n) pair.  Hardware deals block b
-// to XCD b % 8; consecutive ids on one XCD are regrouped into GROUP_M-tall
-// column-major patches of tiles.
-template <int GROUP_M>
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  int bid = blockIdx.x;
+// y = x + gate * (acc + bias) with the residual x and the output y of either
+// storage type (bf16 or fp32): the two-stream block keeps its mid-block
+// residual x' in fp32 between the attention and MLP halves.
+__device__ __forceinline__ f32x4 load4(const bf16_t* p) { return load_bf4(p); }
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) { store_bf4(p, v); }
+__device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+template <class XT, class YT>
+struct EpiGated {
+  static constexpr bool kHeadNorm = false;
+  const bf16_t* bias;
+  const XT* x;
+  const float* gate;
+  YT* y;
+  int M, N;
+  __device__ __forceinline__ Cols4 col(int col0) const {
+    Cols4 c;
+    c.a = (bias && col0 < N) ? load_bf4(bias + col0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    c.b = col0 < N ? *reinterpret_cast<const f32x4*>(gate + col0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    return c;
+  }
+  __device__ __forceinline__ void store(int row, int col0, const Cols4& c, const f32x4& v) const {
+    if (row >= M || col0 >= N) return;
+    const size_t o = size_t(row) * N + col0;
+    const f32x4 xv = load4(x + o);
+    f32x4 z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = fmaf(c.b[i], v[i] + c.a[i], xv[i]);
+    store4(y + o, z);
+  }
+};
+
+// One GEMM of a launch: C = A B^T with A [M, K], B [N, K], finished by epi.
+template <class Epi>
+struct GemmProblem {
+  const bf16_t* A;
+  const bf16_t* B;
+  int M, N, K;
+  Epi epi;
+};
+
+// NP independent GEMMs in one launch (e.g. the text and image streams of a
+// two-stream block): problem i owns tile ids [first[i], first[i + 1]) of the
+// XCD-remapped numbering, so the launch fills the chip once instead of
+// leaving it half idle for the smaller problem.
+template <class Epi, int NP>
+struct GemmGroup {
+  GemmProblem<Epi> p[NP];
+  int first[NP];  // first[0] == 0
+};
+
+// Hardware deals block b to XCD b % 8; the remap makes consecutive ids run on
+// one XCD, so that a problem's tiles stay together on an XCD.
+__device__ __forceinline__ int xcd_block_id() {
   const int nb = gridDim.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int bid = blockIdx.x;
+  return (nb & 7) == 0 ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
+}
+
+// Map a problem-local tile id to a (tile_m, tile_n) pair: consecutive ids
+// form GROUP_M-tall column-major patches of tiles sharing A and B panels.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int group = GROUP_M * tiles_n;
   const int g = bid / group;
   const int first_m = g * GROUP_M;
@@ -219,18 +279,27 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in / gsz;
 }
 
-template <class C, class Epi>
+template <class C, class Epi, int NP>
 __global__ void __launch_bounds__(C::NT, C::NW / 4)
-gemm_bf16_tn_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, int M, int N,
-                    int K, Epi epi) {
+gemm_bf16_tn_kernel(GemmGroup<Epi, NP> grp) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
+  int bid = xcd_block_id();
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < NP; ++i)
+    if (bid >= grp.first[i]) pi = i;
+  bid -= grp.first[pi];
+  const bf16_t* __restrict__ A = grp.p[pi].A;
+  const bf16_t* __restrict__ B = grp.p[pi].B;
+  const int M = grp.p[pi].M, N = grp.p[pi].N, K = grp.p[pi].K;
+  const Epi& epi = grp.p[pi].epi;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
   int tm, tn;
-  tile_coords<4>(tiles_m, tiles_n, tm, tn);
+  tile_coords<4>(bid, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
 
   // Direct-to-LDS loads.  Wave w issues wave-loads j = w, w + NW, ...; lane i
@@ -381,8 +450,9 @@ void prepare_device() { (void)num_cus(); }
 enum TileKind { K288x192 = 0, K256 = 1, K128 = 2 };
 
 // Pick the tile that minimises rounds-of-workgroups x tile area / efficiency
-// (a proxy for the time of the busiest CU).
-static TileKind choose_tile(int M, int N) {
+// (a proxy for the time of the busiest CU) over the tiles of all problems of
+// one launch.
+static TileKind choose_tile(const int* Ms, const int* Ns, int np) {
   const int cus = num_cus();
   struct Opt { TileKind k; int bm, bn; double eff; } opts[] = {
       // per-tile efficiency measured at the Flux shape (288x192 waves hold a
@@ -391,7 +461,8 @@ static TileKind choose_tile(int M, int N) {
   TileKind best = K128;
   double best_cost = 1e300;
   for (const Opt& o : opts) {
-    const long long tiles = (long long)((M + o.bm - 1) / o.bm) * ((N + o.bn - 1) / o.bn);
+    long long tiles = 0;
+    for (int i = 0; i < np; ++i) tiles += (long long)((Ms[i] + o.bm - 1) / o.bm) * ((Ns[i] + o.bn - 1) / o.bn);
     const long long rounds = (tiles + cus - 1) / cus;
     const double cost = double(rounds) * o.bm * o.bn / o.eff;
     if (cost < best_cost - 1e-9) {
@@ -401,13 +472,56 @@ static TileKind choose_tile(int M, int N) {
   }
   return best;
 }
+static TileKind choose_tile(int M, int N) { return choose_tile(&M, &N, 1); }
 
 template <class C, class Epi>
 static hipError_t launch_tile(const bf16_t* A, const bf16_t* B, int M, int N, int K, const Epi& e,
                               hipStream_t st) {
   const int tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
-  gemm_bf16_tn_kernel<C, Epi><<<tiles, C::NT, 0, st>>>(A, B, M, N, K, e);
+  GemmGroup<Epi, 1> g;
+  g.p[0] = GemmProblem<Epi>{A, B, M, N, K, e};
+  g.first[0] = 0;
+  gemm_bf16_tn_kernel<C, Epi, 1><<<tiles, C::NT, 0, st>>>(g);
   return hipGetLastError();
+}
+
+// One launch for np (1 or 2) problems on the tile config C; problems with
+// no rows or columns get no tiles.
+template <class C, class Epi>
+static hipError_t launch_tile_group(const GemmProblem<Epi>* ps, int np, hipStream_t st) {
+  GemmGroup<Epi, 2> g;
+  int n = 0, tiles = 0;
+  for (int i = 0; i < np; ++i) {
+    if (ps[i].M == 0 || ps[i].N == 0) continue;
+    g.p[n] = ps[i];
+    g.first[n] = tiles;
+    tiles += ((ps[i].M + C::BM - 1) / C::BM) * ((ps[i].N + C::BN - 1) / C::BN);
+    ++n;
+  }
+  if (n == 0) return hipSuccess;
+  if (n == 1) return launch_tile<C>(g.p[0].A, g.p[0].B, g.p[0].M, g.p[0].N, g.p[0].K, g.p[0].epi, st);
+  gemm_bf16_tn_kernel<C, Epi, 2><<<tiles, C::NT, 0, st>>>(g);
+  return hipGetLastError();
+}
+
+template <class Epi>
+static TileKind choose_group_tile(const GemmProblem<Epi>* ps, int np) {
+  int Ms[2], Ns[2];
+  for (int i = 0; i < np; ++i) {
+    Ms[i] = ps[i].M;
+    Ns[i] = ps[i].N;
+  }
+  return choose_tile(Ms, Ns, np);
+}
+
+template <class Epi>
+static hipError_t launch_gemm_group(const GemmProblem<Epi>* ps, int np, hipStream_t st) {
+  if (np < 1 || np > 2) return hipErrorInvalidValue;
+  switch (choose_group_tile(ps, np)) {
+    case K288x192: return launch_tile_group<T288x192>(ps, np, st);
+    case K256: return launch_tile_group<T256>(ps, np, st);
+    default: return launch_tile_group<T128>(ps, np, st);
+  }
 }
 
 template <class Epi>
@@ -423,7 +537,7 @@ static hipError_t launch_gemm(const bf16_t* A, const bf16_t* B, int M, int N, in
 
 hipError_t launch_linear1(const bf16_t* u, const bf16_t* w1, const bf16_t* b1, bf16_t* qkv,
                           bf16_t* cat, int S, int d, int mlp, hipStream_t st) {
-  EpiLinear1 e{b1, qkv, cat, S, 3 * d + mlp, 3 * d, d, 3 * d, d + mlp};
+  EpiLinear1 e{b1, qkv, cat, S, 3 * d + mlp, 3 * d, d, 3 * d, d + mlp, d};
   return launch_gemm(u, w1, S, 3 * d + mlp, d, e, st);
 }
 
@@ -436,7 +550,7 @@ hipError_t launch_linear1_qk(const bf16_t* u, const bf16_t* w1, const bf16_t* b1
                              const float* rsin, float eps, hipStream_t st) {
   if (!linear1_fuses_qk(S, d, mlp, 128)) return hipErrorInvalidValue;
   EpiLinear1QK e;
-  static_cast<EpiLinear1&>(e) = EpiLinear1{b1, qkv, cat, S, 3 * d + mlp, 3 * d, d, 3 * d, d + mlp};
+  static_cast<EpiLinear1&>(e) = EpiLinear1{b1, qkv, cat, S, 3 * d + mlp, 3 * d, d, 3 * d, d + mlp, d};
   e.qw = qw;
   e.kw = kw;
   e.rcos = rcos;
@@ -449,6 +563,75 @@ hipError_t launch_linear2(const bf16_t* cat, const bf16_t* w2, const bf16_t* b2,
                           const float* gate, bf16_t* y, int S, int d, int mlp, hipStream_t st) {
   EpiLinear2 e{b2, x, gate, y, S, d};
   return launch_gemm(cat, w2, S, d, d + mlp, e, st);
+}
+
+// ------------------------------------------------ grouped linears (1 or 2 problems)
+static EpiLinear1 bias_act_epi(const BiasActArgs& a) {
+  return EpiLinear1{a.b, a.plain, a.gelu, a.M, a.N, a.n_plain, a.qk_dim, a.ld_plain, a.ld_gelu, a.gelu_col0};
+}
+
+hipError_t launch_bias_act_group(const BiasActArgs* a, int np, hipStream_t st) {
+  if (np < 1 || np > 2) return hipErrorInvalidValue;
+  GemmProblem<EpiLinear1> ps[2];
+  for (int i = 0; i < np; ++i) ps[i] = GemmProblem<EpiLinear1>{a[i].A, a[i].W, a[i].M, a[i].N, a[i].K, bias_act_epi(a[i])};
+  return launch_gemm_group(ps, np, st);
+}
+
+bool bias_act_fuses_qk(const BiasActArgs* a, int np, int DH) {
+  if (DH != 128 || np < 1 || np > 2) return false;
+  int Ms[2], Ns[2];
+  for (int i = 0; i < np; ++i) {
+    if (a[i].qk_dim % 128 != 0 || 2 * a[i].qk_dim > a[i].n_plain) return false;
+    Ms[i] = a[i].M;
+    Ns[i] = a[i].N;
+  }
+  return choose_tile(Ms, Ns, np) == K256;
+}
+
+hipError_t launch_bias_act_qk_group(const BiasActArgs* a, const QKNormArgs* q, int np, hipStream_t st) {
+  if (!bias_act_fuses_qk(a, np, 128)) return hipErrorInvalidValue;
+  GemmProblem<EpiLinear1QK> ps[2];
+  for (int i = 0; i < np; ++i) {
+    EpiLinear1QK e;
+    static_cast<EpiLinear1&>(e) = bias_act_epi(a[i]);
+    e.qw = q[i].qw;
+    e.kw = q[i].kw;
+    e.rcos = q[i].rcos;
+    e.rsin = q[i].rsin;
+    e.eps = q[i].eps;
+    ps[i] = GemmProblem<EpiLinear1QK>{a[i].A, a[i].W, a[i].M, a[i].N, a[i].K, e};
+  }
+  return launch_tile_group<T256>(ps, np, st);
+}
+
+hipError_t launch_gated_group(const GatedArgs* a, int np, hipStream_t st) {
+  if (np < 1 || np > 2) return hipErrorInvalidValue;
+  GemmProblem<EpiLinear2> ps[2];
+  for (int i = 0; i < np; ++i)
+    ps[i] = GemmProblem<EpiLinear2>{a[i].A, a[i].W, a[i].M, a[i].N, a[i].K,
+                                    EpiLinear2{a[i].b, a[i].x, a[i].gate, a[i].y, a[i].M, a[i].N}};
+  return launch_gemm_group(ps, np, st);
+}
+
+template <class XT, class YT>
+static hipError_t gated_typed_group(const GatedArgs* a, int np, const XT* const* xs, YT* const* ys,
+                                    hipStream_t st) {
+  if (np < 1 || np > 2) return hipErrorInvalidValue;
+  GemmProblem<EpiGated<XT, YT>> ps[2];
+  for (int i = 0; i < np; ++i)
+    ps[i] = GemmProblem<EpiGated<XT, YT>>{a[i].A, a[i].W, a[i].M, a[i].N, a[i].K,
+                                          EpiGated<XT, YT>{a[i].b, xs[i], a[i].gate, ys[i], a[i].M, a[i].N}};
+  return launch_gemm_group(ps, np, st);
+}
+
+hipError_t launch_gated_f32out_group(const GatedArgs* a, float* const* y32, int np, hipStream_t st) {
+  const bf16_t* xs[2] = {a[0].x, np > 1 ? a[1].x : nullptr};
+  return gated_typed_group<bf16_t, float>(a, np, xs, y32, st);
+}
+
+hipError_t launch_gated_f32in_group(const GatedArgs* a, const float* const* x32, int np, hipStream_t st) {
+  bf16_t* ys[2] = {a[0].y, np > 1 ? a[1].y : nullptr};
+  return gated_typed_group<float, bf16_t>(a, np, x32, ys, st);
 }
 
 }  // namespace dit

@@ -17,6 +17,9 @@ hipError_t launch_modulation(const bf16_t* temb, const bf16_t* w, const bf16_t* 
                              int rows, int cols, hipStream_t st);
 hipError_t launch_modulate_norm(const bf16_t* x, const float* shift, const float* scale,
                                 bf16_t* out, int rows, int cols, float eps, hipStream_t st);
+// the same with an fp32 input x [rows, cols]
+hipError_t launch_modulate_norm(const float* x, const float* shift, const float* scale,
+                                bf16_t* out, int rows, int cols, float eps, hipStream_t st);
 hipError_t launch_gated_residual(const bf16_t* x, const bf16_t* h, const float* gate, bf16_t* y,
                                  int rows, int cols, hipStream_t st);
 hipError_t launch_qk_rmsnorm_rope(bf16_t* qkv, const float* qw, const float* kw, const float* rcos,
@@ -37,6 +40,48 @@ hipError_t launch_linear1_qk(const bf16_t* u, const bf16_t* w1, const bf16_t* b1
 // linear2: y = x + gate * (cat W2^T + b2)
 hipError_t launch_linear2(const bf16_t* cat, const bf16_t* w2, const bf16_t* b2, const bf16_t* x,
                           const float* gate, bf16_t* y, int S, int d, int mlp, hipStream_t st);
+// Grouped linears: one launch for 1 or 2 independent problems (the text and
+// image streams of a two-stream block), tiles of both spread over the chip.
+// z = A W^T + b with A [M, K], W [N, K]; columns [0, n_plain) -> plain (row
+// stride ld_plain), columns [n_plain, N) -> GELU-tanh -> gelu[:, gelu_col0 + ...]
+// (row stride ld_gelu).  qk_dim: width of q and of k for the fused head norm.
+struct BiasActArgs {
+  const bf16_t* A;
+  const bf16_t* W;
+  const bf16_t* b;
+  int M, N, K, n_plain;
+  bf16_t* plain;
+  int ld_plain;
+  bf16_t* gelu;
+  int ld_gelu, gelu_col0, qk_dim;
+};
+// per-head RMSNorm + RoPE of the q and k columns (tables [M, 64] for these rows)
+struct QKNormArgs {
+  const float* qw;
+  const float* kw;
+  const float* rcos;
+  const float* rsin;
+  float eps;
+};
+// y = x + gate * (A W^T + b), x and y [M, N] (may alias), gate [N] fp32
+struct GatedArgs {
+  const bf16_t* A;
+  const bf16_t* W;
+  const bf16_t* b;
+  const bf16_t* x;
+  const float* gate;
+  bf16_t* y;
+  int M, N, K;
+};
+hipError_t launch_bias_act_group(const BiasActArgs* a, int np, hipStream_t st);
+bool bias_act_fuses_qk(const BiasActArgs* a, int np, int DH);
+hipError_t launch_bias_act_qk_group(const BiasActArgs* a, const QKNormArgs* q, int np, hipStream_t st);
+hipError_t launch_gated_group(const GatedArgs* a, int np, hipStream_t st);
+// the same with an fp32 output y32[i] [M, N] (a[i].y unused) ...
+hipError_t launch_gated_f32out_group(const GatedArgs* a, float* const* y32, int np, hipStream_t st);
+// ... or with an fp32 residual x32[i] [M, N] (a[i].x unused)
+hipError_t launch_gated_f32in_group(const GatedArgs* a, const float* const* x32, int np, hipStream_t st);
+
 // attention over qkv [S, 3*H*DH] -> out [S, ld_out] columns [0, H*DH)
 hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
                             hipStream_t st);

@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the Flux-style single-stream DiT block.
+"""Seeded synthetic inputs for the Flux-style DiT blocks (single-stream,
+two-stream and sequential).
 
 This module is shared by the CPU oracle and by the GPU tests / bench.  It
 holds no arithmetic of the block itself: only the workload shapes, the
@@ -9,10 +10,12 @@ embedding.
 Workload shapes follow the page "ChituDiffusion compile_graph" (chenyy20.com),
 section 2 (one Flux single-stream block: S=4608, dim 3072, 24 heads x 128,
 bf16), and the workload list of this project (tiny block, memory-bound chain,
-Flux block, 57-block x 50-step replay, long-sequence video block).
+Flux block, 57-block x 50-step replay, long-sequence video block, and the
+two-stream block at the Flux shape with 512 text tokens).
 
 Seeding recipe: ``seed = 1000*cfg_index + tensor_id`` (+100*block for the
-stack, tensor id 10000+s for the temb of denoising step s); draws are
+stack, +50 for the image stream of a two-stream block, tensor id 10000+s for
+the temb of denoising step s); draws are
 ``numpy.random.default_rng(seed).standard_normal(dtype=float32) * sigma``,
 then rounded to bf16 with round-to-nearest-even.
 """
@@ -23,7 +26,10 @@ import numpy as np
 
 # tensor ids of the seeding recipe
 TID = dict(x=1, temb=2, w_mod=3, b_mod=4, w1=5, b1=6, w2=7, b2=8,
-           q_norm_w=9, k_norm_w=10, h=11, scale=12, shift=13, gate=14)
+           q_norm_w=9, k_norm_w=10, h=11, scale=12, shift=13, gate=14,
+           # weights of one stream of a two-stream / sequential block (+50 for stream 1)
+           w_mod6=15, b_mod6=16, w_qkv=17, b_qkv=18, w_o=19, b_o=20,
+           w_fc1=21, b_fc1=22, w_fc2=23, b_fc2=24)
 
 
 @dataclass(frozen=True)
@@ -63,7 +69,9 @@ CHAIN = BlockShape("chain", 1, 4608, 3072, 24, 128, 12288)
 FLUX = BlockShape("flux", 2, 4608, 3072, 24, 128, 12288, (64, 64), (64, 64), 512)
 STACK = BlockShape("stack", 3, 4608, 3072, 24, 128, 12288, (64, 64), (64, 64), 512)
 VIDEO = BlockShape("video", 4, 16384, 1536, 12, 128, 8960, (32, 48, 48), (16, 32, 32), 0)
-SHAPES = {s.name: s for s in (TINY, CHAIN, FLUX, STACK, VIDEO)}
+# two-stream block at the Flux shape: 512 text tokens then the 64x64 image grid
+FLUX_DOUBLE = BlockShape("flux_double", 5, 4608, 3072, 24, 128, 12288, (64, 64), (64, 64), 512)
+SHAPES = {s.name: s for s in (TINY, CHAIN, FLUX, STACK, VIDEO, FLUX_DOUBLE)}
 
 
 def small_shape(seq_len=192, dim=256, num_heads=2, head_dim=128, mlp_hidden=512,
@@ -160,6 +168,45 @@ def block_weights(shape: BlockShape, block: int = 0, norm_weights: str = "ones",
         w1=draw(s("w1"), (n1, d), sigma), b1=draw(s("b1"), (n1,), sigma),
         w2=draw(s("w2"), (d, n2), sigma), b2=draw(s("b2"), (d,), sigma),
         q_norm_w=qw, k_norm_w=kw)
+
+
+@dataclass
+class StreamWeights:
+    """One stream of a two-stream block (or a sequential block)."""
+    w_mod: np.ndarray     # [6d, temb_dim]
+    b_mod: np.ndarray     # [6d]
+    w_qkv: np.ndarray     # [3d, d]
+    b_qkv: np.ndarray     # [3d]
+    q_norm_w: np.ndarray  # [head_dim] float32
+    k_norm_w: np.ndarray  # [head_dim] float32
+    w_o: np.ndarray       # [d, d]
+    b_o: np.ndarray       # [d]
+    w_fc1: np.ndarray     # [mlp, d]
+    b_fc1: np.ndarray     # [mlp]
+    w_fc2: np.ndarray     # [d, mlp]
+    b_fc2: np.ndarray     # [d]
+
+
+def stream_weights(shape: BlockShape, stream: int = 0, block: int = 0, norm_weights: str = "ones",
+                   sigma: float = 0.02) -> StreamWeights:
+    """Weights of stream ``stream`` (0 text, 1 image) of a two-stream block:
+    N(0, sigma) bf16 values, seeds offset by 50 per stream; RMSNorm weights as
+    in block_weights."""
+    d, t, m, dh = shape.dim, shape.tdim, shape.mlp_hidden, shape.head_dim
+    s = lambda name: seed_of(shape, name, block) + 50 * stream
+    if norm_weights == "ones":
+        qw = np.ones(dh, np.float32)
+        kw = np.ones(dh, np.float32)
+    else:
+        qw = (1.0 + 0.1 * np.random.default_rng(s("q_norm_w")).standard_normal(dh)).astype(np.float32)
+        kw = (1.0 + 0.1 * np.random.default_rng(s("k_norm_w")).standard_normal(dh)).astype(np.float32)
+    return StreamWeights(
+        w_mod=draw(s("w_mod6"), (6 * d, t), sigma), b_mod=draw(s("b_mod6"), (6 * d,), sigma),
+        w_qkv=draw(s("w_qkv"), (3 * d, d), sigma), b_qkv=draw(s("b_qkv"), (3 * d,), sigma),
+        q_norm_w=qw, k_norm_w=kw,
+        w_o=draw(s("w_o"), (d, d), sigma), b_o=draw(s("b_o"), (d,), sigma),
+        w_fc1=draw(s("w_fc1"), (m, d), sigma), b_fc1=draw(s("b_fc1"), (m,), sigma),
+        w_fc2=draw(s("w_fc2"), (d, m), sigma), b_fc2=draw(s("b_fc2"), (d,), sigma))
 
 
 def block_activations(shape: BlockShape):

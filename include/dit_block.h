@@ -180,6 +180,61 @@ int dit_block_forward(const dit_block_config* cfg, const dit_block_weights* w,
                       const float* rope_sin, dit_bf16* y, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/* ---- two-stream (MMDiT) and sequential blocks ------------------------------ */
+
+/* Weights of one stream.  The Flux page (section 3.1) names the block lists
+ * of the models it compiles: Flux's transformer_blocks (two-stream) and
+ * single_transformer_blocks, and Wan's blocks.  A stream of a two-stream
+ * block has its own adaLN modulation with six vectors, attention
+ * projections and MLP: */
+typedef struct {
+  const dit_bf16* w_mod;   /* [6d, temb_dim]  rows shift1|scale1|gate1|shift2|scale2|gate2 */
+  const dit_bf16* b_mod;   /* [6d] or NULL */
+  const dit_bf16* w_qkv;   /* [3d, d]         output columns q | k | v */
+  const dit_bf16* b_qkv;   /* [3d] or NULL */
+  const float* q_norm_w;   /* [head_dim]      RMSNorm weight of q, shared by heads */
+  const float* k_norm_w;   /* [head_dim] */
+  const dit_bf16* w_o;     /* [d, d]          attention output projection */
+  const dit_bf16* b_o;     /* [d] or NULL */
+  const dit_bf16* w_fc1;   /* [mlp, d]        MLP in (GELU-tanh follows) */
+  const dit_bf16* b_fc1;   /* [mlp] or NULL */
+  const dit_bf16* w_fc2;   /* [d, mlp]        MLP out */
+  const dit_bf16* b_fc2;   /* [d] or NULL */
+} dit_stream_weights;
+
+/* Bytes of workspace dit_mmdit_block_forward and dit_sequential_block_forward
+ * need (0 on an invalid config). */
+size_t dit_mmdit_block_workspace_bytes(const dit_block_config* cfg);
+
+/* One two-stream block forward.  x, y [S, d] hold the text tokens (rows
+ * [0, txt_len)) followed by the image tokens (rows [txt_len, S)); y may
+ * equal x.  For each stream s with its own weights and rows x_s:
+ *   shift1, scale1, gate1, shift2, scale2, gate2 = W_mod.SiLU(temb) + b_mod
+ *   u = LN(x_s)(1 + scale1) + shift1;  q|k|v = u W_qkv^T + b_qkv;
+ *   q, k <- per-head RMSNorm (the stream's weights), then RoPE (table rows
+ *   of the stream's tokens);
+ * then one attention over the concatenated q, k, v of all S tokens (text and
+ * image attend to each other), and per stream, with o_s its output rows:
+ *   x' = x_s + gate1 * (o_s W_o^T + b_o)
+ *   y_s = x' + gate2 * (GELU_tanh((LN(x')(1 + scale2) + shift2) W_fc1^T + b_fc1) W_fc2^T + b_fc2)
+ * Same LayerNorm, RMSNorm, RoPE, attention and GELU as the single-stream
+ * block; x' is kept in fp32 (workspace), other intermediates in bf16.  txt_len in [0, S]; txt may be NULL when txt_len == 0 (then the
+ * block is one stream: see dit_sequential_block_forward).  Each linear is
+ * one launch for both streams (their tiles share the chip).  workspace:
+ * dit_mmdit_block_workspace_bytes(cfg) bytes, 256-byte aligned. */
+int dit_mmdit_block_forward(const dit_block_config* cfg, int64_t txt_len, const dit_stream_weights* txt,
+                            const dit_stream_weights* img, const dit_bf16* x, const dit_bf16* temb,
+                            const float* rope_cos, const float* rope_sin, dit_bf16* y, void* workspace,
+                            size_t ws_bytes, void* stream);
+
+/* One sequential block (the block of the Wan video page: attention, gated
+ * residual, then the MLP with its own LayerNorm+modulate and gated
+ * residual), i.e. one stream of the two-stream block over all S tokens.
+ * Cross-attention to a text context is not part of it. */
+int dit_sequential_block_forward(const dit_block_config* cfg, const dit_stream_weights* w, const dit_bf16* x,
+                                 const dit_bf16* temb, const float* rope_cos, const float* rope_sin,
+                                 dit_bf16* y, void* workspace, size_t ws_bytes, void* stream);
+
 /* ---- block stack replayed over denoising steps --------------------------- */
 
 typedef struct dit_stack dit_stack;  /* opaque: owns the captured graph */

@@ -1,4 +1,5 @@
-"""CPU oracle of the Flux-style single-stream DiT block forward.
+"""CPU oracle of the Flux-style DiT block forwards (single-stream, two-stream
+and sequential).
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
 ``cpu_baseline`` leg may import this module.  The GPU library never calls it,
@@ -26,6 +27,13 @@ Readings of what the pages leave open (all are documented with the tests):
     split in equal chunks, one per position axis, in axis order;
   * attention: no mask, scale 1/sqrt(head_dim), softmax over all tokens;
   * GELU in its tanh form;
+  * two-stream block (Flux's transformer_blocks; internals not on the
+    pages): per stream its own six-vector modulation (shift1, scale1,
+    gate1, shift2, scale2, gate2), q|k|v linear, q/k RMSNorm weights,
+    output projection and MLP; one attention over text then image tokens;
+    attention and MLP branches in sequence, each with its own
+    LayerNorm+modulate and gated residual; the sequential video block is
+    the same with a single stream (no cross-attention);
   * chunked attention (the one-GPU math of ring attention): a chunk's
     partial output is the softmax average over the chunk's keys alone, its
     lse the natural log of the chunk's sum of exp(score); partials of
@@ -271,6 +279,80 @@ def _attention_rows(q_rows, k, v, num_heads, head_dim):
     """attention() with a query matrix that already holds only the wanted rows."""
     qfull = np.asarray(q_rows, F64)
     return attention(qfull, k, v, num_heads, head_dim, q_rows=np.arange(qfull.shape[0]))
+
+
+# ------------------------------------------- two-stream / sequential blocks
+def stream_modulation(temb, w_mod, b_mod):
+    """Six adaLN vectors of one stream of a two-stream block:
+    W_mod . SiLU(temb) + b_mod split into shift1, scale1, gate1 (attention
+    branch) and shift2, scale2, gate2 (MLP branch), each [d]."""
+    m = linear(silu(temb)[None, :], w_mod, b_mod)[0]
+    d = m.shape[0] // 6
+    return tuple(m[i * d:(i + 1) * d] for i in range(6))
+
+
+def double_block_forward(shape, w_txt, w_img, x, temb, pos, n_txt=None, rows=None):
+    """One two-stream (MMDiT) block forward: Flux's transformer_blocks, named
+    beside single_transformer_blocks in section 3.1 of the Flux page.
+
+    Tokens [0, n_txt) are the text stream (weights w_txt), tokens [n_txt, S)
+    the image stream (w_img); n_txt defaults to shape.text_tokens.  Per
+    stream, with its own weights:
+      1. shift1, scale1, gate1, shift2, scale2, gate2 = W_mod . SiLU(temb) + b_mod
+      2. u = LN(x) * (1 + scale1) + shift1
+      3. q, k, v = u W_qkv^T + b_qkv; q, k <- per-head RMSNorm, then RoPE
+    4. one attention over the q, k, v of all S tokens (both streams)
+    then per stream, o being its rows of the attention output:
+      5. x' = x + gate1 * (o W_o^T + b_o)
+      6. y = x' + gate2 * (GELU_tanh((LN(x') (1 + scale2) + shift2) W_fc1^T + b_fc1) W_fc2^T + b_fc2)
+    With n_txt = 0 this is the sequential block (one stream over all tokens).
+    ``rows`` restricts the output to those tokens (keys and values still
+    cover every token, so each returned row is exact).
+    """
+    d, H, Dh = shape.dim, shape.num_heads, shape.head_dim
+    eps, qeps = shape.ln_eps, shape.qk_eps
+    x = np.asarray(x, F64)
+    S = x.shape[0]
+    n_txt = shape.text_tokens if n_txt is None else n_txt
+    theta = rope_angles(pos, shape.rope_axes_dims, Dh, shape.rope_base)
+    streams = [(w_txt, 0, n_txt), (w_img, n_txt, S)]
+    # keys and values of every token, each stream with its own weights
+    k = np.zeros((S, d), F64)
+    v = np.zeros((S, d), F64)
+    for w, a, b in streams:
+        if b <= a:
+            continue
+        shift1, scale1 = stream_modulation(temb, w.w_mod, w.b_mod)[:2]
+        u = layer_norm_modulate(x[a:b], shift1, scale1, eps)
+        wq, bq = np.asarray(w.w_qkv, F64), np.asarray(w.b_qkv, F64)
+        kk = linear(u, wq[d:2 * d], bq[d:2 * d])
+        k[a:b] = rope_apply(rms_norm_heads(kk, H, Dh, w.k_norm_w, qeps), theta[a:b], H, Dh)
+        v[a:b] = linear(u, wq[2 * d:], bq[2 * d:])
+    rr = np.arange(S) if rows is None else np.asarray(rows)
+    out = np.empty((rr.shape[0], d), F64)
+    for w, a, b in streams:
+        sel = (rr >= a) & (rr < b)
+        if not sel.any():
+            continue
+        rs = rr[sel]
+        shift1, scale1, gate1, shift2, scale2, gate2 = stream_modulation(temb, w.w_mod, w.b_mod)
+        u = layer_norm_modulate(x[rs], shift1, scale1, eps)
+        wq, bq = np.asarray(w.w_qkv, F64), np.asarray(w.b_qkv, F64)
+        q = rope_apply(rms_norm_heads(linear(u, wq[:d], bq[:d]), H, Dh, w.q_norm_w, qeps), theta[rs], H, Dh)
+        o = _attention_rows(q, k, v, H, Dh)
+        x1 = gated_residual(x[rs], gate1, linear(o, w.w_o, w.b_o))
+        u2 = layer_norm_modulate(x1, shift2, scale2, eps)
+        mlp = linear(gelu_tanh(linear(u2, w.w_fc1, w.b_fc1)), w.w_fc2, w.b_fc2)
+        out[sel] = gated_residual(x1, gate2, mlp)
+    return out
+
+
+def sequential_block_forward(shape, w, x, temb, pos, rows=None):
+    """The sequential (Wan-style) block: attention, gated residual, then the
+    MLP with its own LayerNorm+modulate and gated residual, over all tokens
+    with one set of weights; the two-stream block with no text stream.
+    Cross-attention to a text context is not part of it."""
+    return double_block_forward(shape, None, w, x, temb, pos, n_txt=0, rows=rows)
 
 
 def stack_forward(shape, weights_list, x_in, temb_steps, pos, chain=False, bf16_io=True):

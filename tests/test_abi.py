@@ -127,6 +127,36 @@ def test_block_forward_argument_checks(lib):
     assert lib.dit_block_forward(None, ctypes.byref(w), P, P, P, P, P, P, need, None) == B.DIT_ERR_INVALID_ARG
 
 
+def test_mmdit_block_argument_checks(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    P = ctypes.c_void_p(0x1000)
+    c = cfg()
+    a = lambda n: (n + 255) // 256 * 256
+    S, d, mlp = 256, 256, 1024
+    need = B.mmdit_block_workspace_bytes(c)
+    assert need == a(12 * d * 4) + a(S * d * 2) + a(S * 3 * d * 2) + a(S * d * 2) + a(S * d * 4) + a(S * mlp * 2)
+    assert B.mmdit_block_workspace_bytes(cfg(num_heads=3)) == 0
+    w = B.StreamWeightsC(*([0x1000] * 12))
+    fwd = lambda cc, T, wt, wi, ws_bytes, ws=P: lib.dit_mmdit_block_forward(
+        ctypes.byref(cc), T, wt, wi, P, P, P, P, P, ws, ws_bytes, None)
+    W = ctypes.byref(w)
+    assert fwd(c, 16, W, W, need - 1) == B.DIT_ERR_WORKSPACE
+    assert fwd(c, 16, W, W, need, ctypes.c_void_p(0x1010)) == B.DIT_ERR_WORKSPACE
+    assert fwd(c, -1, W, W, need) == B.DIT_ERR_INVALID_ARG
+    assert fwd(c, S + 1, W, W, need) == B.DIT_ERR_INVALID_ARG
+    assert fwd(c, 16, None, W, need) == B.DIT_ERR_INVALID_ARG      # text weights needed when txt_len > 0
+    assert fwd(c, 0, W, None, need) == B.DIT_ERR_INVALID_ARG       # image weights needed when txt_len < S
+    bad = B.StreamWeightsC(*([0x1000] * 6 + [0] + [0x1000] * 5))     # w_o missing
+    assert fwd(c, 16, W, ctypes.byref(bad), need) == B.DIT_ERR_INVALID_ARG
+    odd = B.StreamWeightsC(*([0x1000] * 11 + [0x1008]))              # b_fc2 not 16-byte aligned
+    assert fwd(c, 16, W, ctypes.byref(odd), need) == B.DIT_ERR_INVALID_ARG
+    assert fwd(cfg(head_dim=32, num_heads=8), 16, W, W, need) == B.DIT_ERR_UNSUPPORTED
+    assert lib.dit_sequential_block_forward(ctypes.byref(c), None, P, P, P, P, P, P, need, None) == \
+        B.DIT_ERR_INVALID_ARG
+    assert lib.dit_sequential_block_forward(ctypes.byref(c), W, P, P, P, P, P, P, need - 1, None) == \
+        B.DIT_ERR_WORKSPACE
+
+
 def test_stack_argument_checks(lib):
     from diffusion_transformer_dit_amd import binding as B
     P = ctypes.c_void_p(0x1000)

@@ -35,7 +35,7 @@ def cfg_of(B, shape, flags=0):
 def sample_rows(S, extra=()):
     if S <= 512:
         return np.arange(S)
-    return np.unique(np.concatenate([np.arange(0, S, max(1, S // 40)), [S - 1], list(extra)]))
+    return np.unique(np.concatenate([np.arange(0, S, max(1, S // 40)), [S - 1], list(extra)])).astype(np.int64)
 
 
 BLOCK_SHAPES = [

@@ -297,9 +297,132 @@ def pin_stack(o):
     assert np.array_equal(o.stack_forward(sh, zw, x, tembs, pos)[1], x.astype(np.float64))
 
 
+# ------------------------------------------------- two-stream / sequential blocks
+def _torch_rope(t, pos, shape):
+    S, Dh = t.shape[0], shape.head_dim
+    ang = []
+    for a, D in enumerate(shape.rope_axes_dims):
+        freq = shape.rope_base ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
+        ang.append(torch.outer(t64(pos[:, a]), freq))
+    rot = torch.polar(torch.ones(S, Dh // 2, dtype=torch.float64), torch.cat(ang, 1))[:, None, :]
+    return torch.view_as_real(torch.view_as_complex(t.reshape(S, -1, Dh // 2, 2).contiguous()) * rot).reshape(S, -1, Dh)
+
+
+def torch_double_block(shape, wt, wi, x, temb, pos, n_txt):
+    """The two-stream block from PyTorch float64 library routines: both
+    streams' q, k, v concatenated for one scaled_dot_product_attention call,
+    RoPE with complex numbers; an independent second writing."""
+    d, H, Dh = shape.dim, shape.num_heads, shape.head_dim
+    X = t64(x)
+    S = X.shape[0]
+    parts = [(wt, slice(0, n_txt)), (wi, slice(n_txt, S))]
+    qs, ks, vs, mods = [], [], [], []
+    for w, sl in parts:
+        m = F.linear(F.silu(t64(temb)), t64(w.w_mod), t64(w.b_mod)).chunk(6) if w is not None else None
+        mods.append(m)
+        if w is None or sl.stop <= sl.start:
+            continue
+        u = F.layer_norm(X[sl], (d,), eps=shape.ln_eps) * (1 + m[1]) + m[0]
+        q, k, v = F.linear(u, t64(w.w_qkv), t64(w.b_qkv)).chunk(3, dim=1)
+        n = sl.stop - sl.start
+        q = F.rms_norm(q.reshape(n, H, Dh), (Dh,), weight=t64(w.q_norm_w), eps=shape.qk_eps)
+        k = F.rms_norm(k.reshape(n, H, Dh), (Dh,), weight=t64(w.k_norm_w), eps=shape.qk_eps)
+        qs.append(_torch_rope(q, pos[sl], shape))
+        ks.append(_torch_rope(k, pos[sl], shape))
+        vs.append(v.reshape(n, H, Dh))
+    q, k, v = (torch.cat(t, 0).transpose(0, 1) for t in (qs, ks, vs))
+    o = F.scaled_dot_product_attention(q, k, v).transpose(0, 1).reshape(S, d)
+    out = []
+    for (w, sl), m in zip(parts, mods):
+        if w is None or sl.stop <= sl.start:
+            continue
+        x1 = X[sl] + m[2] * F.linear(o[sl], t64(w.w_o), t64(w.b_o))
+        u2 = F.layer_norm(x1, (d,), eps=shape.ln_eps) * (1 + m[4]) + m[3]
+        hh = F.linear(F.gelu(F.linear(u2, t64(w.w_fc1), t64(w.b_fc1)), approximate="tanh"), t64(w.w_fc2), t64(w.b_fc2))
+        out.append(x1 + m[5] * hh)
+    return torch.cat(out, 0).numpy()
+
+
+def _small_double(same_weights=False):
+    sh = DI.small_shape(seq_len=40, dim=64, num_heads=2, head_dim=32, mlp_hidden=96,
+                        grid=(4, 6), text_tokens=8, axes=(16, 16))
+    wt = DI.stream_weights(sh, 0, norm_weights="random", sigma=0.1)
+    wi = wt if same_weights else DI.stream_weights(sh, 1, norm_weights="random", sigma=0.1)
+    x, temb = DI.block_activations(sh)
+    return sh, wt, wi, x, temb, DI.positions(sh)
+
+
+def _sw(w, **kw):
+    f = dict(w.__dict__)
+    f.update(kw)
+    return DI.StreamWeights(**f)
+
+
+def pin_double_block(o):
+    sh, wt, wi, x, temb, pos = _small_double()
+    for n_txt in (8, 1, 39, 40):
+        y = o.double_block_forward(sh, wt, wi, x, temb, pos, n_txt=n_txt)
+        ref = torch_double_block(sh, wt, wi, x, temb, pos, n_txt)
+        assert np.allclose(y, ref, rtol=1e-10, atol=1e-10), n_txt
+    y0 = o.sequential_block_forward(sh, wi, x, temb, pos)
+    assert np.allclose(y0, torch_double_block(sh, None, wi, x, temb, pos, 0), rtol=1e-10, atol=1e-10)
+    rows = np.array([0, 7, 8, 21, 39])
+    y = o.double_block_forward(sh, wt, wi, x, temb, pos)
+    assert np.allclose(o.double_block_forward(sh, wt, wi, x, temb, pos, rows=rows), y[rows], rtol=1e-12, atol=1e-12)
+
+
+def pin_double_block_reductions(o):
+    """Special cases that reduce the two-stream block to the (separately
+    pinned) single-stream block, to its own halves, or to the identity."""
+    sh, wt, wi, x, temb, pos = _small_double()
+    d, T, S = sh.dim, sh.text_tokens, sh.seq_len
+    y = o.double_block_forward(sh, wt, wi, x, temb, pos)
+    # all six gates of both streams zero -> the input, bitwise
+    zg = lambda w: _sw(w, w_mod=np.concatenate([w.w_mod[:2 * d], 0 * w.w_mod[2 * d:3 * d], w.w_mod[3 * d:5 * d],
+                                                0 * w.w_mod[5 * d:]]),
+                       b_mod=np.concatenate([w.b_mod[:2 * d], 0 * w.b_mod[2 * d:3 * d], w.b_mod[3 * d:5 * d],
+                                             0 * w.b_mod[5 * d:]]))
+    assert np.array_equal(o.double_block_forward(sh, zg(wt), zg(wi), x, temb, pos), x.astype(np.float64))
+    # no attention branch (W_o = 0, b_o = 0): each stream is the single-stream
+    # block whose linear2 ignores the attention columns, modulated by the
+    # second triple (shift2, scale2, gate2)
+    no_att = lambda w: _sw(w, w_o=0 * w.w_o, b_o=0 * w.b_o)
+    ya = o.double_block_forward(sh, no_att(wt), no_att(wi), x, temb, pos)
+    for w, sl in ((wt, slice(0, T)), (wi, slice(T, S))):
+        bw = DI.BlockWeights(w_mod=w.w_mod[3 * d:], b_mod=w.b_mod[3 * d:],
+                             w1=np.concatenate([w.w_qkv, w.w_fc1]), b1=np.concatenate([w.b_qkv, w.b_fc1]),
+                             w2=np.concatenate([0 * w.w_o, w.w_fc2], axis=1), b2=w.b_fc2,
+                             q_norm_w=w.q_norm_w, k_norm_w=w.k_norm_w)
+        ref = o.block_forward(sh, bw, x[sl], temb, pos[sl])
+        assert np.allclose(ya[sl], ref, rtol=1e-12, atol=1e-12)
+    # no MLP branch (W_fc2 = 0, b_fc2 = 0) and one set of weights for both
+    # streams: the single-stream block over all tokens whose linear2 ignores
+    # the MLP columns, modulated by the first triple -- joint attention
+    sh1, ws, _, x1, temb1, pos1 = _small_double(same_weights=True)
+    no_mlp = _sw(ws, w_fc2=0 * ws.w_fc2, b_fc2=0 * ws.b_fc2)
+    yb = o.double_block_forward(sh1, no_mlp, no_mlp, x1, temb1, pos1)
+    bw = DI.BlockWeights(w_mod=ws.w_mod[:3 * d], b_mod=ws.b_mod[:3 * d],
+                         w1=np.concatenate([ws.w_qkv, ws.w_fc1]), b1=np.concatenate([ws.b_qkv, ws.b_fc1]),
+                         w2=np.concatenate([ws.w_o, 0 * ws.w_fc2], axis=1), b2=ws.b_o,
+                         q_norm_w=ws.q_norm_w, k_norm_w=ws.k_norm_w)
+    assert np.allclose(yb, o.block_forward(sh1, bw, x1, temb1, pos1), rtol=1e-12, atol=1e-12)
+    # the block is its attention half followed by its MLP half
+    half_a = lambda w: _sw(w, w_fc2=0 * w.w_fc2, b_fc2=0 * w.b_fc2)
+    mid = o.double_block_forward(sh, half_a(wt), half_a(wi), x, temb, pos)
+    yc = o.double_block_forward(sh, no_att(wt), no_att(wi), mid, temb, pos)
+    assert np.allclose(yc, y, rtol=1e-12, atol=1e-12)
+    # one set of weights: where the text/image boundary lies does not matter
+    ys = [o.double_block_forward(sh1, ws, ws, x1, temb1, pos1, n_txt=t) for t in (0, 8, 40)]
+    assert np.allclose(ys[0], ys[1], rtol=1e-12, atol=1e-12) and np.allclose(ys[0], ys[2], rtol=1e-12, atol=1e-12)
+    # permuting image tokens together with their positions permutes the output
+    perm = np.concatenate([np.arange(T), T + RNG.permutation(S - T)])
+    yp = o.double_block_forward(sh, wt, wi, x[perm], temb, pos[perm])
+    assert np.allclose(yp, y[perm], rtol=1e-12, atol=1e-12)
+
+
 PINS = [pin_layer_norm, pin_modulate, pin_gated_residual, pin_silu, pin_gelu, pin_linear,
         pin_modulation, pin_rms_norm, pin_rope, pin_attention, pin_attention_chunks, pin_block, pin_round_bf16,
-        pin_stack]
+        pin_stack, pin_double_block, pin_double_block_reductions]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -444,6 +567,83 @@ def test_planted_mistake_is_caught(monkeypatch, name, mutant, pin):
     monkeypatch.setattr(O, name, mutant)
     with pytest.raises(AssertionError):
         pin(O)
+
+
+def _double_with_bug(bug):
+    """A two-stream block with one planted mistake, for the pins to catch."""
+    def f(shape, w_txt, w_img, x, temb, pos, n_txt=None, rows=None):
+        d, H, Dh = shape.dim, shape.num_heads, shape.head_dim
+        x = np.asarray(x, np.float64)
+        S = x.shape[0]
+        n_txt = shape.text_tokens if n_txt is None else n_txt
+        theta = O.rope_angles(pos, shape.rope_axes_dims, Dh, shape.rope_base)
+        streams = [(w_txt, 0, n_txt), (w_img, n_txt, S)]
+        if bug == "text_uses_image_weights":
+            streams = [(w_img, 0, n_txt), (w_img, n_txt, S)]
+        q, k, v = (np.zeros((S, d)) for _ in range(3))
+        mods = []
+        for w, a, b in streams:
+            m = O.stream_modulation(temb, w.w_mod, w.b_mod) if w is not None else None
+            if bug == "gates_swapped" and m is not None:
+                m = (m[0], m[1], m[5], m[3], m[4], m[2])
+            mods.append(m)
+            if b <= a:
+                continue
+            u = O.layer_norm_modulate(x[a:b], m[0], m[1], shape.ln_eps)
+            z = O.linear(u, w.w_qkv, w.b_qkv)
+            th = theta[0:b - a] if bug == "rope_not_offset" else theta[a:b]
+            q[a:b] = O.rope_apply(O.rms_norm_heads(z[:, :d], H, Dh, w.q_norm_w, shape.qk_eps), th, H, Dh)
+            k[a:b] = O.rope_apply(O.rms_norm_heads(z[:, d:2 * d], H, Dh, w.k_norm_w, shape.qk_eps), th, H, Dh)
+            v[a:b] = z[:, 2 * d:]
+        out = np.zeros((S, d))
+        for (w, a, b), m in zip(streams, mods):
+            if b <= a:
+                continue
+            if bug == "stream_local_attention":
+                o = O.attention(q[a:b], k[a:b], v[a:b], H, Dh)
+            else:
+                o = O.attention(q, k, v, H, Dh, q_rows=np.arange(a, b))
+            x1 = O.gated_residual(x[a:b], m[2], O.linear(o, w.w_o, w.b_o))
+            u2 = O.layer_norm_modulate(x[a:b] if bug == "ln2_on_x" else x1, m[3], m[4], shape.ln_eps)
+            mlp = O.linear(O.gelu_tanh(O.linear(u2, w.w_fc1, w.b_fc1)), w.w_fc2, w.b_fc2)
+            out[a:b] = O.gated_residual(x1, m[5], mlp)
+        return out if rows is None else out[np.asarray(rows)]
+    return f
+
+
+def _mut_stream_modulation_branch_order(temb, w_mod, b_mod):
+    m = _REAL_STREAM_MOD(temb, w_mod, b_mod)
+    return m[3:] + m[:3]
+
+
+_REAL_STREAM_MOD = O.stream_modulation
+
+
+def test_double_block_bug_free_variant_passes():
+    # the variant machinery itself, with no bug, satisfies every pin
+    import types
+    shim = types.SimpleNamespace(**{k: getattr(O, k) for k in dir(O) if not k.startswith("__")})
+    shim.double_block_forward = _double_with_bug(None)
+    shim.sequential_block_forward = lambda sh, w, x, temb, pos, rows=None: shim.double_block_forward(
+        sh, None, w, x, temb, pos, n_txt=0, rows=rows)
+    pin_double_block(shim)
+    pin_double_block_reductions(shim)
+
+
+@pytest.mark.parametrize("bug", ["text_uses_image_weights", "gates_swapped", "rope_not_offset",
+                                 "stream_local_attention", "ln2_on_x"])
+def test_planted_double_block_mistake_is_caught(monkeypatch, bug):
+    monkeypatch.setattr(O, "double_block_forward", _double_with_bug(bug))
+    with pytest.raises(AssertionError):
+        pin_double_block(O)
+    with pytest.raises(AssertionError):
+        pin_double_block_reductions(O)
+
+
+def test_planted_stream_modulation_order_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "stream_modulation", _mut_stream_modulation_branch_order)
+    with pytest.raises(AssertionError):
+        pin_double_block(O)
 
 
 def test_planted_linear_transpose_is_caught(monkeypatch):
