@@ -112,7 +112,7 @@ def time_graph(fn, iters, replays=3):
 
 
 KERNEL_NAMES = ("modulation", "block_modulate_norm", "modulate_norm", "linear1_gelu", "qk_rmsnorm_rope",
-                "attention", "linear2_gated_residual", "gated_residual", "copy", "block_forward")
+                "attention", "linear2_gated_residual", "gated_residual", "copy", "block_forward", "other_blocks")
 
 
 def block_sequence_times(B, blocks, x_in, temb, rc, rs, iters, only=None):
@@ -356,7 +356,10 @@ def main():
         pos = torch.from_numpy(DI.positions(DI.FLUX)).to(dev)
         rc, rs = B.rope_table(pos, list(DI.FLUX.rope_axes_dims), DH)
         k, _ = kernel_phase(B, g, dev, blocks, x_in, temb, rc, rs, args.kernel_iters, only)
-        print(json.dumps({"kernels_us": {n: round(v * 1e3, 2) for n, v in k.items()}}), flush=True)
+        out = {"kernels_us": {n: round(v * 1e3, 2) for n, v in k.items()}}
+        if "other_blocks" in only:
+            out["other_blocks"] = other_block_times(B, g, dev)
+        print(json.dumps(out), flush=True)
         return 0
 
     nb = args.blocks
