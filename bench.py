@@ -506,6 +506,31 @@ def main():
     }
     log(f"chunked attention: 8 partials {ca['partials_ms'] * 1e3:.1f} us + merge {ca['merge_ms'] * 1e3:.1f} us, "
         f"single pass {ca['single_pass_ms'] * 1e3:.1f} us, 3-head share {ca['ulysses_share_3heads_ms'] * 1e3:.1f} us")
+    # ---- step-level skip (MeanCache-style control): 50 denoising steps with
+    # steps 0, 1 and every even step after computed (26 forwards), the others
+    # predicted from the last two computed outputs, against all 50 computed
+    n50 = 50
+    fresh = [1 if (s_ < 2 or s_ % 2 == 0) else 0 for s_ in range(n50)]
+    temb50 = randn((n50, D), 1.0)
+    out50 = torch.empty(n50, S, D, dtype=torch.bfloat16, device=dev)
+    tsteps = [1.0 - s_ / n50 for s_ in range(n50)]
+    c0, c1, c2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    c0.record()
+    st.replay(cfg, blocks, x_in, temb50, rc, rs, out50, ws)
+    c1.record()
+    st.replay_cached(cfg, blocks, x_in, temb50, rc, rs, out50, ws, fresh, tsteps)
+    c2.record()
+    torch.cuda.synchronize()
+    ms_all, ms_cached = c0.elapsed_time(c1), c1.elapsed_time(c2)
+    result["step_skip"] = {
+        "workload": "57-block Flux stack, 50 denoising steps",
+        "schedule": "steps 0, 1 and every even step computed (26 of 50); skipped steps predicted by the "
+                    "first-order finite difference in t through the last two computed outputs",
+        "forwards": sum(fresh), "ms_50_steps_all_computed": round(ms_all, 2),
+        "ms_50_steps_cached": round(ms_cached, 2), "speedup": round(ms_all / ms_cached, 3),
+    }
+    log(f"step skip: 50 steps {ms_all:.1f} ms all computed, {ms_cached:.1f} ms with {sum(fresh)} computed")
+    del out50, temb50
     ob = other_block_times(B, g, dev)
     for v in ob.values():
         v["note"] = "one block forward captured in a graph and replayed (same weights each replay)"

@@ -69,6 +69,8 @@ SIGNATURES = {
     "dit_stack_replay": ([VP, VP, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
     "dit_attention_partial": ([VP, I64, I64, I64, I64, I64, VP, VP, VP], ctypes.c_int),
     "dit_attention_merge": ([VP, VP, I64, I64, I64, I64, VP, I64, VP], ctypes.c_int),
+    "dit_stack_replay_cached": ([VP, VP, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP, VP, VP, SZ, VP, VP, VP],
+                                ctypes.c_int),
     "dit_stack_set_probe": ([VP, ctypes.c_uint32], ctypes.c_int),
     "dit_stack_probe_ms": ([VP, VP, ctypes.c_int], ctypes.c_int),
     "dit_last_error": ([], ctypes.c_char_p),
@@ -425,4 +427,29 @@ class Stack:
         _check(_lib.dit_stack_replay(self.handle, ctypes.byref(cfg), ctypes.cast(arr, VP), len(blocks), _p(x_in),
                                      _p(temb_steps), n_steps, _p(rope_cos), _p(rope_sin), _p(out), _p(workspace),
                                      workspace.numel(), _stream(stream)))
+        return out
+
+    def replay_cached(self, cfg, blocks, x_in, temb_steps, rope_cos, rope_sin, out, workspace, fresh,
+                      t_steps=None, stream=None):
+        """Replay only the steps with fresh[s] true; a skipped step's output is
+        the finite-difference prediction from the last two computed outputs
+        (see dit_stack_replay_cached).  fresh: sequence of n_steps bools;
+        t_steps: n_steps floats (strictly monotonic) or None for t_s = s."""
+        _need(x_in, BF16, "x_in", 2)
+        _need(temb_steps, BF16, "temb_steps", 2)
+        _need(out, BF16, "out", 3)
+        _need(workspace, torch.uint8, "workspace", 1)
+        n_steps = temb_steps.shape[0]
+        if out.shape != (n_steps, cfg.seq_len, cfg.dim):
+            raise ValueError("out must be [n_steps, S, d]")
+        if len(fresh) != n_steps or (t_steps is not None and len(t_steps) != n_steps):
+            raise ValueError("fresh / t_steps must have one entry per step")
+        fr = (ctypes.c_uint8 * max(n_steps, 1))(*[1 if f else 0 for f in fresh])
+        ts = None if t_steps is None else (ctypes.c_float * max(n_steps, 1))(*[float(t) for t in t_steps])
+        arr = (BlockWeightsC * len(blocks))(*[b.c for b in blocks])
+        self._keep = (blocks, arr)
+        _check(_lib.dit_stack_replay_cached(self.handle, ctypes.byref(cfg), ctypes.cast(arr, VP), len(blocks),
+                                            _p(x_in), _p(temb_steps), n_steps, _p(rope_cos), _p(rope_sin), _p(out),
+                                            _p(workspace), workspace.numel(), ctypes.cast(fr, VP),
+                                            None if ts is None else ctypes.cast(ts, VP), _stream(stream)))
         return out

@@ -3,6 +3,7 @@
 // only; the kernels live in elementwise.hip, gemm.hip and attention.hip.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -576,10 +577,12 @@ extern "C" size_t dit_stack_workspace_bytes(const dit_block_config* cfg) {
   return layout(D).stack_end;
 }
 
-extern "C" int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks,
-                                int n_blocks, const dit_bf16* x_in, const dit_bf16* temb_steps, int n_steps,
-                                const float* rope_cos, const float* rope_sin, dit_bf16* out, void* workspace,
-                                size_t ws_bytes, void* stream) {
+namespace {
+// Argument checks shared by the replay entry points, then the capture of the
+// block sequence on first use.
+int stack_setup(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks, int n_blocks,
+                const dit_bf16* x_in, const dit_bf16* temb_steps, int n_steps, const float* rope_cos,
+                const float* rope_sin, dit_bf16* out, void* workspace, size_t ws_bytes, hipStream_t s, Dims* Dout) {
   if (!st) return fail(DIT_ERR_INVALID_ARG, "stack is NULL");
   Dims D;
   int rc = dims_of(cfg, &D);
@@ -594,73 +597,140 @@ extern "C" int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, cons
   if (!workspace || ws_bytes < L.stack_end)
     return fail(DIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.stack_end);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(DIT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  hipStream_t s = as_stream(stream);
   if ((rc = check_not_capturing(s))) return rc;
+  *Dout = D;
 
   const bool chain = (cfg->flags & DIT_STACK_CHAIN) != 0;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   dit_bf16* xbuf = reinterpret_cast<dit_bf16*>(ws + L.xbuf);
   dit_bf16* tbuf = reinterpret_cast<dit_bf16*>(ws + L.tbuf);
-  const size_t act_bytes = size_t(D.S) * D.d * 2;
 
   std::vector<uintptr_t> key =
       make_key(cfg, blocks, n_blocks, x_in, rope_cos, rope_sin, workspace, ws_bytes, st->probe_mask);
   if (st->exec && key != st->key)
     return fail(DIT_ERR_GRAPH_KEY, "stack was captured for another config / pointer set; destroy and re-create it");
-  if (!st->exec) {
-    dit::prepare_device();  // device queries happen before capture
-    if (!st->cap) DIT_CHECK_HIP(hipStreamCreateWithFlags(&st->cap, hipStreamNonBlocking), "hipStreamCreate");
-    if (st->probe_mask) {
-      int dev = 0;
-      DIT_CHECK_HIP(hipGetDevice(&dev), "hipGetDevice");
-      DIT_CHECK_HIP(hipDeviceGetAttribute(&st->wall_khz, hipDeviceAttributeWallClockRate, dev),
-                    "hipDeviceGetAttribute");
-      if (st->wall_khz <= 0) return fail(DIT_ERR_HIP, "device reports no wall-clock rate");
-      const size_t bytes = size_t(n_blocks) * kProbeChannels * 2 * sizeof(unsigned long long);
-      if (st->probe_buf) hipFree(st->probe_buf);
-      st->probe_buf = nullptr;
-      DIT_CHECK_HIP(hipMalloc(&st->probe_buf, bytes), "hipMalloc");
-      DIT_CHECK_HIP(hipMemset(st->probe_buf, 0, bytes), "hipMemset");
-      st->probe_blocks = n_blocks;
-      st->probe_replays = 0;
-    }
-    DIT_CHECK_HIP(hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
-    int brc = DIT_OK;
-    for (int b = 0; b < n_blocks && brc == DIT_OK; ++b) {
-      const dit_bf16* xin = (b == 0 && !chain) ? x_in : xbuf;
-      Probe pr;
-      if (st->probe_mask) {
-        pr.mask = st->probe_mask;
-        pr.ch = st->probe_buf + size_t(b) * kProbeChannels * 2;
-      }
-      brc = enqueue_block(D, cfg, &blocks[b], xin, tbuf, rope_cos, rope_sin, xbuf, ws, st->cap, pr);
-    }
-    hipGraph_t g = nullptr;
-    hipError_t e = hipStreamEndCapture(st->cap, &g);
-    if (brc != DIT_OK) {
-      if (g) hipGraphDestroy(g);
-      return brc;
-    }
-    if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
-    hipGraphExec_t ex = nullptr;
-    e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
-    if (e != hipSuccess) {
-      hipGraphDestroy(g);
-      return hip_fail(e, "hipGraphInstantiate");
-    }
-    st->graph = g;
-    st->exec = ex;
-    st->key = key;
+  if (st->exec) return DIT_OK;
+  dit::prepare_device();  // device queries happen before capture
+  if (!st->cap) DIT_CHECK_HIP(hipStreamCreateWithFlags(&st->cap, hipStreamNonBlocking), "hipStreamCreate");
+  if (st->probe_mask) {
+    int dev = 0;
+    DIT_CHECK_HIP(hipGetDevice(&dev), "hipGetDevice");
+    DIT_CHECK_HIP(hipDeviceGetAttribute(&st->wall_khz, hipDeviceAttributeWallClockRate, dev),
+                  "hipDeviceGetAttribute");
+    if (st->wall_khz <= 0) return fail(DIT_ERR_HIP, "device reports no wall-clock rate");
+    const size_t bytes = size_t(n_blocks) * kProbeChannels * 2 * sizeof(unsigned long long);
+    if (st->probe_buf) hipFree(st->probe_buf);
+    st->probe_buf = nullptr;
+    DIT_CHECK_HIP(hipMalloc(&st->probe_buf, bytes), "hipMalloc");
+    DIT_CHECK_HIP(hipMemset(st->probe_buf, 0, bytes), "hipMemset");
+    st->probe_blocks = n_blocks;
+    st->probe_replays = 0;
   }
+  DIT_CHECK_HIP(hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
+  int brc = DIT_OK;
+  for (int b = 0; b < n_blocks && brc == DIT_OK; ++b) {
+    const dit_bf16* xin = (b == 0 && !chain) ? x_in : xbuf;
+    Probe pr;
+    if (st->probe_mask) {
+      pr.mask = st->probe_mask;
+      pr.ch = st->probe_buf + size_t(b) * kProbeChannels * 2;
+    }
+    brc = enqueue_block(D, cfg, &blocks[b], xin, tbuf, rope_cos, rope_sin, xbuf, ws, st->cap, pr);
+  }
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(st->cap, &g);
+  if (brc != DIT_OK) {
+    if (g) hipGraphDestroy(g);
+    return brc;
+  }
+  if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(g);
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  st->graph = g;
+  st->exec = ex;
+  st->key = key;
+  return DIT_OK;
+}
+
+// One computed step: stage temb_s, launch the graph, copy the result to out[step].
+int stack_fresh_step(dit_stack* st, const Dims& D, bool chain, int step, const dit_bf16* x_in,
+                     const dit_bf16* temb_steps, dit_bf16* out, unsigned char* ws, bool first, hipStream_t s) {
+  const WsLayout L = layout(D);
+  dit_bf16* xbuf = reinterpret_cast<dit_bf16*>(ws + L.xbuf);
+  dit_bf16* tbuf = reinterpret_cast<dit_bf16*>(ws + L.tbuf);
+  const size_t act_bytes = size_t(D.S) * D.d * 2;
+  if (chain && first) DIT_CHECK_HIP(hipMemcpyAsync(xbuf, x_in, act_bytes, hipMemcpyDeviceToDevice, s), "copy x_in");
+  DIT_CHECK_HIP(hipMemcpyAsync(tbuf, temb_steps + size_t(step) * D.tdim, size_t(D.tdim) * 2,
+                               hipMemcpyDeviceToDevice, s), "copy temb");
+  DIT_CHECK_HIP(hipGraphLaunch(st->exec, s), "hipGraphLaunch");
+  if (st->probe_mask) ++st->probe_replays;
+  DIT_CHECK_HIP(hipMemcpyAsync(out + size_t(step) * D.S * D.d, xbuf, act_bytes, hipMemcpyDeviceToDevice, s),
+                "copy out");
+  return DIT_OK;
+}
+}  // namespace
+
+extern "C" int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks,
+                                int n_blocks, const dit_bf16* x_in, const dit_bf16* temb_steps, int n_steps,
+                                const float* rope_cos, const float* rope_sin, dit_bf16* out, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  hipStream_t s = as_stream(stream);
+  Dims D;
+  int rc = stack_setup(st, cfg, blocks, n_blocks, x_in, temb_steps, n_steps, rope_cos, rope_sin, out, workspace,
+                       ws_bytes, s, &D);
+  if (rc) return rc;
+  const bool chain = (cfg->flags & DIT_STACK_CHAIN) != 0;
+  for (int step = 0; step < n_steps; ++step)
+    if ((rc = stack_fresh_step(st, D, chain, step, x_in, temb_steps, out, static_cast<unsigned char*>(workspace),
+                               step == 0, s)))
+      return rc;
+  return DIT_OK;
+}
+
+extern "C" int dit_stack_replay_cached(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks,
+                                       int n_blocks, const dit_bf16* x_in, const dit_bf16* temb_steps, int n_steps,
+                                       const float* rope_cos, const float* rope_sin, dit_bf16* out,
+                                       void* workspace, size_t ws_bytes, const uint8_t* fresh, const float* t_steps,
+                                       void* stream) {
+  if (n_steps > 0 && !fresh) return fail(DIT_ERR_INVALID_ARG, "fresh is NULL");
+  if (n_steps > 0 && !fresh[0]) return fail(DIT_ERR_INVALID_ARG, "step 0 must be computed (no history before it)");
+  if (t_steps) {
+    for (int i = 0; i < n_steps; ++i)
+      if (!std::isfinite(t_steps[i])) return fail(DIT_ERR_INVALID_ARG, "t_steps[%d] is not finite", i);
+    for (int i = 1; i < n_steps; ++i) {
+      const bool up = t_steps[1] > t_steps[0];
+      if (up ? !(t_steps[i] > t_steps[i - 1]) : !(t_steps[i] < t_steps[i - 1]))
+        return fail(DIT_ERR_INVALID_ARG, "t_steps must be strictly monotonic (step %d)", i);
+    }
+  }
+  hipStream_t s = as_stream(stream);
+  Dims D;
+  int rc = stack_setup(st, cfg, blocks, n_blocks, x_in, temb_steps, n_steps, rope_cos, rope_sin, out, workspace,
+                       ws_bytes, s, &D);
+  if (rc) return rc;
+  const bool chain = (cfg->flags & DIT_STACK_CHAIN) != 0;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  dit_bf16* xbuf = reinterpret_cast<dit_bf16*>(ws + layout(D).xbuf);
+  const size_t act = size_t(D.S) * D.d;
+  int fa = -1, fb = -1;  // the last two computed steps
+  auto tt = [&](int i) { return t_steps ? double(t_steps[i]) : double(i); };
   for (int step = 0; step < n_steps; ++step) {
-    if (chain && step == 0)
-      DIT_CHECK_HIP(hipMemcpyAsync(xbuf, x_in, act_bytes, hipMemcpyDeviceToDevice, s), "copy x_in");
-    DIT_CHECK_HIP(hipMemcpyAsync(tbuf, temb_steps + size_t(step) * D.tdim, size_t(D.tdim) * 2,
-                                 hipMemcpyDeviceToDevice, s), "copy temb");
-    DIT_CHECK_HIP(hipGraphLaunch(st->exec, s), "hipGraphLaunch");
-    if (st->probe_mask) ++st->probe_replays;
-    DIT_CHECK_HIP(hipMemcpyAsync(out + size_t(step) * D.S * D.d, xbuf, act_bytes, hipMemcpyDeviceToDevice, s),
-                  "copy out");
+    if (fresh[step]) {
+      if ((rc = stack_fresh_step(st, D, chain, step, x_in, temb_steps, out, ws, step == 0, s))) return rc;
+      fb = fa;
+      fa = step;
+      continue;
+    }
+    // skipped: first-order finite difference in t through the last two
+    // computed outputs (a copy of the last one while only one exists)
+    const float w = fb < 0 ? 0.f : float((tt(step) - tt(fa)) / (tt(fa) - tt(fb)));
+    DIT_CHECK_HIP(dit::launch_extrapolate(out + size_t(fa) * act, fb < 0 ? nullptr : out + size_t(fb) * act, w,
+                                          out + size_t(step) * act, chain ? xbuf : nullptr, act, s),
+                  "extrapolate");
   }
   return DIT_OK;
 }

@@ -1,7 +1,8 @@
 // Memory-bound kernels of the single-stream block, for gfx950:
 //   modulation GEMV (SiLU(temb) -> shift | scale | gate),
 //   fused LayerNorm + adaLN modulate, gated residual,
-//   per-head QK RMSNorm + RoPE, RoPE cos/sin tables.
+//   per-head QK RMSNorm + RoPE, RoPE cos/sin tables, and the output
+//   prediction of a skipped denoising step.
 // These are the "cast / modulate / norm" HBM round trips between the GEMMs
 // that the Flux page (ChituDiffusion, section 2) finds in the eager trace and
 // that its section 1.1 fuses; here each is one pass over HBM with 16-byte
@@ -314,6 +315,37 @@ __global__ void rope_table_kernel(const int32_t* __restrict__ pos, RopeAxes ax, 
   rsin[i] = s;
 }
 
+// ------------------------------------------------------------------------
+// Step prediction for a skipped denoising step: y = a + w (a - b) over n
+// bf16 values (a, b the outputs of the last two computed steps), or y = a
+// when b is NULL; written to y1 and, when non-NULL, also to y2.  Flat
+// streaming: each workgroup owns a contiguous run of 4 x 256 16-byte chunks.
+// ------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+extrapolate_kernel(const bf16_t* __restrict__ a, const bf16_t* __restrict__ b, float w, bf16_t* __restrict__ y1,
+                   bf16_t* __restrict__ y2, long long n8) {
+  const long long base = (long long)blockIdx.x * 1024;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const long long i = base + k * 256 + threadIdx.x;
+    if (i >= n8) return;
+    float fa[8], o[8];
+    unpack8(reinterpret_cast<const u32x4*>(a)[i], fa);
+    if (b) {
+      float fb[8];
+      unpack8(reinterpret_cast<const u32x4*>(b)[i], fb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(w, fa[e] - fb[e], fa[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fa[e];
+    }
+    const u32x4 v = pack8(o);
+    reinterpret_cast<u32x4*>(y1)[i] = v;
+    if (y2) reinterpret_cast<u32x4*>(y2)[i] = v;
+  }
+}
+
 // ------------------------------------------------------------------------ launchers
 static int rows_per_wave_for(int rows, int target_waves) {
   int rpw = (rows + target_waves - 1) / target_waves;
@@ -427,6 +459,15 @@ __global__ void probe_stamp_kernel(unsigned long long* ch, int finish) {
 
 hipError_t launch_probe_stamp(unsigned long long* ch, int finish, hipStream_t st) {
   probe_stamp_kernel<<<1, 64, 0, st>>>(ch, finish);
+  return hipGetLastError();
+}
+
+hipError_t launch_extrapolate(const bf16_t* a, const bf16_t* b, float w, bf16_t* y1, bf16_t* y2, size_t n,
+                              hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  if (n % 8 != 0) return hipErrorInvalidValue;
+  const long long n8 = (long long)(n / 8);
+  extrapolate_kernel<<<dim3((unsigned)((n8 + 1023) / 1024)), dim3(256), 0, st>>>(a, b, w, y1, y2, n8);
   return hipGetLastError();
 }
 

@@ -92,6 +92,10 @@ hipError_t launch_attention_partial(const bf16_t* qkv, int S, int H, int DH, int
 hipError_t launch_attention_merge(const float* o_parts, const float* lses, int n_chunks, int S, int H, int DH,
                                   bf16_t* out, int ld_out, hipStream_t st);
 
+// y1 (and y2 if non-NULL) = a + w (a - b), or a when b is NULL; n bf16 values, n % 8 == 0
+hipError_t launch_extrapolate(const bf16_t* a, const bf16_t* b, float w, bf16_t* y1, bf16_t* y2, size_t n,
+                              hipStream_t st);
+
 // timing probe channel ch[2]: finish == 0 stamps ch[0], else ch[1] += now - ch[0]
 hipError_t launch_probe_stamp(unsigned long long* ch, int finish, hipStream_t st);
 

@@ -259,6 +259,25 @@ int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, const dit_block
                      int n_steps, const float* rope_cos, const float* rope_sin, dit_bf16* out,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* Step-level replay/skip (the control of a model-level feature cache such as
+ * MeanCache, Flux page section 7: the captured forward stays whole and the
+ * cache only decides, per denoising step, whether to replay it or to
+ * predict the step's output from history).  As dit_stack_replay, except
+ * that only the steps with fresh[s] != 0 replay the graph.  A skipped step
+ * s gets the first-order finite difference through the outputs of the last
+ * two computed steps a > b:
+ *   out[s] = out[a] + (t_s - t_a) / (t_a - t_b) * (out[a] - out[b])
+ * (out[a] itself while only one step has been computed), in fp32 from the
+ * stored bf16 outputs, rounded once to bf16.  With DIT_STACK_CHAIN the
+ * prediction is also the next step's input.  fresh: HOST array [n_steps],
+ * fresh[0] must be nonzero.  t_steps: HOST array [n_steps] of strictly
+ * monotonic step times (e.g. the sampler's timesteps) or NULL for t_s = s.
+ * Shares the stack's captured graph and key with dit_stack_replay. */
+int dit_stack_replay_cached(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks,
+                            int n_blocks, const dit_bf16* x_in, const dit_bf16* temb_steps, int n_steps,
+                            const float* rope_cos, const float* rope_sin, dit_bf16* out, void* workspace,
+                            size_t ws_bytes, const uint8_t* fresh, const float* t_steps, void* stream);
+
 /* Timing probes (diagnostics for benchmarks; must be set before the first
  * replay, i.e. before the graph is captured; DIT_ERR_GRAPH_KEY after).  For
  * every block and every kernel i (0 modulation, 1 LayerNorm+modulate,

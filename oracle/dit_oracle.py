@@ -34,6 +34,9 @@ Readings of what the pages leave open (all are documented with the tests):
     attention and MLP branches in sequence, each with its own
     LayerNorm+modulate and gated residual; the sequential video block is
     the same with a single stream (no cross-attention);
+  * step-level skip (the MeanCache-style control of the Flux page, section
+    7): a skipped step's output is the first-order finite difference in the
+    step time through the stored outputs of the last two computed steps;
   * chunked attention (the one-GPU math of ring attention): a chunk's
     partial output is the softmax average over the chunk's keys alone, its
     lse the natural log of the chunk's sum of exp(score); partials of
@@ -374,3 +377,53 @@ def stack_forward(shape, weights_list, x_in, temb_steps, pos, chain=False, bf16_
         outs.append(cur)
         xs = round_bf16(cur) if bf16_io else cur
     return np.stack(outs)
+
+
+# ------------------------------------------------ step-level replay / skip
+def extrapolate_step(out_a, out_b, t_s, t_a, t_b):
+    """Prediction of a skipped step's output from history: the first-order
+    finite difference in the step time through the outputs of the last two
+    computed steps a (most recent, time t_a) and b (time t_b),
+        out_a + (t_s - t_a) / (t_a - t_b) * (out_a - out_b),
+    or out_a itself when no second step exists (out_b is None).  The Flux
+    page (section 7) describes MeanCache's skipped steps as a finite-
+    difference prediction from history that never enters the model."""
+    a = np.asarray(out_a, F64)
+    if out_b is None:
+        return a.copy()
+    return a + (t_s - t_a) / (t_a - t_b) * (a - np.asarray(out_b, F64))
+
+
+def stack_forward_cached(shape, weights_list, x_in, temb_steps, pos, fresh, t=None, chain=False):
+    """stack_forward in which only the steps with fresh[s] run the block
+    stack; a skipped step's output is extrapolate_step() from the stored
+    (bf16) outputs of the last two computed steps, t[s] the step times
+    (the step index when t is None).  With ``chain`` the next step starts
+    from this step's stored output, computed or predicted.  Returns
+    [n_steps, S, d]: computed steps unrounded, predicted steps from the
+    rounded history."""
+    n = len(temb_steps)
+    tt = list(range(n)) if t is None else [float(v) for v in t]
+    assert n == 0 or fresh[0], "step 0 has no history"
+    outs, stored = [], []
+    hist = []   # step indices of computed steps, most recent last
+    cur_in = np.asarray(x_in, F64)
+    for s in range(n):
+        if fresh[s]:
+            cur = cur_in if chain else np.asarray(x_in, F64)
+            for b, w in enumerate(weights_list):
+                cur = block_forward(shape, w, cur, temb_steps[s], pos)
+                if b + 1 < len(weights_list):
+                    cur = round_bf16(cur)
+            hist.append(s)
+            y = cur
+        else:
+            a = hist[-1]
+            bb = hist[-2] if len(hist) > 1 else None
+            y = extrapolate_step(stored[a], None if bb is None else stored[bb], tt[s], tt[a],
+                                 None if bb is None else tt[bb])
+        outs.append(y)
+        stored.append(round_bf16(y))
+        cur_in = stored[-1]
+    return np.stack(outs) if outs else np.zeros((0,) + np.asarray(x_in).shape)
+

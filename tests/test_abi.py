@@ -175,6 +175,30 @@ def test_stack_argument_checks(lib):
     assert lib.dit_stack_destroy(None) == B.DIT_OK
 
 
+def test_stack_cached_argument_checks(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    P = ctypes.c_void_p(0x1000)
+    h = ctypes.c_void_p()
+    assert lib.dit_stack_create(ctypes.byref(h)) == B.DIT_OK and h.value
+    c = cfg()
+    w = (B.BlockWeightsC * 1)(B.BlockWeightsC(0x1000, 0, 0x1000, 0, 0x1000, 0, 0x1000, 0x1000))
+    need = B.stack_workspace_bytes(c)
+
+    def rep(fresh, t, ns=3, ws_bytes=need, st=h):
+        fr = None if fresh is None else ctypes.cast((ctypes.c_uint8 * len(fresh))(*fresh), ctypes.c_void_p)
+        ts = None if t is None else ctypes.cast((ctypes.c_float * len(t))(*t), ctypes.c_void_p)
+        return lib.dit_stack_replay_cached(st, ctypes.byref(c), ctypes.cast(w, ctypes.c_void_p), 1, P, P, ns, P, P,
+                                           P, P, ws_bytes, fr, ts, None)
+    assert rep(None, None) == B.DIT_ERR_INVALID_ARG                      # fresh missing
+    assert rep([0, 1, 1], None) == B.DIT_ERR_INVALID_ARG                 # step 0 has no history
+    assert rep([1, 0, 1], [1.0, 0.5, 0.5]) == B.DIT_ERR_INVALID_ARG      # not strictly monotonic
+    assert rep([1, 0, 1], [0.0, 1.0, 0.5]) == B.DIT_ERR_INVALID_ARG
+    assert rep([1, 0, 1], [0.0, float("nan"), 2.0]) == B.DIT_ERR_INVALID_ARG
+    assert rep([1, 0, 1], [1.0, 0.5, 0.25], st=None) == B.DIT_ERR_INVALID_ARG
+    assert rep([1, 0, 1], None, ws_bytes=need - 256) == B.DIT_ERR_WORKSPACE
+    assert lib.dit_stack_destroy(h) == B.DIT_OK
+
+
 def test_stack_probe_argument_checks(lib):
     from diffusion_transformer_dit_amd import binding as B
     h = ctypes.c_void_p()

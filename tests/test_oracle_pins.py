@@ -420,9 +420,55 @@ def pin_double_block_reductions(o):
     assert np.allclose(yp, y[perm], rtol=1e-12, atol=1e-12)
 
 
+def pin_extrapolate_step(o):
+    # exact on histories that are affine in the step time, for any times
+    A = RNG.standard_normal((5, 7))
+    Bv = RNG.standard_normal((5, 7))
+    f = lambda t: A + Bv * t
+    for ta, tb, ts in ((3.0, 2.0, 4.0), (0.7, 0.9, 0.1), (10.0, 2.0, 13.5), (1.0, 0.0, 1.0)):
+        assert np.allclose(o.extrapolate_step(f(ta), f(tb), ts, ta, tb), f(ts), rtol=1e-12, atol=1e-12)
+    # zero-order without a second point; the prediction at t_a is out_a
+    assert np.array_equal(o.extrapolate_step(A, None, 5.0, 1.0, None), A)
+    assert np.array_equal(o.extrapolate_step(A, Bv, 2.0, 2.0, 1.0), A)
+    # uniform steps: out_s = 2 out_a - out_b
+    assert np.allclose(o.extrapolate_step(A, Bv, 6, 5, 4), 2 * A - Bv, rtol=1e-14, atol=1e-14)
+
+
+def pin_stack_cached(o):
+    sh, w, x, temb, pos = _small_block()
+    w2 = DI.block_weights(sh, block=1, sigma=0.1)
+    tembs = [temb, temb * 0.5, temb * 0.25, temb * -0.5, temb * 0.75]
+    full = o.stack_forward(sh, [w, w2], x, tembs, pos)
+    # every step computed -> the plain stack, bitwise
+    assert np.array_equal(o.stack_forward_cached(sh, [w, w2], x, tembs, pos, [1] * 5), full)
+    # steps 2 and 4 skipped: computed steps unchanged, skipped ones predicted
+    # from the bf16-stored history (times t)
+    rb = lambda a: torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).double().numpy()
+    t = [1.0, 0.8, 0.55, 0.3, 0.1]
+    got = o.stack_forward_cached(sh, [w, w2], x, tembs, pos, [1, 1, 0, 1, 0], t=t)
+    for s_ in (0, 1, 3):
+        assert np.array_equal(got[s_], full[s_])
+    p2 = rb(full[1]) + (t[2] - t[1]) / (t[1] - t[0]) * (rb(full[1]) - rb(full[0]))
+    p4 = rb(full[3]) + (t[4] - t[3]) / (t[3] - t[1]) * (rb(full[3]) - rb(full[1]))
+    assert np.allclose(got[2], p2, rtol=1e-12, atol=1e-12)
+    assert np.allclose(got[4], p4, rtol=1e-12, atol=1e-12)
+    # only step 0 computed: every later step holds its output
+    hold = o.stack_forward_cached(sh, [w, w2], x, tembs, pos, [1, 0, 0, 0, 0])
+    for s_ in range(1, 5):
+        assert np.array_equal(hold[s_], rb(full[0]))
+    # chained: the step after a skipped one starts from the stored prediction
+    ch = o.stack_forward_cached(sh, [w, w2], x, tembs[:4], pos, [1, 1, 0, 1], chain=True)
+    c0 = o.stack_forward(sh, [w, w2], x, tembs[:2], pos, chain=True)
+    assert np.array_equal(ch[:2], c0)
+    pred = rb(c0[1]) + (rb(c0[1]) - rb(c0[0]))
+    assert np.allclose(ch[2], pred, rtol=1e-12, atol=1e-12)
+    nxt = o.block_forward(sh, w2, rb(o.block_forward(sh, w, rb(ch[2]), tembs[3], pos)), tembs[3], pos)
+    assert np.allclose(ch[3], nxt, rtol=1e-12, atol=1e-12)
+
+
 PINS = [pin_layer_norm, pin_modulate, pin_gated_residual, pin_silu, pin_gelu, pin_linear,
         pin_modulation, pin_rms_norm, pin_rope, pin_attention, pin_attention_chunks, pin_block, pin_round_bf16,
-        pin_stack, pin_double_block, pin_double_block_reductions]
+        pin_stack, pin_double_block, pin_double_block_reductions, pin_extrapolate_step, pin_stack_cached]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -644,6 +690,28 @@ def test_planted_stream_modulation_order_is_caught(monkeypatch):
     monkeypatch.setattr(O, "stream_modulation", _mut_stream_modulation_branch_order)
     with pytest.raises(AssertionError):
         pin_double_block(O)
+
+
+def _mut_extrapolate_sign(out_a, out_b, t_s, t_a, t_b):
+    if out_b is None:
+        return np.asarray(out_a, np.float64).copy()
+    return np.asarray(out_a, np.float64) - (t_s - t_a) / (t_a - t_b) * (np.asarray(out_a) - np.asarray(out_b))
+
+
+def _mut_extrapolate_step_index(out_a, out_b, t_s, t_a, t_b):
+    # ignores the step times: always one step ahead
+    if out_b is None:
+        return np.asarray(out_a, np.float64).copy()
+    return 2 * np.asarray(out_a, np.float64) - np.asarray(out_b)
+
+
+@pytest.mark.parametrize("mutant", [_mut_extrapolate_sign, _mut_extrapolate_step_index])
+def test_planted_extrapolation_mistake_is_caught(monkeypatch, mutant):
+    monkeypatch.setattr(O, "extrapolate_step", mutant)
+    with pytest.raises(AssertionError):
+        pin_extrapolate_step(O)
+    with pytest.raises(AssertionError):
+        pin_stack_cached(O)
 
 
 def test_planted_linear_transpose_is_caught(monkeypatch):
