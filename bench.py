@@ -530,7 +530,37 @@ def main():
         "ms_50_steps_cached": round(ms_cached, 2), "speedup": round(ms_all / ms_cached, 3),
     }
     log(f"step skip: 50 steps {ms_all:.1f} ms all computed, {ms_cached:.1f} ms with {sum(fresh)} computed")
-    del out50, temb50
+    del out50
+    # ---- the Flux composition: 19 two-stream blocks then 38 single-stream
+    # blocks in one captured graph (the 57 blocks of the pages' forward)
+    import dit_inputs as DI
+    nd_, ns_ = 19, 38
+    one = torch.ones(DH, device=dev)
+    sw = lambda: B.StreamWeights(randn((6 * D, D), 0.02), randn((6 * D,), 0.02), randn((3 * D, D), 0.02),
+                                 randn((3 * D,), 0.02), one, one, randn((D, D), 0.02), randn((D,), 0.02),
+                                 randn((MLP, D), 0.02), randn((MLP,), 0.02), randn((D, MLP), 0.02), randn((D,), 0.02))
+    fdoubles = [(sw(), sw()) for _ in range(nd_)]
+    fsingles = blocks[:ns_]
+    wsf = B.alloc_workspace(B.stack_mixed_workspace_bytes(cfg))
+    outf = torch.empty(4, S, D, dtype=torch.bfloat16, device=dev)
+    stf = B.Stack()
+    stf.replay_mixed(cfg, DI.FLUX.text_tokens, fdoubles, fsingles, x_in, temb[:1], rc, rs, outf[:1], wsf)
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    stf.replay_mixed(cfg, DI.FLUX.text_tokens, fdoubles, fsingles, x_in, temb50[:3], rc, rs, outf[1:4], wsf)
+    f1.record()
+    torch.cuda.synchronize()
+    ms_flux = f0.elapsed_time(f1) / 3
+    stf.close()
+    result["flux_forward"] = {
+        "workload": "Flux transformer blocks: 19 two-stream (512 text + 4096 image tokens) + 38 single-stream, "
+                    "S=4608, d=3072, one captured graph per denoising step",
+        "ms_per_step": round(ms_flux, 2),
+        "pages_h20_ms_per_forward_eager": 762.7, "pages_h20_ms_per_forward_compiled": 637.8,
+        "note": "context only: the pages' figures are another machine's whole transformer forward",
+    }
+    log(f"flux forward (19 two-stream + 38 single-stream blocks): {ms_flux:.2f} ms per step")
+    del fdoubles, wsf, outf, temb50
     ob = other_block_times(B, g, dev)
     for v in ob.values():
         v["note"] = "one block forward captured in a graph and replayed (same weights each replay)"

@@ -71,6 +71,9 @@ SIGNATURES = {
     "dit_attention_merge": ([VP, VP, I64, I64, I64, I64, VP, I64, VP], ctypes.c_int),
     "dit_stack_replay_cached": ([VP, VP, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP, VP, VP, SZ, VP, VP, VP],
                                 ctypes.c_int),
+    "dit_stack_mixed_workspace_bytes": ([VP], SZ),
+    "dit_stack_replay_mixed": ([VP, VP, I64, VP, VP, ctypes.c_int, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP,
+                                VP, VP, SZ, VP, VP, VP], ctypes.c_int),
     "dit_stack_set_probe": ([VP, ctypes.c_uint32], ctypes.c_int),
     "dit_stack_probe_ms": ([VP, VP, ctypes.c_int], ctypes.c_int),
     "dit_last_error": ([], ctypes.c_char_p),
@@ -356,6 +359,10 @@ def stack_workspace_bytes(cfg: BlockConfig) -> int:
     return int(_lib.dit_stack_workspace_bytes(ctypes.byref(cfg)))
 
 
+def stack_mixed_workspace_bytes(cfg: BlockConfig) -> int:
+    return int(_lib.dit_stack_mixed_workspace_bytes(ctypes.byref(cfg)))
+
+
 def alloc_workspace(nbytes: int, device="cuda"):
     # torch's caching allocator returns 512-byte aligned blocks
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -453,3 +460,38 @@ class Stack:
                                             _p(workspace), workspace.numel(), ctypes.cast(fr, VP),
                                             None if ts is None else ctypes.cast(ts, VP), _stream(stream)))
         return out
+
+    def replay_mixed(self, cfg, txt_len, doubles, singles, x_in, temb_steps, rope_cos, rope_sin, out, workspace,
+                     fresh=None, t_steps=None, stream=None):
+        """A Flux-style stack: the two-stream blocks ``doubles`` (a list of
+        (text StreamWeights or None, image StreamWeights or None)) then the
+        single-stream blocks ``singles``; steps as in replay_cached (fresh
+        None = every step computed)."""
+        _need(x_in, BF16, "x_in", 2)
+        _need(temb_steps, BF16, "temb_steps", 2)
+        _need(out, BF16, "out", 3)
+        _need(workspace, torch.uint8, "workspace", 1)
+        n_steps = temb_steps.shape[0]
+        if out.shape != (n_steps, cfg.seq_len, cfg.dim):
+            raise ValueError("out must be [n_steps, S, d]")
+        nd, ns = len(doubles), len(singles)
+        empty = StreamWeightsC()
+        txt = (StreamWeightsC * max(nd, 1))(*[(t.c if t is not None else empty) for t, _ in doubles])
+        img = (StreamWeightsC * max(nd, 1))(*[(i.c if i is not None else empty) for _, i in doubles])
+        sg = (BlockWeightsC * max(ns, 1))(*[b.c for b in singles])
+        fr = None if fresh is None else (ctypes.c_uint8 * max(n_steps, 1))(*[1 if f else 0 for f in fresh])
+        ts = None if t_steps is None else (ctypes.c_float * max(n_steps, 1))(*[float(t) for t in t_steps])
+        if (fresh is not None and len(fresh) != n_steps) or (t_steps is not None and len(t_steps) != n_steps):
+            raise ValueError("fresh / t_steps must have one entry per step")
+        self._keep = (doubles, singles, txt, img, sg)
+        no_txt = nd == 0 or all(t is None for t, _ in doubles)
+        no_img = nd == 0 or all(i is None for _, i in doubles)
+        _check(_lib.dit_stack_replay_mixed(self.handle, ctypes.byref(cfg), int(txt_len),
+                                           None if no_txt else ctypes.cast(txt, VP),
+                                           None if no_img else ctypes.cast(img, VP), nd,
+                                           None if ns == 0 else ctypes.cast(sg, VP), ns, _p(x_in), _p(temb_steps),
+                                           n_steps, _p(rope_cos), _p(rope_sin), _p(out), _p(workspace),
+                                           workspace.numel(), None if fr is None else ctypes.cast(fr, VP),
+                                           None if ts is None else ctypes.cast(ts, VP), _stream(stream)))
+        return out
+

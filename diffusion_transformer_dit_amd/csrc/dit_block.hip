@@ -3,6 +3,7 @@
 // only; the kernels live in elementwise.hip, gemm.hip and attention.hip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -521,9 +522,36 @@ struct dit_stack {
 };
 
 namespace {
-std::vector<uintptr_t> make_key(const dit_block_config* cfg, const dit_block_weights* blocks, int n_blocks,
-                                const dit_bf16* x_in, const float* rcos, const float* rsin, void* ws,
-                                size_t ws_bytes, uint32_t probe_mask) {
+// The blocks a stack replays: n_double two-stream blocks (text rows [0, T)),
+// then n_single single-stream blocks, all on one [S, d] activation.
+struct StackPlan {
+  int64_t T = 0;
+  const dit_stream_weights* txt = nullptr;
+  const dit_stream_weights* img = nullptr;
+  int n_double = 0;
+  const dit_block_weights* singles = nullptr;
+  int n_single = 0;
+};
+
+// Workspace of a stack: the per-block scratch (the larger of the two block
+// kinds when the plan has two-stream blocks), then the activation carried
+// from block to block and the staged temb.
+struct StackWs {
+  size_t xbuf, tbuf, end;
+};
+
+StackWs stack_ws(const Dims& D, bool mixed) {
+  size_t o = layout(D).block_end;
+  if (mixed) o = std::max(o, mm_layout(D).end);
+  StackWs W;
+  W.xbuf = o; o = align256(o + size_t(D.S) * D.d * 2);
+  W.tbuf = o; o = align256(o + size_t(D.tdim) * 2);
+  W.end = o;
+  return W;
+}
+
+std::vector<uintptr_t> make_key(const dit_block_config* cfg, const StackPlan& P, const dit_bf16* x_in,
+                                const float* rcos, const float* rsin, void* ws, size_t ws_bytes, uint32_t probe_mask) {
   std::vector<uintptr_t> k;
   k.push_back(uintptr_t(cfg->seq_len));
   k.push_back(uintptr_t(cfg->dim));
@@ -537,18 +565,32 @@ std::vector<uintptr_t> make_key(const dit_block_config* cfg, const dit_block_wei
   k.push_back(e1);
   k.push_back(e2);
   k.push_back(cfg->flags);
-  k.push_back(uintptr_t(n_blocks));
+  k.push_back(uintptr_t(P.n_double));
+  k.push_back(uintptr_t(P.T));
+  k.push_back(uintptr_t(P.n_single));
   k.push_back(uintptr_t(x_in));
   k.push_back(uintptr_t(rcos));
   k.push_back(uintptr_t(rsin));
   k.push_back(uintptr_t(ws));
   k.push_back(uintptr_t(ws_bytes));
   k.push_back(uintptr_t(probe_mask));
-  for (int b = 0; b < n_blocks; ++b) {
-    const dit_block_weights& w = blocks[b];
-    for (const void* p : {(const void*)w.w_mod, (const void*)w.b_mod, (const void*)w.w1, (const void*)w.b1,
+  for (int b = 0; b < P.n_double; ++b)
+    for (const dit_stream_weights* sw : {P.txt ? &P.txt[b] : nullptr, P.img ? &P.img[b] : nullptr}) {
+      if (!sw) {
+        k.push_back(0);
+        continue;
+      }
+      for (const void* q : {(const void*)sw->w_mod, (const void*)sw->b_mod, (const void*)sw->w_qkv,
+                            (const void*)sw->b_qkv, (const void*)sw->q_norm_w, (const void*)sw->k_norm_w,
+                            (const void*)sw->w_o, (const void*)sw->b_o, (const void*)sw->w_fc1, (const void*)sw->b_fc1,
+                            (const void*)sw->w_fc2, (const void*)sw->b_fc2})
+        k.push_back(uintptr_t(q));
+    }
+  for (int b = 0; b < P.n_single; ++b) {
+    const dit_block_weights& w = P.singles[b];
+    for (const void* q : {(const void*)w.w_mod, (const void*)w.b_mod, (const void*)w.w1, (const void*)w.b1,
                           (const void*)w.w2, (const void*)w.b2, (const void*)w.q_norm_w, (const void*)w.k_norm_w})
-      k.push_back(uintptr_t(p));
+      k.push_back(uintptr_t(q));
   }
   return k;
 }
@@ -574,39 +616,56 @@ extern "C" int dit_stack_destroy(dit_stack* st) {
 extern "C" size_t dit_stack_workspace_bytes(const dit_block_config* cfg) {
   Dims D;
   if (dims_of(cfg, &D)) return 0;
-  return layout(D).stack_end;
+  return stack_ws(D, false).end;
+}
+
+extern "C" size_t dit_stack_mixed_workspace_bytes(const dit_block_config* cfg) {
+  Dims D;
+  if (dims_of(cfg, &D)) return 0;
+  return stack_ws(D, true).end;
 }
 
 namespace {
 // Argument checks shared by the replay entry points, then the capture of the
 // block sequence on first use.
-int stack_setup(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks, int n_blocks,
-                const dit_bf16* x_in, const dit_bf16* temb_steps, int n_steps, const float* rope_cos,
-                const float* rope_sin, dit_bf16* out, void* workspace, size_t ws_bytes, hipStream_t s, Dims* Dout) {
+int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, const dit_bf16* x_in,
+                const dit_bf16* temb_steps, int n_steps, const float* rope_cos, const float* rope_sin, dit_bf16* out,
+                void* workspace, size_t ws_bytes, hipStream_t s, Dims* Dout) {
   if (!st) return fail(DIT_ERR_INVALID_ARG, "stack is NULL");
   Dims D;
   int rc = dims_of(cfg, &D);
   if (rc) return rc;
-  if (!blocks || n_blocks <= 0) return fail(DIT_ERR_INVALID_ARG, "n_blocks=%d", n_blocks);
+  if (P.n_double < 0 || P.n_single < 0 || P.n_double + P.n_single <= 0)
+    return fail(DIT_ERR_INVALID_ARG, "n_double=%d n_single=%d", P.n_double, P.n_single);
   if (n_steps < 0) return fail(DIT_ERR_INVALID_ARG, "n_steps=%d", n_steps);
-  for (int b = 0; b < n_blocks; ++b)
-    if ((rc = check_weights(&blocks[b]))) return rc;
+  if (P.n_single > 0 && !P.singles) return fail(DIT_ERR_INVALID_ARG, "single-stream blocks are NULL");
+  for (int b = 0; b < P.n_single; ++b)
+    if ((rc = check_weights(&P.singles[b]))) return rc;
+  if (P.n_double > 0) {
+    if (P.T < 0 || P.T > D.S) return fail(DIT_ERR_INVALID_ARG, "txt_len=%lld outside [0, %d]", (long long)P.T, D.S);
+    if (P.T > 0 && !P.txt) return fail(DIT_ERR_INVALID_ARG, "text stream weights are NULL");
+    if (P.T < D.S && !P.img) return fail(DIT_ERR_INVALID_ARG, "image stream weights are NULL");
+    for (int b = 0; b < P.n_double; ++b) {
+      if (P.T > 0 && (rc = check_stream_weights(&P.txt[b], "text"))) return rc;
+      if (P.T < D.S && (rc = check_stream_weights(&P.img[b], "image"))) return rc;
+    }
+  }
   if (!x_in || !temb_steps || !rope_cos || !rope_sin || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   if ((rc = check_aligned({x_in, temb_steps, rope_cos, rope_sin, out}))) return rc;
-  const WsLayout L = layout(D);
-  if (!workspace || ws_bytes < L.stack_end)
-    return fail(DIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.stack_end);
+  const StackWs W = stack_ws(D, P.n_double > 0);
+  if (!workspace || ws_bytes < W.end) return fail(DIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, W.end);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(DIT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (st->probe_mask && P.n_double > 0)
+    return fail(DIT_ERR_INVALID_ARG, "timing probes cover stacks of single-stream blocks only");
   if ((rc = check_not_capturing(s))) return rc;
   *Dout = D;
 
   const bool chain = (cfg->flags & DIT_STACK_CHAIN) != 0;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  dit_bf16* xbuf = reinterpret_cast<dit_bf16*>(ws + L.xbuf);
-  dit_bf16* tbuf = reinterpret_cast<dit_bf16*>(ws + L.tbuf);
+  dit_bf16* xbuf = reinterpret_cast<dit_bf16*>(ws + W.xbuf);
+  dit_bf16* tbuf = reinterpret_cast<dit_bf16*>(ws + W.tbuf);
 
-  std::vector<uintptr_t> key =
-      make_key(cfg, blocks, n_blocks, x_in, rope_cos, rope_sin, workspace, ws_bytes, st->probe_mask);
+  std::vector<uintptr_t> key = make_key(cfg, P, x_in, rope_cos, rope_sin, workspace, ws_bytes, st->probe_mask);
   if (st->exec && key != st->key)
     return fail(DIT_ERR_GRAPH_KEY, "stack was captured for another config / pointer set; destroy and re-create it");
   if (st->exec) return DIT_OK;
@@ -618,24 +677,30 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const dit_block_weig
     DIT_CHECK_HIP(hipDeviceGetAttribute(&st->wall_khz, hipDeviceAttributeWallClockRate, dev),
                   "hipDeviceGetAttribute");
     if (st->wall_khz <= 0) return fail(DIT_ERR_HIP, "device reports no wall-clock rate");
-    const size_t bytes = size_t(n_blocks) * kProbeChannels * 2 * sizeof(unsigned long long);
+    const size_t bytes = size_t(P.n_single) * kProbeChannels * 2 * sizeof(unsigned long long);
     if (st->probe_buf) hipFree(st->probe_buf);
     st->probe_buf = nullptr;
     DIT_CHECK_HIP(hipMalloc(&st->probe_buf, bytes), "hipMalloc");
     DIT_CHECK_HIP(hipMemset(st->probe_buf, 0, bytes), "hipMemset");
-    st->probe_blocks = n_blocks;
+    st->probe_blocks = P.n_single;
     st->probe_replays = 0;
   }
   DIT_CHECK_HIP(hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
   int brc = DIT_OK;
-  for (int b = 0; b < n_blocks && brc == DIT_OK; ++b) {
-    const dit_bf16* xin = (b == 0 && !chain) ? x_in : xbuf;
+  int idx = 0;  // position in the whole sequence: only block 0 reads x_in
+  for (int b = 0; b < P.n_double && brc == DIT_OK; ++b, ++idx) {
+    const dit_bf16* xin = (idx == 0 && !chain) ? x_in : xbuf;
+    brc = enqueue_mmdit(D, int(P.T), cfg, P.txt ? &P.txt[b] : nullptr, P.img ? &P.img[b] : nullptr, xin, tbuf,
+                        rope_cos, rope_sin, xbuf, ws, st->cap);
+  }
+  for (int b = 0; b < P.n_single && brc == DIT_OK; ++b, ++idx) {
+    const dit_bf16* xin = (idx == 0 && !chain) ? x_in : xbuf;
     Probe pr;
     if (st->probe_mask) {
       pr.mask = st->probe_mask;
       pr.ch = st->probe_buf + size_t(b) * kProbeChannels * 2;
     }
-    brc = enqueue_block(D, cfg, &blocks[b], xin, tbuf, rope_cos, rope_sin, xbuf, ws, st->cap, pr);
+    brc = enqueue_block(D, cfg, &P.singles[b], xin, tbuf, rope_cos, rope_sin, xbuf, ws, st->cap, pr);
   }
   hipGraph_t g = nullptr;
   hipError_t e = hipStreamEndCapture(st->cap, &g);
@@ -656,47 +721,8 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const dit_block_weig
   return DIT_OK;
 }
 
-// One computed step: stage temb_s, launch the graph, copy the result to out[step].
-int stack_fresh_step(dit_stack* st, const Dims& D, bool chain, int step, const dit_bf16* x_in,
-                     const dit_bf16* temb_steps, dit_bf16* out, unsigned char* ws, bool first, hipStream_t s) {
-  const WsLayout L = layout(D);
-  dit_bf16* xbuf = reinterpret_cast<dit_bf16*>(ws + L.xbuf);
-  dit_bf16* tbuf = reinterpret_cast<dit_bf16*>(ws + L.tbuf);
-  const size_t act_bytes = size_t(D.S) * D.d * 2;
-  if (chain && first) DIT_CHECK_HIP(hipMemcpyAsync(xbuf, x_in, act_bytes, hipMemcpyDeviceToDevice, s), "copy x_in");
-  DIT_CHECK_HIP(hipMemcpyAsync(tbuf, temb_steps + size_t(step) * D.tdim, size_t(D.tdim) * 2,
-                               hipMemcpyDeviceToDevice, s), "copy temb");
-  DIT_CHECK_HIP(hipGraphLaunch(st->exec, s), "hipGraphLaunch");
-  if (st->probe_mask) ++st->probe_replays;
-  DIT_CHECK_HIP(hipMemcpyAsync(out + size_t(step) * D.S * D.d, xbuf, act_bytes, hipMemcpyDeviceToDevice, s),
-                "copy out");
-  return DIT_OK;
-}
-}  // namespace
-
-extern "C" int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks,
-                                int n_blocks, const dit_bf16* x_in, const dit_bf16* temb_steps, int n_steps,
-                                const float* rope_cos, const float* rope_sin, dit_bf16* out, void* workspace,
-                                size_t ws_bytes, void* stream) {
-  hipStream_t s = as_stream(stream);
-  Dims D;
-  int rc = stack_setup(st, cfg, blocks, n_blocks, x_in, temb_steps, n_steps, rope_cos, rope_sin, out, workspace,
-                       ws_bytes, s, &D);
-  if (rc) return rc;
-  const bool chain = (cfg->flags & DIT_STACK_CHAIN) != 0;
-  for (int step = 0; step < n_steps; ++step)
-    if ((rc = stack_fresh_step(st, D, chain, step, x_in, temb_steps, out, static_cast<unsigned char*>(workspace),
-                               step == 0, s)))
-      return rc;
-  return DIT_OK;
-}
-
-extern "C" int dit_stack_replay_cached(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks,
-                                       int n_blocks, const dit_bf16* x_in, const dit_bf16* temb_steps, int n_steps,
-                                       const float* rope_cos, const float* rope_sin, dit_bf16* out,
-                                       void* workspace, size_t ws_bytes, const uint8_t* fresh, const float* t_steps,
-                                       void* stream) {
-  if (n_steps > 0 && !fresh) return fail(DIT_ERR_INVALID_ARG, "fresh is NULL");
+// Checks of the host arrays of a replay with skipped steps.
+int check_schedule(int n_steps, const uint8_t* fresh, const float* t_steps) {
   if (n_steps > 0 && !fresh[0]) return fail(DIT_ERR_INVALID_ARG, "step 0 must be computed (no history before it)");
   if (t_steps) {
     for (int i = 0; i < n_steps; ++i)
@@ -707,32 +733,100 @@ extern "C" int dit_stack_replay_cached(dit_stack* st, const dit_block_config* cf
         return fail(DIT_ERR_INVALID_ARG, "t_steps must be strictly monotonic (step %d)", i);
     }
   }
-  hipStream_t s = as_stream(stream);
-  Dims D;
-  int rc = stack_setup(st, cfg, blocks, n_blocks, x_in, temb_steps, n_steps, rope_cos, rope_sin, out, workspace,
-                       ws_bytes, s, &D);
-  if (rc) return rc;
-  const bool chain = (cfg->flags & DIT_STACK_CHAIN) != 0;
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  dit_bf16* xbuf = reinterpret_cast<dit_bf16*>(ws + layout(D).xbuf);
+  return DIT_OK;
+}
+
+// The denoising steps of a captured stack.  A computed step stages temb_s,
+// launches the graph and copies the result to out[s]; a skipped step
+// (fresh != NULL and fresh[s] == 0) predicts out[s] from the last two
+// computed outputs by a first-order finite difference in t (a copy of the
+// last one while only one exists).  With chain, the step's result is also
+// the next step's input.
+int run_steps(dit_stack* st, const Dims& D, bool chain, bool mixed, const dit_bf16* x_in, const dit_bf16* temb_steps,
+              int n_steps, dit_bf16* out, unsigned char* ws, const uint8_t* fresh, const float* t_steps,
+              hipStream_t s) {
+  const StackWs W = stack_ws(D, mixed);
+  dit_bf16* xbuf = reinterpret_cast<dit_bf16*>(ws + W.xbuf);
+  dit_bf16* tbuf = reinterpret_cast<dit_bf16*>(ws + W.tbuf);
   const size_t act = size_t(D.S) * D.d;
   int fa = -1, fb = -1;  // the last two computed steps
   auto tt = [&](int i) { return t_steps ? double(t_steps[i]) : double(i); };
   for (int step = 0; step < n_steps; ++step) {
-    if (fresh[step]) {
-      if ((rc = stack_fresh_step(st, D, chain, step, x_in, temb_steps, out, ws, step == 0, s))) return rc;
+    if (!fresh || fresh[step]) {
+      if (chain && step == 0)
+        DIT_CHECK_HIP(hipMemcpyAsync(xbuf, x_in, act * 2, hipMemcpyDeviceToDevice, s), "copy x_in");
+      DIT_CHECK_HIP(hipMemcpyAsync(tbuf, temb_steps + size_t(step) * D.tdim, size_t(D.tdim) * 2,
+                                   hipMemcpyDeviceToDevice, s), "copy temb");
+      DIT_CHECK_HIP(hipGraphLaunch(st->exec, s), "hipGraphLaunch");
+      if (st->probe_mask) ++st->probe_replays;
+      DIT_CHECK_HIP(hipMemcpyAsync(out + size_t(step) * act, xbuf, act * 2, hipMemcpyDeviceToDevice, s), "copy out");
       fb = fa;
       fa = step;
       continue;
     }
-    // skipped: first-order finite difference in t through the last two
-    // computed outputs (a copy of the last one while only one exists)
     const float w = fb < 0 ? 0.f : float((tt(step) - tt(fa)) / (tt(fa) - tt(fb)));
     DIT_CHECK_HIP(dit::launch_extrapolate(out + size_t(fa) * act, fb < 0 ? nullptr : out + size_t(fb) * act, w,
                                           out + size_t(step) * act, chain ? xbuf : nullptr, act, s),
                   "extrapolate");
   }
   return DIT_OK;
+}
+
+int replay_plan(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, const dit_bf16* x_in,
+                const dit_bf16* temb_steps, int n_steps, const float* rope_cos, const float* rope_sin, dit_bf16* out,
+                void* workspace, size_t ws_bytes, const uint8_t* fresh, const float* t_steps, void* stream) {
+  int rc;
+  if (fresh && (rc = check_schedule(n_steps, fresh, t_steps))) return rc;
+  hipStream_t s = as_stream(stream);
+  Dims D;
+  if ((rc = stack_setup(st, cfg, P, x_in, temb_steps, n_steps, rope_cos, rope_sin, out, workspace, ws_bytes, s, &D)))
+    return rc;
+  return run_steps(st, D, (cfg->flags & DIT_STACK_CHAIN) != 0, P.n_double > 0, x_in, temb_steps, n_steps, out,
+                   static_cast<unsigned char*>(workspace), fresh, t_steps, s);
+}
+}  // namespace
+
+extern "C" int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks,
+                                int n_blocks, const dit_bf16* x_in, const dit_bf16* temb_steps, int n_steps,
+                                const float* rope_cos, const float* rope_sin, dit_bf16* out, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  if (!blocks || n_blocks <= 0) return fail(DIT_ERR_INVALID_ARG, "n_blocks=%d", n_blocks);
+  StackPlan P;
+  P.singles = blocks;
+  P.n_single = n_blocks;
+  return replay_plan(st, cfg, P, x_in, temb_steps, n_steps, rope_cos, rope_sin, out, workspace, ws_bytes, nullptr,
+                     nullptr, stream);
+}
+
+extern "C" int dit_stack_replay_cached(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks,
+                                       int n_blocks, const dit_bf16* x_in, const dit_bf16* temb_steps, int n_steps,
+                                       const float* rope_cos, const float* rope_sin, dit_bf16* out,
+                                       void* workspace, size_t ws_bytes, const uint8_t* fresh, const float* t_steps,
+                                       void* stream) {
+  if (n_steps > 0 && !fresh) return fail(DIT_ERR_INVALID_ARG, "fresh is NULL");
+  if (!blocks || n_blocks <= 0) return fail(DIT_ERR_INVALID_ARG, "n_blocks=%d", n_blocks);
+  StackPlan P;
+  P.singles = blocks;
+  P.n_single = n_blocks;
+  return replay_plan(st, cfg, P, x_in, temb_steps, n_steps, rope_cos, rope_sin, out, workspace, ws_bytes,
+                     n_steps > 0 ? fresh : nullptr, t_steps, stream);
+}
+
+extern "C" int dit_stack_replay_mixed(dit_stack* st, const dit_block_config* cfg, int64_t txt_len,
+                                      const dit_stream_weights* txt, const dit_stream_weights* img, int n_double,
+                                      const dit_block_weights* singles, int n_single, const dit_bf16* x_in,
+                                      const dit_bf16* temb_steps, int n_steps, const float* rope_cos,
+                                      const float* rope_sin, dit_bf16* out, void* workspace, size_t ws_bytes,
+                                      const uint8_t* fresh, const float* t_steps, void* stream) {
+  StackPlan P;
+  P.T = txt_len;
+  P.txt = txt;
+  P.img = img;
+  P.n_double = n_double;
+  P.singles = singles;
+  P.n_single = n_single;
+  return replay_plan(st, cfg, P, x_in, temb_steps, n_steps, rope_cos, rope_sin, out, workspace, ws_bytes, fresh,
+                     t_steps, stream);
 }
 
 extern "C" int dit_stack_set_probe(dit_stack* st, uint32_t kernel_mask) {

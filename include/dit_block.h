@@ -278,6 +278,27 @@ int dit_stack_replay_cached(dit_stack* st, const dit_block_config* cfg, const di
                             const float* rope_cos, const float* rope_sin, dit_bf16* out, void* workspace,
                             size_t ws_bytes, const uint8_t* fresh, const float* t_steps, void* stream);
 
+/* Bytes of workspace dit_stack_replay_mixed needs (0 on an invalid config). */
+size_t dit_stack_mixed_workspace_bytes(const dit_block_config* cfg);
+
+/* A Flux-style stack: n_double two-stream blocks (text rows [0, txt_len),
+ * weights txt[b] and img[b], HOST arrays of n_double) followed by n_single
+ * single-stream blocks (singles, HOST array), replayed per denoising step
+ * as one captured graph (the Flux page, section 3.1: the model's
+ * transformer_blocks then single_transformer_blocks; section 7: one graph
+ * of the whole model per step).  Steps, chaining and step times as in
+ * dit_stack_replay_cached; fresh may be NULL (every step computed).
+ * txt may be NULL when txt_len == 0 and img when txt_len == S.  Timing
+ * probes are not available for stacks with two-stream blocks.  workspace:
+ * dit_stack_mixed_workspace_bytes(cfg) bytes.  One stack object holds one
+ * captured graph: the key covers both block lists. */
+int dit_stack_replay_mixed(dit_stack* st, const dit_block_config* cfg, int64_t txt_len,
+                           const dit_stream_weights* txt, const dit_stream_weights* img, int n_double,
+                           const dit_block_weights* singles, int n_single, const dit_bf16* x_in,
+                           const dit_bf16* temb_steps, int n_steps, const float* rope_cos, const float* rope_sin,
+                           dit_bf16* out, void* workspace, size_t ws_bytes, const uint8_t* fresh,
+                           const float* t_steps, void* stream);
+
 /* Timing probes (diagnostics for benchmarks; must be set before the first
  * replay, i.e. before the graph is captured; DIT_ERR_GRAPH_KEY after).  For
  * every block and every kernel i (0 modulation, 1 LayerNorm+modulate,

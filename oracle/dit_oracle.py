@@ -379,6 +379,30 @@ def stack_forward(shape, weights_list, x_in, temb_steps, pos, chain=False, bf16_
     return np.stack(outs)
 
 
+def flux_stack_forward(shape, doubles, singles, x_in, temb_steps, pos, n_txt=None, chain=False, bf16_io=True):
+    """stack_forward for a Flux-style stack: the two-stream blocks ``doubles``
+    (a list of (w_txt, w_img)) then the single-stream blocks ``singles``, in
+    order, on one [S, d] activation with the text tokens first (the Flux
+    page, section 3.1, names the two block lists, transformer_blocks then
+    single_transformer_blocks).  Rounding and chaining as in stack_forward.
+    Returns [n_steps, S, d]."""
+    outs = []
+    xs = np.asarray(x_in, F64)
+    kinds = [("d", w) for w in doubles] + [("s", w) for w in singles]
+    for s in range(len(temb_steps)):
+        cur = xs if (chain and s > 0) else np.asarray(x_in, F64)
+        for b, (kind, w) in enumerate(kinds):
+            if kind == "d":
+                cur = double_block_forward(shape, w[0], w[1], cur, temb_steps[s], pos, n_txt=n_txt)
+            else:
+                cur = block_forward(shape, w, cur, temb_steps[s], pos)
+            if bf16_io and b + 1 < len(kinds):
+                cur = round_bf16(cur)
+        outs.append(cur)
+        xs = round_bf16(cur) if bf16_io else cur
+    return np.stack(outs)
+
+
 # ------------------------------------------------ step-level replay / skip
 def extrapolate_step(out_a, out_b, t_s, t_a, t_b):
     """Prediction of a skipped step's output from history: the first-order

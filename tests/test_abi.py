@@ -199,6 +199,35 @@ def test_stack_cached_argument_checks(lib):
     assert lib.dit_stack_destroy(h) == B.DIT_OK
 
 
+def test_stack_mixed_argument_checks(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    P = ctypes.c_void_p(0x1000)
+    h = ctypes.c_void_p()
+    assert lib.dit_stack_create(ctypes.byref(h)) == B.DIT_OK and h.value
+    c = cfg()
+    a = lambda n: (n + 255) // 256 * 256
+    S, d = 256, 256
+    need = B.stack_mixed_workspace_bytes(c)
+    assert need == max(B.block_workspace_bytes(c), B.mmdit_block_workspace_bytes(c)) + a(S * d * 2) + a(d * 2)
+    sw = (B.StreamWeightsC * 2)(*([B.StreamWeightsC(*([0x1000] * 12))] * 2))
+    bw = (B.BlockWeightsC * 1)(B.BlockWeightsC(0x1000, 0, 0x1000, 0, 0x1000, 0, 0x1000, 0x1000))
+    V = lambda arr: ctypes.cast(arr, ctypes.c_void_p)
+
+    def rep(T, txt, img, nd, singles, ns, ws_bytes=need):
+        return lib.dit_stack_replay_mixed(h, ctypes.byref(c), T, txt, img, nd, singles, ns, P, P, 1, P, P, P, P,
+                                          ws_bytes, None, None, None)
+    assert rep(16, V(sw), V(sw), 0, None, 0) == B.DIT_ERR_INVALID_ARG        # no blocks
+    assert rep(16, V(sw), V(sw), -1, V(bw), 1) == B.DIT_ERR_INVALID_ARG
+    assert rep(16, None, V(sw), 2, V(bw), 1) == B.DIT_ERR_INVALID_ARG        # text weights needed
+    assert rep(0, None, None, 2, V(bw), 1) == B.DIT_ERR_INVALID_ARG          # image weights needed
+    assert rep(S + 1, V(sw), V(sw), 2, V(bw), 1) == B.DIT_ERR_INVALID_ARG
+    assert rep(16, V(sw), V(sw), 2, None, 1) == B.DIT_ERR_INVALID_ARG        # singles NULL with n_single 1
+    assert rep(16, V(sw), V(sw), 2, V(bw), 1, need - 256) == B.DIT_ERR_WORKSPACE
+    # a mixed stack needs more than the single-stream stack's workspace
+    assert rep(16, V(sw), V(sw), 2, V(bw), 1, B.stack_workspace_bytes(c)) == B.DIT_ERR_WORKSPACE
+    assert lib.dit_stack_destroy(h) == B.DIT_OK
+
+
 def test_stack_probe_argument_checks(lib):
     from diffusion_transformer_dit_amd import binding as B
     h = ctypes.c_void_p()

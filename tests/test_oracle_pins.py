@@ -466,9 +466,35 @@ def pin_stack_cached(o):
     assert np.allclose(ch[3], nxt, rtol=1e-12, atol=1e-12)
 
 
+def pin_flux_stack(o):
+    sh, wt, wi, x, temb, pos = _small_double()
+    wt2, wi2 = DI.stream_weights(sh, 0, block=1, sigma=0.1), DI.stream_weights(sh, 1, block=1, sigma=0.1)
+    ws_ = DI.block_weights(sh, block=2, sigma=0.1)
+    tembs = [temb, temb * 0.5]
+    rb = lambda a: torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).double().numpy()
+    out = o.flux_stack_forward(sh, [(wt, wi), (wt2, wi2)], [ws_], x, tembs, pos)
+    for s_ in range(2):
+        h1 = rb(o.double_block_forward(sh, wt, wi, x, tembs[s_], pos))
+        h2 = rb(o.double_block_forward(sh, wt2, wi2, h1, tembs[s_], pos))
+        assert np.allclose(out[s_], o.block_forward(sh, ws_, h2, tembs[s_], pos), rtol=1e-12, atol=1e-12)
+    # no two-stream blocks: the single-stream stack
+    assert np.array_equal(o.flux_stack_forward(sh, [], [ws_], x, tembs, pos), o.stack_forward(sh, [ws_], x, tembs, pos))
+    # every gate zero -> the input, bitwise
+    d = sh.dim
+    zg = lambda w: _sw(w, w_mod=np.concatenate([w.w_mod[:2 * d], 0 * w.w_mod[2 * d:3 * d], w.w_mod[3 * d:5 * d],
+                                                0 * w.w_mod[5 * d:]]),
+                       b_mod=np.concatenate([w.b_mod[:2 * d], 0 * w.b_mod[2 * d:3 * d], w.b_mod[3 * d:5 * d],
+                                             0 * w.b_mod[5 * d:]]))
+    wz = DI.BlockWeights(np.concatenate([ws_.w_mod[:2 * d], 0 * ws_.w_mod[2 * d:]]),
+                         np.concatenate([ws_.b_mod[:2 * d], 0 * ws_.b_mod[2 * d:]]), ws_.w1, ws_.b1, ws_.w2, ws_.b2,
+                         ws_.q_norm_w, ws_.k_norm_w)
+    z = o.flux_stack_forward(sh, [(zg(wt), zg(wi))], [wz], x, tembs, pos, chain=True)
+    assert np.array_equal(z[1], x.astype(np.float64))
+
+
 PINS = [pin_layer_norm, pin_modulate, pin_gated_residual, pin_silu, pin_gelu, pin_linear,
         pin_modulation, pin_rms_norm, pin_rope, pin_attention, pin_attention_chunks, pin_block, pin_round_bf16,
-        pin_stack, pin_double_block, pin_double_block_reductions, pin_extrapolate_step, pin_stack_cached]
+        pin_stack, pin_double_block, pin_double_block_reductions, pin_extrapolate_step, pin_stack_cached, pin_flux_stack]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
