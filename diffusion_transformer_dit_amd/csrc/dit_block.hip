@@ -131,12 +131,15 @@ struct Probe {
   unsigned long long* ch = nullptr;    // [kProbeChannels][2] for this block
 };
 
-// The six launches of one block on `st`.  x and y may alias.
+// The six launches of one block on `st`.  x and y may alias.  With mod_pre
+// the modulation vectors were computed beforehand (a stack computes all its
+// blocks' vectors in one launch) and the block's GEMV is skipped.
 int enqueue_block(const Dims& D, const dit_block_config* cfg, const dit_block_weights* w,
                   const dit_bf16* x, const dit_bf16* temb, const float* rcos, const float* rsin,
-                  dit_bf16* y, unsigned char* ws, hipStream_t st, const Probe& pr = Probe()) {
+                  dit_bf16* y, unsigned char* ws, hipStream_t st, const Probe& pr = Probe(),
+                  const float* mod_pre = nullptr) {
   const WsLayout L = layout(D);
-  float* mod = reinterpret_cast<float*>(ws + L.mod);
+  const float* mod = mod_pre ? mod_pre : reinterpret_cast<float*>(ws + L.mod);
   dit_bf16* u = reinterpret_cast<dit_bf16*>(ws + L.u);
   dit_bf16* qkv = reinterpret_cast<dit_bf16*>(ws + L.qkv);
   dit_bf16* cat = reinterpret_cast<dit_bf16*>(ws + L.cat);
@@ -150,8 +153,11 @@ int enqueue_block(const Dims& D, const dit_block_config* cfg, const dit_block_we
     DIT_CHECK_HIP(dit::launch_probe_stamp(pr.ch + 12, 0, st), "probe");
     DIT_CHECK_HIP(dit::launch_probe_stamp(pr.ch + 12, 1, st), "probe");
   }
+  // with mod_pre the bracket of kernel 0 is empty (its probe then reads ~0)
   DIT_CHECK_HIP(pre(0), "probe");
-  DIT_CHECK_HIP(dit::launch_modulation(temb, w->w_mod, w->b_mod, mod, 3 * D.d, D.tdim, st), "modulation");
+  if (!mod_pre)
+    DIT_CHECK_HIP(dit::launch_modulation(temb, w->w_mod, w->b_mod, reinterpret_cast<float*>(ws + L.mod), 3 * D.d,
+                                         D.tdim, st), "modulation");
   DIT_CHECK_HIP(post(0), "probe");
   if (D.S == 0) return DIT_OK;
   DIT_CHECK_HIP(pre(1), "probe");
@@ -215,10 +221,11 @@ MmLayout mm_layout(const Dims& D) {
 // attention and MLP halves (x') stays fp32.  x and y may alias.
 int enqueue_mmdit(const Dims& D, int T, const dit_block_config* cfg, const dit_stream_weights* wt,
                   const dit_stream_weights* wi, const dit_bf16* x, const dit_bf16* temb, const float* rcos,
-                  const float* rsin, dit_bf16* y, unsigned char* ws, hipStream_t st) {
+                  const float* rsin, dit_bf16* y, unsigned char* ws, hipStream_t st, const float* mod_pre = nullptr) {
   const MmLayout L = mm_layout(D);
   const int d = D.d, mlp = D.mlp, half = D.Dh / 2;
-  float* mod0 = reinterpret_cast<float*>(ws + L.mod);
+  // mod_pre: the present streams' six vectors, text first, computed beforehand
+  float* mod0 = mod_pre ? const_cast<float*>(mod_pre) : reinterpret_cast<float*>(ws + L.mod);
   dit_bf16* u = reinterpret_cast<dit_bf16*>(ws + L.u);
   dit_bf16* qkv = reinterpret_cast<dit_bf16*>(ws + L.qkv);
   dit_bf16* o = reinterpret_cast<dit_bf16*>(ws + L.o);
@@ -231,12 +238,13 @@ int enqueue_mmdit(const Dims& D, int T, const dit_block_config* cfg, const dit_s
   } ss[2];
   int n = 0;
   if (T > 0) ss[n++] = Stream{wt, 0, T, mod0};
-  if (D.S - T > 0) ss[n++] = Stream{wi, T, D.S - T, mod0 + 6 * d};
+  if (D.S - T > 0) ss[n++] = Stream{wi, T, D.S - T, mod0 + (mod_pre ? n : 1) * 6 * d};
   if (n == 0) return DIT_OK;
   const size_t rd = size_t(d);
-  for (int i = 0; i < n; ++i)
-    DIT_CHECK_HIP(dit::launch_modulation(temb, ss[i].w->w_mod, ss[i].w->b_mod, ss[i].mod, 6 * d, D.tdim, st),
-                  "modulation");
+  if (!mod_pre)
+    for (int i = 0; i < n; ++i)
+      DIT_CHECK_HIP(dit::launch_modulation(temb, ss[i].w->w_mod, ss[i].w->b_mod, ss[i].mod, 6 * d, D.tdim, st),
+                    "modulation");
   for (int i = 0; i < n; ++i)
     DIT_CHECK_HIP(dit::launch_modulate_norm(x + ss[i].r0 * rd, ss[i].mod, ss[i].mod + d, u + ss[i].r0 * rd,
                                             ss[i].rows, d, cfg->ln_eps, st), "modulate_norm");
@@ -519,6 +527,10 @@ struct dit_stack {
   long long probe_replays = 0;         // probed graph launches since the last read
   int wall_khz = 0;                    // device wall-clock rate
   unsigned long long* probe_buf = nullptr;  // device [n_blocks][kProbeChannels][2]
+  // modulation of every block in one launch per block kind: device tables
+  // of the W_mod / b_mod pointers and the vectors (two-stream blocks first)
+  const dit_bf16** mod_ptrs = nullptr;
+  float* mods = nullptr;
 };
 
 namespace {
@@ -606,6 +618,8 @@ extern "C" int dit_stack_create(dit_stack** out) {
 extern "C" int dit_stack_destroy(dit_stack* st) {
   if (!st) return DIT_OK;
   if (st->probe_buf) hipFree(st->probe_buf);
+  if (st->mod_ptrs) hipFree(st->mod_ptrs);
+  if (st->mods) hipFree(st->mods);
   if (st->exec) hipGraphExecDestroy(st->exec);
   if (st->graph) hipGraphDestroy(st->graph);
   if (st->cap) hipStreamDestroy(st->cap);
@@ -685,13 +699,51 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
     st->probe_blocks = P.n_single;
     st->probe_replays = 0;
   }
+  // Every block's modulation depends on temb only: one launch per block kind
+  // computes them all at the start of the step.  Tables: W_mod pointers of
+  // the two-stream blocks' present streams (text first), then of the
+  // single-stream blocks; the b_mod pointers after them in the same order.
+  const int n_streams = (P.n_double > 0) ? int(P.T > 0) + int(P.T < D.S) : 0;
+  const int n_dm = P.n_double * n_streams, n_mats = n_dm + P.n_single;
+  std::vector<const dit_bf16*> tab(2 * size_t(n_mats));
+  for (int b = 0, m = 0; b < P.n_double; ++b) {
+    if (P.T > 0) tab[m] = P.txt[b].w_mod, tab[n_mats + m] = P.txt[b].b_mod, ++m;
+    if (P.T < D.S) tab[m] = P.img[b].w_mod, tab[n_mats + m] = P.img[b].b_mod, ++m;
+  }
+  for (int b = 0; b < P.n_single; ++b)
+    tab[n_dm + b] = P.singles[b].w_mod, tab[n_mats + n_dm + b] = P.singles[b].b_mod;
+  const size_t n_mod = size_t(n_dm) * 6 * D.d + size_t(P.n_single) * 3 * D.d;
+  if (st->mod_ptrs) hipFree(st->mod_ptrs);
+  if (st->mods) hipFree(st->mods);
+  st->mod_ptrs = nullptr;
+  st->mods = nullptr;
+  DIT_CHECK_HIP(hipMalloc(reinterpret_cast<void**>(&st->mod_ptrs), tab.size() * sizeof(void*)), "hipMalloc");
+  DIT_CHECK_HIP(hipMemcpy(st->mod_ptrs, tab.data(), tab.size() * sizeof(void*), hipMemcpyHostToDevice), "hipMemcpy");
+  DIT_CHECK_HIP(hipMalloc(reinterpret_cast<void**>(&st->mods), n_mod * sizeof(float)), "hipMalloc");
+  float* mods_d = st->mods;                                  // [n_dm][6d]
+  float* mods_s = st->mods + size_t(n_dm) * 6 * D.d;         // [n_single][3d]
+
   DIT_CHECK_HIP(hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
   int brc = DIT_OK;
+  hipError_t me = hipSuccess;
+  if (n_dm > 0)
+    me = dit::launch_modulation_multi(tbuf, st->mod_ptrs, st->mod_ptrs + n_mats, mods_d, n_dm, 6 * D.d, D.tdim,
+                                      st->cap);
+  if (me == hipSuccess && P.n_single > 0) {
+    // probes: kernel 0 of block 0 brackets the whole batched launch
+    const bool pb = (st->probe_mask & 1u) != 0;
+    if (pb) me = dit::launch_probe_stamp(st->probe_buf, 0, st->cap);
+    if (me == hipSuccess)
+      me = dit::launch_modulation_multi(tbuf, st->mod_ptrs + n_dm, st->mod_ptrs + n_mats + n_dm, mods_s,
+                                        P.n_single, 3 * D.d, D.tdim, st->cap);
+    if (me == hipSuccess && pb) me = dit::launch_probe_stamp(st->probe_buf, 1, st->cap);
+  }
+  if (me != hipSuccess) brc = hip_fail(me, "modulation");
   int idx = 0;  // position in the whole sequence: only block 0 reads x_in
   for (int b = 0; b < P.n_double && brc == DIT_OK; ++b, ++idx) {
     const dit_bf16* xin = (idx == 0 && !chain) ? x_in : xbuf;
     brc = enqueue_mmdit(D, int(P.T), cfg, P.txt ? &P.txt[b] : nullptr, P.img ? &P.img[b] : nullptr, xin, tbuf,
-                        rope_cos, rope_sin, xbuf, ws, st->cap);
+                        rope_cos, rope_sin, xbuf, ws, st->cap, mods_d + size_t(b) * n_streams * 6 * D.d);
   }
   for (int b = 0; b < P.n_single && brc == DIT_OK; ++b, ++idx) {
     const dit_bf16* xin = (idx == 0 && !chain) ? x_in : xbuf;
@@ -700,7 +752,8 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
       pr.mask = st->probe_mask;
       pr.ch = st->probe_buf + size_t(b) * kProbeChannels * 2;
     }
-    brc = enqueue_block(D, cfg, &P.singles[b], xin, tbuf, rope_cos, rope_sin, xbuf, ws, st->cap, pr);
+    brc = enqueue_block(D, cfg, &P.singles[b], xin, tbuf, rope_cos, rope_sin, xbuf, ws, st->cap, pr,
+                        mods_s + size_t(b) * 3 * D.d);
   }
   hipGraph_t g = nullptr;
   hipError_t e = hipStreamEndCapture(st->cap, &g);

@@ -316,6 +316,67 @@ __global__ void rope_table_kernel(const int32_t* __restrict__ pos, RopeAxes ax, 
 }
 
 // ------------------------------------------------------------------------
+// The modulation GEMVs of a whole block stack in one launch: matrix m of the
+// table (rows_per_mat rows each) gives mods[m * rows_per_mat + r].  The same
+// per-row arithmetic as mod_gemv_kernel (identical results); a wave walks
+// `rows_per_wave` consecutive rows and loads the next row's chunks before it
+// reduces the current one.
+// ------------------------------------------------------------------------
+template <int NCH>
+__global__ void __launch_bounds__(256)
+mod_gemv_multi_kernel(const bf16_t* __restrict__ temb, const bf16_t* const* __restrict__ ws,
+                      const bf16_t* const* __restrict__ bs, float* __restrict__ mods, int rows_per_mat,
+                      int rows, int cols, int rows_per_wave) {
+  __shared__ __attribute__((aligned(16))) float s_act[NCH * 512];
+  const int nchunk = cols >> 3;
+  for (int i = threadIdx.x; i < cols; i += blockDim.x) s_act[i] = silu(bf2f(temb[i]));
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int r0 = wave * rows_per_wave;
+  if (r0 >= rows) return;
+  const int r1 = min(rows, r0 + rows_per_wave);
+  auto load_row = [&](int r, u32x4 (&v)[NCH]) {
+    const int m = r / rows_per_mat;
+    const bf16_t* w = ws[m] + size_t(r - m * rows_per_mat) * cols;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) v[j] = reinterpret_cast<const u32x4*>(w)[c];
+    }
+  };
+  u32x4 cur[NCH], nxt[NCH];
+  load_row(r0, cur);
+  for (int r = r0; r < r1; ++r) {
+    if (r + 1 < r1) load_row(r + 1, nxt);
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) {
+        float f[8];
+        unpack8(cur[j], f);
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(&s_act[8 * c]);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(&s_act[8 * c + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc += f[e] * a0[e];
+          acc += f[4 + e] * a1[e];
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      const int m = r / rows_per_mat;
+      const bf16_t* b = bs[m];
+      mods[r] = acc + (b ? bf2f(b[r - m * rows_per_mat]) : 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) cur[j] = nxt[j];
+  }
+}
+
+// ------------------------------------------------------------------------
 // Step prediction for a skipped denoising step: y = a + w (a - b) over n
 // bf16 values (a, b the outputs of the last two computed steps), or y = a
 // when b is NULL; written to y1 and, when non-NULL, also to y2.  Flat
@@ -408,6 +469,25 @@ hipError_t launch_modulation(const bf16_t* temb, const bf16_t* w, const bf16_t* 
   switch (nch) {
 #define CASE(N) \
   case N: mod_gemv_kernel<N><<<grid, block, 0, st>>>(temb, w, b, mod, rows, cols, rpw); break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8) CASE(9) CASE(10) CASE(11) CASE(12)
+    CASE(13) CASE(14) CASE(15) CASE(16)
+#undef CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_modulation_multi(const bf16_t* temb, const bf16_t* const* ws, const bf16_t* const* bs,
+                                   float* mods, int n_mats, int rows_per_mat, int cols, hipStream_t st) {
+  const int rows = n_mats * rows_per_mat;
+  if (rows == 0) return hipSuccess;
+  const int nch = (cols / 8 + 63) / 64;
+  const int rpw = rows_per_wave_for(rows, 8192);
+  const int waves = (rows + rpw - 1) / rpw;
+  dim3 grid((waves + 3) / 4), block(256);
+  switch (nch) {
+#define CASE(N) \
+  case N: mod_gemv_multi_kernel<N><<<grid, block, 0, st>>>(temb, ws, bs, mods, rows_per_mat, rows, cols, rpw); break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8) CASE(9) CASE(10) CASE(11) CASE(12)
     CASE(13) CASE(14) CASE(15) CASE(16)
 #undef CASE

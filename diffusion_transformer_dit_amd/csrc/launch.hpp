@@ -15,6 +15,10 @@ void prepare_device();
 
 hipError_t launch_modulation(const bf16_t* temb, const bf16_t* w, const bf16_t* b, float* mod,
                              int rows, int cols, hipStream_t st);
+// n_mats modulation GEMVs in one launch: mods[m * rows_per_mat + r] from
+// ws[m] [rows_per_mat, cols] and bs[m] (DEVICE arrays of pointers; bs[m] may be NULL)
+hipError_t launch_modulation_multi(const bf16_t* temb, const bf16_t* const* ws, const bf16_t* const* bs,
+                                   float* mods, int n_mats, int rows_per_mat, int cols, hipStream_t st);
 hipError_t launch_modulate_norm(const bf16_t* x, const float* shift, const float* scale,
                                 bf16_t* out, int rows, int cols, float eps, hipStream_t st);
 // the same with an fp32 input x [rows, cols]

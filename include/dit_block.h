@@ -237,7 +237,12 @@ int dit_sequential_block_forward(const dit_block_config* cfg, const dit_stream_w
 
 /* ---- block stack replayed over denoising steps --------------------------- */
 
-typedef struct dit_stack dit_stack;  /* opaque: owns the captured graph */
+/* opaque: owns the captured graph, its capture stream and, from the
+ * capture on, two small device buffers: the table of the blocks' W_mod /
+ * b_mod pointers and the blocks' modulation vectors (3d floats per
+ * single-stream block, 6d per stream of a two-stream block), which the
+ * graph computes in one launch per block kind at the start of every step */
+typedef struct dit_stack dit_stack;
 
 int dit_stack_create(dit_stack** out);
 int dit_stack_destroy(dit_stack* st);
@@ -309,6 +314,9 @@ int dit_stack_replay_mixed(dit_stack* st, const dit_block_config* cfg, int64_t t
  * by the stack; a bracket around nothing, once per block, measures the
  * probe's own overhead.  The kernels being timed and their results are
  * unchanged; the graph gains 2 + 2*popcount(mask) tiny nodes per block.
+ * A stack computes every block's modulation in one launch at the start of
+ * the step: kernel 0 of block 0 then reports that whole launch and kernel
+ * 0 of the other blocks ~0 (their mean is the per-block share).
  * kernel_mask bits above 5 -> DIT_ERR_INVALID_ARG. */
 int dit_stack_set_probe(dit_stack* st, uint32_t kernel_mask);
 

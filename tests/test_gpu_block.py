@@ -296,7 +296,13 @@ def test_stack_probes_time_kernels_without_changing_results(gpu_lib):
             pm = st.probe_ms(3)
             assert set(pm) == set(B.Stack.KERNELS)
             for k, v in pm.items():
-                assert len(v) == 3 and all(t > 0 for t in v), (k, v)
+                assert len(v) == 3, (k, v)
+                if k == "modulation":
+                    # one launch computes every block's modulation at the start
+                    # of the step: block 0's bracket holds it, the others are empty
+                    assert v[0] > 0 and all(abs(t) < 0.01 for t in v[1:]), (k, v)
+                else:
+                    assert all(t > 0 for t in v), (k, v)
             with pytest.raises(B.DitError):
                 st.probe_ms(3)  # nothing replayed since the last read
             with pytest.raises(B.DitError):
