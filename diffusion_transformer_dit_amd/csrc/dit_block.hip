@@ -238,13 +238,13 @@ int enqueue_mmdit(const Dims& D, int T, const dit_block_config* cfg, const dit_s
   } ss[2];
   int n = 0;
   if (T > 0) ss[n++] = Stream{wt, 0, T, mod0};
-  if (D.S - T > 0) ss[n++] = Stream{wi, T, D.S - T, mod0 + (mod_pre ? n : 1) * 6 * d};
+  if (D.S - T > 0) ss[n++] = Stream{wi, T, D.S - T, mod0 + n * 6 * d};
   if (n == 0) return DIT_OK;
   const size_t rd = size_t(d);
-  if (!mod_pre)
-    for (int i = 0; i < n; ++i)
-      DIT_CHECK_HIP(dit::launch_modulation(temb, ss[i].w->w_mod, ss[i].w->b_mod, ss[i].mod, 6 * d, D.tdim, st),
-                    "modulation");
+  if (!mod_pre)  // both streams' GEMVs in one launch
+    DIT_CHECK_HIP(dit::launch_modulation_pair(temb, ss[0].w->w_mod, ss[0].w->b_mod, ss[n - 1].w->w_mod,
+                                              ss[n - 1].w->b_mod, n, mod0, 6 * d, D.tdim, st),
+                  "modulation");
   for (int i = 0; i < n; ++i)
     DIT_CHECK_HIP(dit::launch_modulate_norm(x + ss[i].r0 * rd, ss[i].mod, ss[i].mod + d, u + ss[i].r0 * rd,
                                             ss[i].rows, d, cfg->ln_eps, st), "modulate_norm");

@@ -322,10 +322,24 @@ __global__ void rope_table_kernel(const int32_t* __restrict__ pos, RopeAxes ax, 
 // `rows_per_wave` consecutive rows and loads the next row's chunks before it
 // reduces the current one.
 // ------------------------------------------------------------------------
-template <int NCH>
+// Where the matrices come from: a device array of pointers (a stack's
+// blocks) or up to two pointers passed by value (the two streams of a block).
+struct ModTabDev {
+  const bf16_t* const* ws;
+  const bf16_t* const* bs;
+  __device__ __forceinline__ const bf16_t* w(int m) const { return ws[m]; }
+  __device__ __forceinline__ const bf16_t* b(int m) const { return bs[m]; }
+};
+struct ModTab2 {
+  const bf16_t* ws[2];
+  const bf16_t* bs[2];
+  __device__ __forceinline__ const bf16_t* w(int m) const { return m ? ws[1] : ws[0]; }
+  __device__ __forceinline__ const bf16_t* b(int m) const { return m ? bs[1] : bs[0]; }
+};
+
+template <int NCH, class Tab>
 __global__ void __launch_bounds__(256)
-mod_gemv_multi_kernel(const bf16_t* __restrict__ temb, const bf16_t* const* __restrict__ ws,
-                      const bf16_t* const* __restrict__ bs, float* __restrict__ mods, int rows_per_mat,
+mod_gemv_multi_kernel(const bf16_t* __restrict__ temb, Tab tab, float* __restrict__ mods, int rows_per_mat,
                       int rows, int cols, int rows_per_wave) {
   __shared__ __attribute__((aligned(16))) float s_act[NCH * 512];
   const int nchunk = cols >> 3;
@@ -338,7 +352,7 @@ mod_gemv_multi_kernel(const bf16_t* __restrict__ temb, const bf16_t* const* __re
   const int r1 = min(rows, r0 + rows_per_wave);
   auto load_row = [&](int r, u32x4 (&v)[NCH]) {
     const int m = r / rows_per_mat;
-    const bf16_t* w = ws[m] + size_t(r - m * rows_per_mat) * cols;
+    const bf16_t* w = tab.w(m) + size_t(r - m * rows_per_mat) * cols;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = lane + 64 * j;
@@ -368,7 +382,7 @@ mod_gemv_multi_kernel(const bf16_t* __restrict__ temb, const bf16_t* const* __re
     acc = wave_sum(acc);
     if (lane == 0) {
       const int m = r / rows_per_mat;
-      const bf16_t* b = bs[m];
+      const bf16_t* b = tab.b(m);
       mods[r] = acc + (b ? bf2f(b[r - m * rows_per_mat]) : 0.f);
     }
 #pragma unroll
@@ -477,23 +491,41 @@ hipError_t launch_modulation(const bf16_t* temb, const bf16_t* w, const bf16_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_modulation_multi(const bf16_t* temb, const bf16_t* const* ws, const bf16_t* const* bs,
-                                   float* mods, int n_mats, int rows_per_mat, int cols, hipStream_t st) {
+template <class Tab>
+static hipError_t launch_mod_multi(const bf16_t* temb, const Tab& tab, float* mods, int n_mats, int rows_per_mat,
+                                   int cols, int target_waves, hipStream_t st) {
   const int rows = n_mats * rows_per_mat;
   if (rows == 0) return hipSuccess;
   const int nch = (cols / 8 + 63) / 64;
-  const int rpw = rows_per_wave_for(rows, 8192);
+  const int rpw = rows_per_wave_for(rows, target_waves);
   const int waves = (rows + rpw - 1) / rpw;
   dim3 grid((waves + 3) / 4), block(256);
   switch (nch) {
 #define CASE(N) \
-  case N: mod_gemv_multi_kernel<N><<<grid, block, 0, st>>>(temb, ws, bs, mods, rows_per_mat, rows, cols, rpw); break;
+  case N: mod_gemv_multi_kernel<N, Tab><<<grid, block, 0, st>>>(temb, tab, mods, rows_per_mat, rows, cols, rpw); break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8) CASE(9) CASE(10) CASE(11) CASE(12)
     CASE(13) CASE(14) CASE(15) CASE(16)
 #undef CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_modulation_multi(const bf16_t* temb, const bf16_t* const* ws, const bf16_t* const* bs,
+                                   float* mods, int n_mats, int rows_per_mat, int cols, hipStream_t st) {
+  return launch_mod_multi(temb, ModTabDev{ws, bs}, mods, n_mats, rows_per_mat, cols, 8192, st);
+}
+
+hipError_t launch_modulation_pair(const bf16_t* temb, const bf16_t* w0, const bf16_t* b0, const bf16_t* w1,
+                                  const bf16_t* b1, int n_mats, float* mods, int rows_per_mat, int cols,
+                                  hipStream_t st) {
+  if (n_mats < 0 || n_mats > 2) return hipErrorInvalidValue;
+  ModTab2 tab;
+  tab.ws[0] = w0;
+  tab.ws[1] = w1;
+  tab.bs[0] = b0;
+  tab.bs[1] = b1;
+  return launch_mod_multi(temb, tab, mods, n_mats, rows_per_mat, cols, 4096, st);
 }
 
 hipError_t launch_qk_rmsnorm_rope(bf16_t* qkv, const float* qw, const float* kw, const float* rcos,

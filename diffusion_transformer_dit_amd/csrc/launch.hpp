@@ -19,6 +19,10 @@ hipError_t launch_modulation(const bf16_t* temb, const bf16_t* w, const bf16_t* 
 // ws[m] [rows_per_mat, cols] and bs[m] (DEVICE arrays of pointers; bs[m] may be NULL)
 hipError_t launch_modulation_multi(const bf16_t* temb, const bf16_t* const* ws, const bf16_t* const* bs,
                                    float* mods, int n_mats, int rows_per_mat, int cols, hipStream_t st);
+// the same for n_mats <= 2 matrices passed by value (the streams of one block)
+hipError_t launch_modulation_pair(const bf16_t* temb, const bf16_t* w0, const bf16_t* b0, const bf16_t* w1,
+                                  const bf16_t* b1, int n_mats, float* mods, int rows_per_mat, int cols,
+                                  hipStream_t st);
 hipError_t launch_modulate_norm(const bf16_t* x, const float* shift, const float* scale,
                                 bf16_t* out, int rows, int cols, float eps, hipStream_t st);
 // the same with an fp32 input x [rows, cols]
