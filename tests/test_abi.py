@@ -95,6 +95,15 @@ def test_misaligned_tensor_pointers_are_rejected(lib):
         == B.DIT_ERR_INVALID_ARG
 
 
+def test_sizes_beyond_32bit_ranges_are_unsupported(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    P = ctypes.c_void_p(0x1000)
+    # 60000 tokens x 3 x 6144 dims > 2^30 q|k|v elements
+    assert lib.dit_attention(P, P, 60000, 48, 128, 6144, None) == B.DIT_ERR_UNSUPPORTED
+    assert B.block_workspace_bytes(B.make_config(60000, 6144, 48, 128, 12288)) == 0
+    assert B.block_workspace_bytes(B.make_config(50000, 6144, 48, 128, 12288)) > 0
+
+
 def test_chunked_attention_argument_checks(lib):
     from diffusion_transformer_dit_amd import binding as B
     P, Q = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)
