@@ -19,8 +19,12 @@
  *     the HIP or PyTorch allocators is); others give DIT_ERR_INVALID_ARG.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on `stream` and returns; none
- *     synchronises the host, and none allocates device memory.  The caller
- *     owns every buffer, the workspace and the stream.
+ *     synchronises the host, and none allocates device memory, with two
+ *     exceptions: the first replay of a stack (its capture) allocates the
+ *     stack's own small buffers and copies a table of weight pointers to
+ *     the device synchronously, and dit_stack_probe_ms synchronises the
+ *     device.  The caller owns every other buffer, the workspace and the
+ *     stream.
  *   - Every call returns DIT_OK (0) or an error code.  Arguments are checked
  *     before any HIP call; on error nothing is enqueued and dit_last_error()
  *     returns a message (thread-local).  HIP launch failures give DIT_ERR_HIP.
