@@ -226,7 +226,14 @@ def chunked_attention_times(B, g, dev, reps=3):
     qkv3 = (torch.randn(S, 3 * hq * DH, generator=g, device=dev, dtype=torch.float32)).to(torch.bfloat16)
     out3 = torch.empty(S, hq * DH, dtype=torch.bfloat16, device=dev)
     res["ulysses_share_3heads_ms"] = time_graph(lambda i: B.attention(qkv3, out3, hq, DH), 8, reps)
-    del o_parts, lses, qkv, qkv3
+    # the same share with the keys split over more workgroups (one launch of
+    # chunk partials + the merge): 108 workgroups x n chunks
+    op3 = torch.empty(8, S, hq * DH, dtype=torch.float32, device=dev)
+    ls3 = torch.empty(8, hq, S, dtype=torch.float32, device=dev)
+    res["ulysses_share_3heads_split_ms"] = {
+        n: time_graph(lambda i, n=n: B.attention_split(qkv3, out3, hq, DH, n, o_parts=op3, lses=ls3), 8, reps)
+        for n in (2, 4, 6, 8)}
+    del o_parts, lses, qkv, qkv3, op3, ls3
     torch.cuda.synchronize()
     return res
 
@@ -502,10 +509,13 @@ def main():
         "merge_gbs": round(gbs(merge_bytes, ca["merge_ms"]), 1),
         "single_pass_us": round(ca["single_pass_ms"] * 1e3, 1),
         "ulysses_share_3_heads_us": round(ca["ulysses_share_3heads_ms"] * 1e3, 1),
+        "ulysses_share_3_heads_split_us": {f"{n}_chunks": round(v * 1e3, 1)
+                                           for n, v in ca["ulysses_share_3heads_split_ms"].items()},
         "note": "outside the graph of the stack; partials write fp32 outputs that the merge reads back",
     }
     log(f"chunked attention: 8 partials {ca['partials_ms'] * 1e3:.1f} us + merge {ca['merge_ms'] * 1e3:.1f} us, "
-        f"single pass {ca['single_pass_ms'] * 1e3:.1f} us, 3-head share {ca['ulysses_share_3heads_ms'] * 1e3:.1f} us")
+        f"single pass {ca['single_pass_ms'] * 1e3:.1f} us, 3-head share {ca['ulysses_share_3heads_ms'] * 1e3:.1f} us, "
+        "split " + ", ".join(f"{n}: {v * 1e3:.1f} us" for n, v in ca["ulysses_share_3heads_split_ms"].items()))
     # ---- step-level skip (MeanCache-style control): 50 denoising steps with
     # steps 0, 1 and every even step after computed (26 forwards), the others
     # predicted from the last two computed outputs, against all 50 computed

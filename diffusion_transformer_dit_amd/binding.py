@@ -69,6 +69,7 @@ SIGNATURES = {
     "dit_stack_replay": ([VP, VP, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
     "dit_attention_partial": ([VP, I64, I64, I64, I64, I64, VP, VP, VP], ctypes.c_int),
     "dit_attention_merge": ([VP, VP, I64, I64, I64, I64, VP, I64, VP], ctypes.c_int),
+    "dit_attention_split": ([VP, VP, I64, I64, I64, I64, I64, VP, VP, VP], ctypes.c_int),
     "dit_stack_replay_cached": ([VP, VP, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP, VP, VP, SZ, VP, VP, VP],
                                 ctypes.c_int),
     "dit_stack_mixed_workspace_bytes": ([VP], SZ),
@@ -238,6 +239,28 @@ def attention_merge(o_parts, lses, out, num_heads, head_dim, stream=None):
         raise ValueError("shape mismatch")
     _check(_lib.dit_attention_merge(_p(o_parts), _p(lses), C, S, num_heads, head_dim, _p(out), out.shape[1],
                                     _stream(stream)))
+    return out
+
+
+def attention_split(qkv, out, num_heads, head_dim, n_chunks, o_parts=None, lses=None, stream=None):
+    """Attention over all keys, split into up to n_chunks key chunks (one
+    launch of partials + the merge); out columns [0, H*Dh)."""
+    _need(qkv, BF16, "qkv", 2)
+    _need(out, BF16, "out", 2)
+    S = qkv.shape[0]
+    d = num_heads * head_dim
+    if qkv.shape[1] != 3 * d or out.shape[0] != S or out.shape[1] < d:
+        raise ValueError("qkv must be [S, 3*H*Dh], out [S, >= H*Dh]")
+    if o_parts is None:
+        o_parts = torch.empty(n_chunks, S, d, dtype=F32T, device=qkv.device)
+    if lses is None:
+        lses = torch.empty(n_chunks, num_heads, S, dtype=F32T, device=qkv.device)
+    _need(o_parts, F32T, "o_parts", 3)
+    _need(lses, F32T, "lses", 3)
+    if o_parts.shape[0] < n_chunks or lses.shape[0] < n_chunks:
+        raise ValueError("scratch too small for n_chunks")
+    _check(_lib.dit_attention_split(_p(qkv), _p(out), S, num_heads, head_dim, out.stride(0), n_chunks, _p(o_parts),
+                                    _p(lses), _stream(stream)))
     return out
 
 

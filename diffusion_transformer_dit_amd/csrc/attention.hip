@@ -91,12 +91,23 @@ __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 // normalised output in fp32 to out_f32 [S, H*DH] and its log-sum-exp (natural
 // log) to lse [H, S], the per-hop step of ring attention; otherwise write
 // bf16 to out (row stride ld_out) over all keys.
+// With PARTIAL, blockIdx.z selects one of gridDim.z consecutive key chunks
+// of kv_chunk tokens inside [kv_begin, kv_end) and its output slices
+// (out_f32 + z*S*H*DH, lse + z*H*S): a split of the keys over more
+// workgroups when S/128 x H workgroups cannot fill the chip.
 template <int DH, bool PARTIAL>
 __global__ void __launch_bounds__(256, 2)
 attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ out_f32,
                      float* __restrict__ lse, int S, int H, int ld_out, float c_log2, int kv_begin,
-                     int kv_end) {
+                     int kv_end, int kv_chunk) {
   using C = AttCfg<DH>;
+  if constexpr (PARTIAL) {
+    const int z = blockIdx.z;
+    kv_begin += z * kv_chunk;
+    kv_end = min(kv_end, kv_begin + kv_chunk);
+    out_f32 += size_t(z) * S * H * DH;
+    lse += size_t(z) * H * S;
+  }
   constexpr int KCH = C::KCH;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
   const int tid = threadIdx.x;
@@ -325,9 +336,28 @@ hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH
   dim3 grid((S + ATT_BM - 1) / ATT_BM, H), block(256);
   const float c = kLog2e / sqrtf(float(DH));
   if (DH == 128)
-    attention_fwd_kernel<128, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S);
+    attention_fwd_kernel<128, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S, S);
   else if (DH == 64)
-    attention_fwd_kernel<64, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S);
+    attention_fwd_kernel<64, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S, S);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// n_chunks key chunks of ceil((kv_end - kv_begin) / n_chunks) tokens in one
+// launch (every chunk non-empty: callers pass n_chunks from attention_chunks)
+static hipError_t launch_partials(const bf16_t* qkv, int S, int H, int DH, int kv_begin, int kv_end, int n_chunks,
+                                  float* o_part, float* lse, hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  const int chunk = (kv_end - kv_begin + n_chunks - 1) / n_chunks;
+  dim3 grid((S + ATT_BM - 1) / ATT_BM, H, n_chunks), block(256);
+  const float c = kLog2e / sqrtf(float(DH));
+  if (DH == 128)
+    attention_fwd_kernel<128, true><<<grid, block, 0, st>>>(qkv, nullptr, o_part, lse, S, H, 0, c, kv_begin, kv_end,
+                                                            chunk);
+  else if (DH == 64)
+    attention_fwd_kernel<64, true><<<grid, block, 0, st>>>(qkv, nullptr, o_part, lse, S, H, 0, c, kv_begin, kv_end,
+                                                           chunk);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -335,16 +365,22 @@ hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH
 
 hipError_t launch_attention_partial(const bf16_t* qkv, int S, int H, int DH, int kv_begin, int kv_end,
                                     float* o_part, float* lse, hipStream_t st) {
+  return launch_partials(qkv, S, H, DH, kv_begin, kv_end, 1, o_part, lse, st);
+}
+
+int attention_chunks(int S, int n_chunks) {
+  if (S <= 0 || n_chunks <= 1) return 1;
+  const int chunk = (S + n_chunks - 1) / n_chunks;
+  return (S + chunk - 1) / chunk;
+}
+
+hipError_t launch_attention_split(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out, int n_chunks,
+                                  float* o_parts, float* lses, hipStream_t st) {
   if (S == 0) return hipSuccess;
-  dim3 grid((S + ATT_BM - 1) / ATT_BM, H), block(256);
-  const float c = kLog2e / sqrtf(float(DH));
-  if (DH == 128)
-    attention_fwd_kernel<128, true><<<grid, block, 0, st>>>(qkv, nullptr, o_part, lse, S, H, 0, c, kv_begin, kv_end);
-  else if (DH == 64)
-    attention_fwd_kernel<64, true><<<grid, block, 0, st>>>(qkv, nullptr, o_part, lse, S, H, 0, c, kv_begin, kv_end);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  const int n = attention_chunks(S, n_chunks);
+  hipError_t e = launch_partials(qkv, S, H, DH, 0, S, n, o_parts, lses, st);
+  if (e != hipSuccess) return e;
+  return launch_attention_merge(o_parts, lses, n, S, H, DH, out, ld_out, st);
 }
 
 hipError_t launch_attention_merge(const float* o_parts, const float* lses, int n_chunks, int S, int H, int DH,

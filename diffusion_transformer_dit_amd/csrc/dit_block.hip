@@ -411,6 +411,23 @@ extern "C" int dit_attention_partial(const dit_bf16* qkv, int64_t seq_len, int64
   return DIT_OK;
 }
 
+extern "C" int dit_attention_split(const dit_bf16* qkv, dit_bf16* out, int64_t seq_len, int64_t num_heads,
+                                   int64_t head_dim, int64_t ld_out, int64_t n_chunks, float* o_parts, float* lses,
+                                   void* stream) {
+  int rc = check_dims(seq_len, num_heads * head_dim, num_heads, head_dim, 64, 8);
+  if (rc) return rc;
+  if (n_chunks < 1 || n_chunks > 64) return fail(DIT_ERR_INVALID_ARG, "n_chunks=%lld must be in [1, 64]", (long long)n_chunks);
+  if (seq_len == 0) return DIT_OK;
+  if (!qkv || !out || !o_parts || !lses) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({qkv, out, o_parts}))) return rc;
+  if (reinterpret_cast<uintptr_t>(lses) % 4 != 0) return fail(DIT_ERR_INVALID_ARG, "lses must be 4-byte aligned");
+  if (ld_out < num_heads * head_dim || ld_out % 4 != 0 || ld_out > kMaxInt)
+    return fail(DIT_ERR_INVALID_ARG, "ld_out=%lld must be >= H*Dh and a multiple of 4", (long long)ld_out);
+  DIT_CHECK_HIP(dit::launch_attention_split(qkv, out, int(seq_len), int(num_heads), int(head_dim), int(ld_out),
+                                            int(n_chunks), o_parts, lses, as_stream(stream)), "attention_split");
+  return DIT_OK;
+}
+
 extern "C" int dit_attention_merge(const float* o_parts, const float* lses, int64_t n_chunks, int64_t seq_len,
                                    int64_t num_heads, int64_t head_dim, dit_bf16* out, int64_t ld_out,
                                    void* stream) {

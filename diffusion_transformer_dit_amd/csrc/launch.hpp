@@ -96,6 +96,12 @@ hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH
 // attention over keys [kv_begin, kv_end): o_part [S, H*DH] fp32, lse [H, S] fp32
 hipError_t launch_attention_partial(const bf16_t* qkv, int S, int H, int DH, int kv_begin, int kv_end,
                                     float* o_part, float* lse, hipStream_t st);
+// number of non-empty key chunks when S keys are cut into n_chunks equal chunks
+int attention_chunks(int S, int n_chunks);
+// attention over all S keys as attention_chunks(S, n_chunks) partials in one
+// launch (scratch o_parts [n, S, H*DH], lses [n, H, S]) plus the merge
+hipError_t launch_attention_split(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out, int n_chunks,
+                                  float* o_parts, float* lses, hipStream_t st);
 // out[t, :H*DH] (row stride ld_out) = lse-weighted sum of n_chunks partials
 hipError_t launch_attention_merge(const float* o_parts, const float* lses, int n_chunks, int S, int H, int DH,
                                   bf16_t* out, int ld_out, hipStream_t st);

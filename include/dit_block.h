@@ -153,6 +153,19 @@ int dit_attention_partial(const dit_bf16* qkv, int64_t seq_len, int64_t num_head
 int dit_attention_merge(const float* o_parts, const float* lses, int64_t n_chunks, int64_t seq_len,
                         int64_t num_heads, int64_t head_dim, dit_bf16* out, int64_t ld_out, void* stream);
 
+/* Attention over all seq_len keys with the keys split into up to n_chunks
+ * equal chunks (n_chunks in [1, 64]; chunks are ceil(S / n_chunks) tokens,
+ * so fewer may result, never an empty one): the partials of all chunks in
+ * one launch, then dit_attention_merge's weighting into out (bf16, row stride
+ * ld_out).  For head counts too small to fill the chip with one workgroup
+ * per 128 queries and head (e.g. one GPU's heads after an all-to-all from
+ * sequence to head sharding, the Flux page, section 5): the chunks give
+ * n_chunks times as many workgroups.  o_parts [n_chunks, S, H*Dh] fp32 and
+ * lses [n_chunks, H, S] fp32 are caller-owned scratch. */
+int dit_attention_split(const dit_bf16* qkv, dit_bf16* out, int64_t seq_len, int64_t num_heads,
+                        int64_t head_dim, int64_t ld_out, int64_t n_chunks, float* o_parts, float* lses,
+                        void* stream);
+
 /* linear2 with fused gated residual: y = x + gate * (cat . W2^T + b2).
  * cat [S, d+mlp]; w2 [d, d+mlp]; b2 [d] or NULL; x, y [S, d] (y may equal x);
  * gate [d] fp32. */

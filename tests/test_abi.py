@@ -104,6 +104,19 @@ def test_sizes_beyond_32bit_ranges_are_unsupported(lib):
     assert B.block_workspace_bytes(B.make_config(50000, 6144, 48, 128, 12288)) > 0
 
 
+def test_split_attention_argument_checks(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    P = ctypes.c_void_p(0x1000)
+    split = lambda S, n, ld=128, lses=P: lib.dit_attention_split(P, P, S, 1, 128, ld, n, P, lses, None)
+    assert split(64, 0) == B.DIT_ERR_INVALID_ARG
+    assert split(64, 65) == B.DIT_ERR_INVALID_ARG
+    assert split(64, 4, ld=64) == B.DIT_ERR_INVALID_ARG          # ld_out < H*Dh
+    assert split(64, 4, lses=ctypes.c_void_p(0x1002)) == B.DIT_ERR_INVALID_ARG
+    assert split(64, 4, lses=None) == B.DIT_ERR_INVALID_ARG
+    assert split(0, 4) == B.DIT_OK                              # empty: a no-op
+    assert lib.dit_attention_split(P, P, 64, 1, 96, 128, 4, P, P, None) == B.DIT_ERR_UNSUPPORTED
+
+
 def test_chunked_attention_argument_checks(lib):
     from diffusion_transformer_dit_amd import binding as B
     P, Q = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)

@@ -225,6 +225,41 @@ def test_attention_chunked_flux_eight_chunks(gpu_lib):
     assert st["excess"] <= 2 * 2e-2 * st["rms"], st
 
 
+SPLIT_CASES = [(300, 2, 128, 3), (129, 2, 64, 2), (5, 1, 128, 8), (4608, 3, 128, 4), (256, 4, 64, 1)]
+
+
+@pytest.mark.parametrize("S,H,Dh,n", SPLIT_CASES, ids=[f"S{c[0]}-H{c[1]}-D{c[2]}-n{c[3]}" for c in SPLIT_CASES])
+def test_attention_split(gpu_lib, S, H, Dh, n):
+    """Split-key attention (one launch of chunk partials + the merge) against
+    the oracle; the 3-head Flux-length case is one GPU's share of the heads
+    under an 8-way head split."""
+    import torch
+    B = gpu_lib
+    d = H * Dh
+    print(f"attention split S={S} H={H} Dh={Dh} n={n}", flush=True)
+    qkv = _qkv_for_attention(S, H, Dh, 36)
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    out = torch.zeros(S, d + 64, dtype=torch.bfloat16, device="cuda")
+    B.attention_split(dev_bf16(qkv), out, H, Dh, n)
+    torch.cuda.synchronize()
+    rows = np.arange(S) if S <= 512 else np.unique(np.concatenate([np.arange(0, S, 97), [S - 1]]))
+    ref = O.attention(q, k, v, H, Dh, q_rows=rows)
+    g = host(out)
+    assert_parity(g[rows, :d], ref, f"split attention S={S} H={H} n={n}")
+    assert np.all(g[:, d:] == 0)
+
+
+def test_attention_split_rejects_bad_chunk_counts(gpu_lib):
+    import torch
+    B = gpu_lib
+    qkv = torch.zeros(64, 3 * 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros(64, 128, dtype=torch.bfloat16, device="cuda")
+    for n in (0, 65):
+        with pytest.raises(B.DitError):
+            B.attention_split(qkv, out, 1, 128, n, o_parts=torch.empty(max(n, 1), 64, 128, device="cuda"),
+                              lses=torch.empty(max(n, 1), 1, 64, device="cuda"))
+
+
 def test_attention_partial_rejects_bad_ranges(gpu_lib):
     import torch
     B = gpu_lib
