@@ -107,8 +107,9 @@ int check_weights(const dit_block_weights* w) {
   return check_aligned({w->w_mod, w->b_mod, w->w1, w->b1, w->w2, w->b2, w->q_norm_w, w->k_norm_w});
 }
 
+// Workspace of one single-stream block forward.
 struct WsLayout {
-  size_t mod, u, qkv, cat, block_end, xbuf, tbuf, stack_end;
+  size_t mod, u, qkv, cat, block_end;
 };
 
 WsLayout layout(const Dims& D) {
@@ -119,9 +120,6 @@ WsLayout layout(const Dims& D) {
   L.qkv = o; o = align256(o + size_t(D.S) * 3 * D.d * 2);
   L.cat = o; o = align256(o + size_t(D.S) * (D.d + D.mlp) * 2);
   L.block_end = o;
-  L.xbuf = o; o = align256(o + size_t(D.S) * D.d * 2);
-  L.tbuf = o; o = align256(o + size_t(D.tdim) * 2);
-  L.stack_end = o;
   return L;
 }
 

@@ -1,7 +1,10 @@
-// bf16 GEMMs of the single-stream block on gfx950 matrix cores, with the
+// bf16 GEMMs of the DiT blocks on gfx950 matrix cores, with the
 // elementwise tails fused into the epilogue:
 //   linear1:  z = u W1^T + b1; q|k|v columns -> qkv, mlp columns -> GELU -> cat
+//             (optionally with the per-head q/k RMSNorm + RoPE)
 //   linear2:  y = x + gate * (cat W2^T + b2)
+// and the same epilogues for the two-stream block's linears, where one
+// launch carries the text and the image stream's problems.
 // Both operands are K-contiguous ([rows, K] row-major, the nn.Linear layout
 // for the weight), C = A B^T.  The Flux page (ChituDiffusion, sections 2 and
 // 3.2) finds these GEMMs dominating the block's timeline before and after
