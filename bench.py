@@ -47,10 +47,16 @@ def log(msg):
 
 
 def kernel_source_hash():
+    """Hash of the GEMM sources with comments and blank lines removed: the
+    stored traffic counters stay valid across comment-only edits and are
+    dropped on any change of the code."""
+    import re
     h = hashlib.sha256()
     for name in ("gemm.hip", "dit_common.hpp"):
-        with open(os.path.join(ROOT, "diffusion_transformer_dit_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "diffusion_transformer_dit_amd", "csrc", name)) as f:
+            src = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        lines = [ln.split("//", 1)[0].rstrip() for ln in src.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 
