@@ -99,7 +99,7 @@ template <int DH, bool PARTIAL>
 __global__ void __launch_bounds__(256, 2)
 attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ out_f32,
                      float* __restrict__ lse, int S, int H, int ld_out, float c_log2, int kv_begin,
-                     int kv_end, int kv_chunk) {
+                     int kv_end, int kv_chunk, int xcd_remap) {
   using C = AttCfg<DH>;
   if constexpr (PARTIAL) {
     const int z = blockIdx.z;
@@ -113,14 +113,24 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS targets stay scalar
-  const int head = blockIdx.y;
+  // (query block, head) from the linear block id; with xcd_remap the ids are
+  // remapped so that the workgroups one XCD runs at a time (blocks are dealt
+  // round-robin to the 8 XCDs) are consecutive query blocks of the same few
+  // heads, whose K and V then stay in that XCD's 4 MB L2 (the launchers set
+  // it when one head's K and V fit in 4 MB: +2-3 % at the Flux shape, -1.5 %
+  // at S = 16384 where they do not).
+  int bid = blockIdx.x + blockIdx.y * gridDim.x;
+  const int nb = gridDim.x * gridDim.y;
+  if (xcd_remap && (nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int qblock = bid % gridDim.x;
+  const int head = bid / gridDim.x;
   const int d = H * DH;
   const int ld = 3 * d;
   const bf16_t* Qg = qkv + head * DH;
 
   const int ql = lane & 31;  // query column of this lane
   const int hh = lane >> 5;  // lane half
-  const int q = blockIdx.x * ATT_BM + wave * 32 + ql;
+  const int q = qblock * ATT_BM + wave * 32 + ql;
   const int qc = min(q, S - 1);
 
   // Q^T operand: 8 dims (16*s + 8*hh ..) of this lane's query for each K-step s.
@@ -330,15 +340,21 @@ attention_merge_kernel(const float* __restrict__ o_parts, const float* __restric
   *reinterpret_cast<u32x2*>(out + size_t(t) * ld_out + c4) = wv;
 }
 
+// one head's K and V fit in an XCD's 4 MB L2
+static int att_remap(int S, int DH) { return (long long)S * DH * 2 * 2 <= (4ll << 20) ? 1 : 0; }
+
 hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
                             hipStream_t st) {
   if (S == 0) return hipSuccess;
   dim3 grid((S + ATT_BM - 1) / ATT_BM, H), block(256);
   const float c = kLog2e / sqrtf(float(DH));
+  const int rm = att_remap(S, DH);
   if (DH == 128)
-    attention_fwd_kernel<128, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S, S);
+    attention_fwd_kernel<128, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S, S,
+                                                             rm);
   else if (DH == 64)
-    attention_fwd_kernel<64, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S, S);
+    attention_fwd_kernel<64, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S, S,
+                                                            rm);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -352,12 +368,13 @@ static hipError_t launch_partials(const bf16_t* qkv, int S, int H, int DH, int k
   const int chunk = (kv_end - kv_begin + n_chunks - 1) / n_chunks;
   dim3 grid((S + ATT_BM - 1) / ATT_BM, H, n_chunks), block(256);
   const float c = kLog2e / sqrtf(float(DH));
+  const int rm = att_remap(chunk, DH);
   if (DH == 128)
     attention_fwd_kernel<128, true><<<grid, block, 0, st>>>(qkv, nullptr, o_part, lse, S, H, 0, c, kv_begin, kv_end,
-                                                            chunk);
+                                                            chunk, rm);
   else if (DH == 64)
     attention_fwd_kernel<64, true><<<grid, block, 0, st>>>(qkv, nullptr, o_part, lse, S, H, 0, c, kv_begin, kv_end,
-                                                           chunk);
+                                                           chunk, rm);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
