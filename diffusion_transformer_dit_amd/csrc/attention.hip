@@ -4,9 +4,10 @@
 // video page (mhpq.cn, section 5.1) recommends, as one LDS-tiled online-
 // softmax kernel.
 //
-// One workgroup = 4 wavefronts = 128 queries of one head; each wave owns 32
-// queries.  K and V stream through LDS in tiles of 64 tokens, double
-// buffered, filled by direct buffer->LDS loads (buffer_load_dwordx4 ... lds,
+// One workgroup = 8 wavefronts = 256 queries of one head, one workgroup per
+// CU (4 wavefronts = 128 queries, two per CU, when the 8-wave grid would
+// leave CUs idle); each wave owns 32 queries.  K and V stream through LDS in
+// tiles of 64 tokens, double buffered, filled by direct buffer->LDS loads (buffer_load_dwordx4 ... lds,
 // no VALU address work per load) issued one tile ahead.  Both tiles keep the
 // token-major layout of qkv (rows of Dh bf16) with 16-byte chunks
 // XOR-swizzled by row.  Per tile and wave, in two halves of 32 keys:
@@ -16,7 +17,9 @@
 //   online softmax in fp32 with exp2 and the 1/sqrt(Dh)*log2(e) scale folded
 //                 into one FMA, against a running max that is only
 //                 recomputed when the probabilities grow past 2^8; P is
-//                 packed to bf16 (v_cvt_pk_bf16_f32);
+//                 packed to bf16 (v_cvt_pk_bf16_f32) and the denominator
+//                 sums the packed values, so the output is a convex
+//                 combination of V rows with exactly the weights applied;
 //   O^T += V^T P^T, where the P^T operand comes straight from the S^T
 //                 accumulator registers and the V^T operand is read from the
 //                 token-major V tile with ds_read_b64_tr_b16 (a transposing
@@ -29,8 +32,7 @@
 
 namespace dit {
 
-constexpr int ATT_BM = 128;  // queries per workgroup
-constexpr int ATT_BN = 64;   // keys per tile
+constexpr int ATT_BN = 64;  // keys per tile
 
 template <int DH>
 struct AttCfg {
@@ -38,7 +40,6 @@ struct AttCfg {
   static constexpr int TILE = ATT_BN * ROW;         // one K or V tile
   static constexpr int STAGE = 2 * TILE;            // K tile then V tile
   static constexpr int KCH = DH / 8;                // 16-byte chunks per row
-  static constexpr int LPW = ATT_BN * KCH / 64 / 4;  // 1 KB wave-loads per wave per tile
   static_assert(KCH == 8 || KCH == 16, "head_dim 64 or 128");
 };
 
@@ -81,6 +82,24 @@ __device__ __forceinline__ float sum16(const float* e) {
   for (int i = 0; i < 4; ++i) s4[i] = s8[2 * i] + s8[2 * i + 1];
   return (s4[0] + s4[1]) + (s4[2] + s4[3]);
 }
+// P in bf16 for the PV product: packs the 16 probabilities of a lane
+// (p[0] = keys of the first 16-key step, p[1] of the second) and returns the
+// sum of the ROUNDED values, so that the denominator is the sum of the exact
+// weights the matrix cores multiply V by.  The sum is taken on the packed
+// pairs by v_dot2c_f32_bf16 against (1, 1): one instruction per pair.
+__device__ __forceinline__ float pack_p(const float* e, u32x4* p) {
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  float s[2] = {0.f, 0.f};
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t w = pack_bf2(e[8 * half + 2 * t], e[8 * half + 2 * t + 1]);
+      p[half][t] = w;
+      s[t & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, s[t & 1], false);
+    }
+  return s[0] + s[1];
+}
 __device__ __forceinline__ float xor32_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -95,12 +114,15 @@ __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 // of kv_chunk tokens inside [kv_begin, kv_end) and its output slices
 // (out_f32 + z*S*H*DH, lse + z*H*S): a split of the keys over more
 // workgroups when S/128 x H workgroups cannot fill the chip.
-template <int DH, bool PARTIAL>
-__global__ void __launch_bounds__(256, 2)
+// NW waves per workgroup (32 NW queries): 8 (one workgroup per CU) or 4 (two).
+template <int DH, bool PARTIAL, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
 attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ out_f32,
                      float* __restrict__ lse, int S, int H, int ld_out, float c_log2, int kv_begin,
                      int kv_end, int kv_chunk, int xcd_remap) {
   using C = AttCfg<DH>;
+  constexpr int BM = 32 * NW;                      // queries per workgroup
+  constexpr int LPW = ATT_BN * C::KCH / 64 / NW;  // 1 KB wave-loads per wave per tile
   if constexpr (PARTIAL) {
     const int z = blockIdx.z;
     kv_begin += z * kv_chunk;
@@ -130,7 +152,7 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
 
   const int ql = lane & 31;  // query column of this lane
   const int hh = lane >> 5;  // lane half
-  const int q = qblock * ATT_BM + wave * 32 + ql;
+  const int q = qblock * BM + wave * 32 + ql;
   const int qc = min(q, S - 1);
 
   // Q^T operand: 8 dims (16*s + 8*hh ..) of this lane's query for each K-step s.
@@ -145,10 +167,10 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
   // tile).  Each tile gets a descriptor whose range ends with the key range,
   // so the rows of a ragged last tile past it read as zero: their scores are
   // masked to -inf and their V rows meet zero probabilities.
-  int koff[C::LPW], voff[C::LPW];
+  int koff[LPW], voff[LPW];
 #pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    const int p = (wave * C::LPW + i) * 64 + lane;
+  for (int i = 0; i < LPW; ++i) {
+    const int p = (wave * LPW + i) * 64 + lane;
     const int row = p / KCH, cp = p % KCH;
     koff[i] = (row * ld + d + head * DH + 8 * (cp ^ k_swz<KCH>(row))) * 2;
     voff[i] = (row * ld + 2 * d + head * DH + 8 * (cp ^ v_swz<KCH>(row))) * 2;
@@ -158,8 +180,8 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
     unsigned char* sV = sK + C::TILE;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(qkv + size_t(t0) * ld, uint32_t(kv_end - t0) * uint32_t(ld) * 2u);
 #pragma unroll
-    for (int i = 0; i < C::LPW; ++i) {
-      const int w = wave * C::LPW + i;
+    for (int i = 0; i < LPW; ++i) {
+      const int w = wave * LPW + i;
       buffer_load_lds_16(r, sK + w * 1024, koff[i]);
       buffer_load_lds_16(r, sV + w * 1024, voff[i]);
     }
@@ -226,7 +248,8 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
       float mc = m_run * c_log2;
 #pragma unroll
       for (int i = 0; i < 16; ++i) e[i] = exp2_fast(fmaf(sacc[i], c_log2, -mc));
-      float hs = sum16(e);
+      u32x4 pk[2];
+      float hs = pack_p(e, pk);
       if (__builtin_amdgcn_ballot_w64(!(hs <= 256.0f))) {
         float mx = sacc[0];
 #pragma unroll
@@ -243,17 +266,10 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
         mc = m_run * c_log2;
 #pragma unroll
         for (int i = 0; i < 16; ++i) e[i] = exp2_fast(fmaf(sacc[i], c_log2, -mc));
-        hs = sum16(e);
+        hs = pack_p(e, pk);
       }
       l_run += hs;
-      bf16x8 pf[2];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 pk;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) pk[t] = pack_bf2(e[8 * half + 2 * t], e[8 * half + 2 * t + 1]);
-        pf[half] = __builtin_bit_cast(bf16x8, pk);
-      }
+      const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, pk[0]), __builtin_bit_cast(bf16x8, pk[1])};
       // O^T += V^T P^T over the two 16-key steps of this half; step m covers
       // keys 16m + 4hh + (0..3) and 16m + 8 + 4hh + (0..3) of the tile.
 #pragma unroll
@@ -343,21 +359,39 @@ attention_merge_kernel(const float* __restrict__ o_parts, const float* __restric
 // one head's K and V fit in an XCD's 4 MB L2
 static int att_remap(int S, int DH) { return (long long)S * DH * 2 * 2 <= (4ll << 20) ? 1 : 0; }
 
+// One launch of n_chunks key chunks (1 for a plain attention) of `chunk`
+// keys inside [kv_begin, kv_end).  Eight-wave workgroups (one per CU) load
+// each K/V tile once for 256 queries instead of 128, which halves the tile
+// loads a wave issues; they are used when their grid still gives every CU a
+// workgroup, else the 4-wave kernel keeps twice as many workgroups in flight
+// (a few heads, short sequences).
+template <bool PARTIAL>
+static hipError_t launch_fwd(const bf16_t* qkv, bf16_t* out, float* o_part, float* lse, int S, int H, int DH,
+                             int ld_out, int kv_begin, int kv_end, int chunk, int n_chunks, hipStream_t st) {
+  if (DH != 128 && DH != 64) return hipErrorInvalidValue;
+  const float c = kLog2e / sqrtf(float(DH));
+  const int rm = att_remap(chunk, DH);
+  const bool wide = (long long)((S + 255) / 256) * H * n_chunks >= num_cus();
+  const int nw = wide ? 8 : 4;
+  dim3 grid((S + 32 * nw - 1) / (32 * nw), H, n_chunks), block(64 * nw);
+#define DIT_ATT_LAUNCH(D, W)                                                                                    \
+  attention_fwd_kernel<D, PARTIAL, W><<<grid, block, 0, st>>>(qkv, out, o_part, lse, S, H, ld_out, c, kv_begin, \
+                                                              kv_end, chunk, rm)
+  if (DH == 128) {
+    if (wide) DIT_ATT_LAUNCH(128, 8);
+    else DIT_ATT_LAUNCH(128, 4);
+  } else {
+    if (wide) DIT_ATT_LAUNCH(64, 8);
+    else DIT_ATT_LAUNCH(64, 4);
+  }
+#undef DIT_ATT_LAUNCH
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
                             hipStream_t st) {
   if (S == 0) return hipSuccess;
-  dim3 grid((S + ATT_BM - 1) / ATT_BM, H), block(256);
-  const float c = kLog2e / sqrtf(float(DH));
-  const int rm = att_remap(S, DH);
-  if (DH == 128)
-    attention_fwd_kernel<128, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S, S,
-                                                             rm);
-  else if (DH == 64)
-    attention_fwd_kernel<64, false><<<grid, block, 0, st>>>(qkv, out, nullptr, nullptr, S, H, ld_out, c, 0, S, S,
-                                                            rm);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  return launch_fwd<false>(qkv, out, nullptr, nullptr, S, H, DH, ld_out, 0, S, S, 1, st);
 }
 
 // n_chunks key chunks of ceil((kv_end - kv_begin) / n_chunks) tokens in one
@@ -366,18 +400,7 @@ static hipError_t launch_partials(const bf16_t* qkv, int S, int H, int DH, int k
                                   float* o_part, float* lse, hipStream_t st) {
   if (S == 0) return hipSuccess;
   const int chunk = (kv_end - kv_begin + n_chunks - 1) / n_chunks;
-  dim3 grid((S + ATT_BM - 1) / ATT_BM, H, n_chunks), block(256);
-  const float c = kLog2e / sqrtf(float(DH));
-  const int rm = att_remap(chunk, DH);
-  if (DH == 128)
-    attention_fwd_kernel<128, true><<<grid, block, 0, st>>>(qkv, nullptr, o_part, lse, S, H, 0, c, kv_begin, kv_end,
-                                                            chunk, rm);
-  else if (DH == 64)
-    attention_fwd_kernel<64, true><<<grid, block, 0, st>>>(qkv, nullptr, o_part, lse, S, H, 0, c, kv_begin, kv_end,
-                                                           chunk, rm);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  return launch_fwd<true>(qkv, nullptr, o_part, lse, S, H, DH, 0, kv_begin, kv_end, chunk, n_chunks, st);
 }
 
 hipError_t launch_attention_partial(const bf16_t* qkv, int S, int H, int DH, int kv_begin, int kv_end,

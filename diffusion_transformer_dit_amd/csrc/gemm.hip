@@ -436,7 +436,7 @@ using T288x192 = TileCfg<288, 192, 2, 4, 4>;  // 8 waves of 144 x 48; groups own
 using T256 = TileCfg<256, 256, 4, 2, 4>;      // 8 waves of 64 x 128; groups own 128-row halves
 using T128 = TileCfg<128, 128, 4, 2, 4>;      // 8 waves of 32 x 64
 
-static int num_cus() {
+int num_cus() {
   static int n = 0;
   if (n == 0) {
     int dev = 0;

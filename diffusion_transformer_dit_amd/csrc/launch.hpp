@@ -12,6 +12,8 @@ typedef uint16_t bf16_t;
 
 // Cache device properties used for launch shapes (call before a stream capture).
 void prepare_device();
+// compute units of the current device (cached on first use)
+int num_cus();
 
 hipError_t launch_modulation(const bf16_t* temb, const bf16_t* w, const bf16_t* b, float* mod,
                              int rows, int cols, hipStream_t st);

@@ -126,8 +126,10 @@ def _qkv_for_attention(S, H, Dh, seed):
     return qkv
 
 
+# The last two cases give grids of >= 256 eight-wave workgroups, which selects
+# the 8-wave (256-query) kernel; the others run the 4-wave kernel.
 @pytest.mark.parametrize("S,H,Dh", [(200, 2, 128), (256, 4, 64), (64, 1, 128), (1, 2, 64), (333, 3, 128),
-                                    (129, 2, 64)])
+                                    (129, 2, 64), (300, 128, 64), (800, 64, 128)])
 def test_attention_small(gpu_lib, S, H, Dh):
     import torch
     d = H * Dh
@@ -140,17 +142,18 @@ def test_attention_small(gpu_lib, S, H, Dh):
     assert np.all(g[:, d:] == 0)  # columns past H*Dh untouched
 
 
-def test_attention_sharp_scores(gpu_lib):
+@pytest.mark.parametrize("S,H", [(300, 2), (800, 64)])  # 4-wave and 8-wave kernels
+def test_attention_sharp_scores(gpu_lib, S, H):
     """Scores far from 0 (large |q|, |k|) exercise the running max."""
     import torch
-    S, H, Dh = 300, 2, 128
+    Dh = 128
     d = H * Dh
     qkv = _qkv_for_attention(S, H, Dh, 32)
     qkv[:, :2 * d] = DI.round_bf16((qkv[:, :2 * d] * 3.0).astype(np.float32))
     out = torch.empty(S, d, dtype=torch.bfloat16, device="cuda")
     gpu_lib.attention(dev_bf16(qkv), out, H, Dh)
     ref = O.attention(qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:], H, Dh)
-    assert_parity(host(out), ref, "attention sharp")
+    assert_parity(host(out), ref, f"attention sharp S={S} H={H}")
 
 
 @pytest.mark.parametrize("S,H", [(4608, 24), (16384, 12)])
@@ -225,7 +228,8 @@ def test_attention_chunked_flux_eight_chunks(gpu_lib):
     assert st["excess"] <= 2 * 2e-2 * st["rms"], st
 
 
-SPLIT_CASES = [(300, 2, 128, 3), (129, 2, 64, 2), (5, 1, 128, 8), (4608, 3, 128, 4), (256, 4, 64, 1)]
+SPLIT_CASES = [(300, 2, 128, 3), (129, 2, 64, 2), (5, 1, 128, 8), (4608, 3, 128, 4), (256, 4, 64, 1),
+               (300, 64, 128, 2)]  # the last: 8-wave partials
 
 
 @pytest.mark.parametrize("S,H,Dh,n", SPLIT_CASES, ids=[f"S{c[0]}-H{c[1]}-D{c[2]}-n{c[3]}" for c in SPLIT_CASES])
