@@ -75,6 +75,18 @@ def test_gated_residual(gpu_lib, rows, cols):
     assert_parity(host(y), ref, f"gated_residual {rows}x{cols}")
 
 
+@pytest.mark.parametrize("into", ["x", "h"])
+def test_gated_residual_in_place(gpu_lib, into):
+    """y may be x or h (the header allows both)."""
+    import torch
+    ch = DI.chain_inputs(513, 3072)
+    xt, ht = dev_bf16(ch["x"]), dev_bf16(ch["h"])
+    gpu_lib.gated_residual(xt, ht, dev_f32(ch["gate"]), out=xt if into == "x" else ht)
+    torch.cuda.synchronize()
+    ref = O.gated_residual(ch["x"], ch["gate"], ch["h"])
+    assert_parity(host(xt if into == "x" else ht), ref, f"gated_residual in place into {into}")
+
+
 def test_gated_residual_gate_zero_is_identity(gpu_lib):
     ch = DI.chain_inputs(300, 3072)
     y = gpu_lib.gated_residual(dev_bf16(ch["x"]), dev_bf16(ch["h"]), dev_f32(np.zeros(3072, np.float32)))
