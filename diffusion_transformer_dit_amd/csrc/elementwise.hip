@@ -152,53 +152,6 @@ gated_residual_kernel(const bf16_t* x, const bf16_t* h, const float* __restrict_
 }
 
 // ------------------------------------------------------------------------
-// Modulation GEMV: mod[r] = sum_c W[r, c] * SiLU(temb[c]) + b[r].
-// SiLU(temb) is computed once per workgroup into LDS; each wave then streams
-// `rows_per_wave` rows of W with 16-byte loads and reduces across the wave.
-// ------------------------------------------------------------------------
-template <int NCH>
-__global__ void __launch_bounds__(256)
-mod_gemv_kernel(const bf16_t* __restrict__ temb, const bf16_t* __restrict__ w,
-                const bf16_t* __restrict__ b, float* __restrict__ mod, int rows, int cols,
-                int rows_per_wave) {
-  __shared__ __attribute__((aligned(16))) float s_act[NCH * 512];
-  const int nchunk = cols >> 3;
-  for (int i = threadIdx.x; i < cols; i += blockDim.x) s_act[i] = silu(bf2f(temb[i]));
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int r0 = wave * rows_per_wave;
-  if (r0 >= rows) return;
-  const int r1 = min(rows, r0 + rows_per_wave);
-  for (int r = r0; r < r1; ++r) {
-    u32x4 wv[NCH];
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = lane + 64 * j;
-      if (c < nchunk) wv[j] = reinterpret_cast<const u32x4*>(w + size_t(r) * cols)[c];
-    }
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = lane + 64 * j;
-      if (c < nchunk) {
-        float f[8];
-        unpack8(wv[j], f);
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(&s_act[8 * c]);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(&s_act[8 * c + 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc += f[e] * a0[e];
-          acc += f[4 + e] * a1[e];
-        }
-      }
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) mod[r] = acc + (b ? bf2f(b[r]) : 0.f);
-  }
-}
-
-// ------------------------------------------------------------------------
 // Per-head QK RMSNorm + RoPE, in place.  One thread owns 8 consecutive dims
 // (4 rotation pairs) of one (token, q|k, head) row; the DH/8 threads of a row
 // reduce the sum of squares with lane shuffles.
@@ -281,11 +234,14 @@ __global__ void rope_table_kernel(const int32_t* __restrict__ pos, RopeAxes ax, 
 }
 
 // ------------------------------------------------------------------------
-// The modulation GEMVs of a whole block stack in one launch: matrix m of the
-// table (rows_per_mat rows each) gives mods[m * rows_per_mat + r].  The same
-// per-row arithmetic as mod_gemv_kernel (identical results); a wave walks
-// `rows_per_wave` consecutive rows and loads the next row's chunks before it
-// reduces the current one.
+// Modulation GEMVs: mod[r] = sum_c W[r, c] * SiLU(temb[c]) + b[r] for the
+// matrices of a table (one block, the two streams of a block, or a whole
+// block stack in one launch): matrix m (rows_per_mat rows) gives
+// mods[m * rows_per_mat + r].  SiLU(temb) is computed once per workgroup into
+// LDS; a wave walks `rows_per_wave` consecutive rows with 16-byte loads,
+// loads the next row's chunks before it reduces the current one, and reduces
+// across the wave.  Every row's arithmetic is the same whatever the table,
+// so a stack's batched launch gives bitwise the results of per-block ones.
 // ------------------------------------------------------------------------
 // Where the matrices come from: a device array of pointers (a stack's
 // blocks) or up to two pointers passed by value (the two streams of a block).
@@ -308,12 +264,9 @@ mod_gemv_multi_kernel(const bf16_t* __restrict__ temb, Tab tab, float* __restric
                       int rows, int cols, int rows_per_wave) {
   __shared__ __attribute__((aligned(16))) float s_act[NCH * 512];
   const int nchunk = cols >> 3;
-  for (int i = threadIdx.x; i < cols; i += blockDim.x) s_act[i] = silu(bf2f(temb[i]));
-  __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int r0 = wave * rows_per_wave;
-  if (r0 >= rows) return;
   const int r1 = min(rows, r0 + rows_per_wave);
   auto load_row = [&](int r, u32x4 (&v)[NCH]) {
     const int m = r / rows_per_mat;
@@ -324,8 +277,12 @@ mod_gemv_multi_kernel(const bf16_t* __restrict__ temb, Tab tab, float* __restric
       if (c < nchunk) v[j] = reinterpret_cast<const u32x4*>(w)[c];
     }
   };
+  // the first row's loads are in flight while the workgroup computes SiLU
   u32x4 cur[NCH], nxt[NCH];
-  load_row(r0, cur);
+  if (r0 < rows) load_row(r0, cur);
+  for (int i = threadIdx.x; i < cols; i += blockDim.x) s_act[i] = silu(bf2f(temb[i]));
+  __syncthreads();
+  if (r0 >= rows) return;
   for (int r = r0; r < r1; ++r) {
     if (r + 1 < r1) load_row(r + 1, nxt);
     float acc = 0.f;
@@ -435,23 +392,6 @@ hipError_t launch_gated_residual(const bf16_t* x, const bf16_t* h, const float* 
   return hipGetLastError();
 }
 
-hipError_t launch_modulation(const bf16_t* temb, const bf16_t* w, const bf16_t* b, float* mod,
-                             int rows, int cols, hipStream_t st) {
-  const int nch = (cols / 8 + 63) / 64;
-  const int rpw = rows_per_wave_for(rows, 4096);
-  const int waves = (rows + rpw - 1) / rpw;
-  dim3 grid((waves + 3) / 4), block(256);
-  switch (nch) {
-#define CASE(N) \
-  case N: mod_gemv_kernel<N><<<grid, block, 0, st>>>(temb, w, b, mod, rows, cols, rpw); break;
-    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8) CASE(9) CASE(10) CASE(11) CASE(12)
-    CASE(13) CASE(14) CASE(15) CASE(16)
-#undef CASE
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 template <class Tab>
 static hipError_t launch_mod_multi(const bf16_t* temb, const Tab& tab, float* mods, int n_mats, int rows_per_mat,
                                    int cols, int target_waves, hipStream_t st) {
@@ -487,6 +427,11 @@ hipError_t launch_modulation_pair(const bf16_t* temb, const bf16_t* w0, const bf
   tab.bs[0] = b0;
   tab.bs[1] = b1;
   return launch_mod_multi(temb, tab, mods, n_mats, rows_per_mat, cols, 4096, st);
+}
+
+hipError_t launch_modulation(const bf16_t* temb, const bf16_t* w, const bf16_t* b, float* mod, int rows, int cols,
+                             hipStream_t st) {
+  return launch_modulation_pair(temb, w, b, nullptr, nullptr, 1, mod, rows, cols, st);
 }
 
 hipError_t launch_qk_rmsnorm_rope(bf16_t* qkv, const float* qw, const float* kw, const float* rcos,
