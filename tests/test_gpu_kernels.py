@@ -187,6 +187,7 @@ def test_attention_full_size_sampled(gpu_lib, S, H):
     (333, 3, 128, [0, 1, 17, 18, 200, 333]),      # one-token chunks
     (256, 4, 64, [0, 64, 128, 192, 256]),         # tile-aligned, Dh = 64
     (129, 2, 64, [0, 65, 129]),
+    (300, 128, 64, [0, 100, 300]),                # 8-wave partials (grid of 256 workgroups)
 ])
 def test_attention_partial_and_merge(gpu_lib, S, H, Dh, bounds):
     import torch
