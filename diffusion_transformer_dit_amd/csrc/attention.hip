@@ -327,33 +327,56 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
 
 // Merge of the partial results of disjoint key chunks: with
 // lse = ln sum_c exp(lse_c), out = sum_c exp(lse_c - lse) o_c.  One thread
-// owns 4 consecutive dims of one (token, head); the chunk weights are
-// recomputed by each of the head's DH/4 threads.
+// owns 8 consecutive dims of one (token, head); the chunk weights are
+// recomputed by each of the head's DH/8 threads, and the partial outputs are
+// read four chunks at a time (all four loads in flight before the sums).
 __global__ void __launch_bounds__(256)
 attention_merge_kernel(const float* __restrict__ o_parts, const float* __restrict__ lses, int n_chunks, int S,
                        int H, int DH, bf16_t* __restrict__ out, int ld_out) {
   const int d = H * DH;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)S * (d / 4);
+  const long long total = (long long)S * (d / 8);
   if (gid >= total) return;
-  const int t = int(gid / (d / 4));
-  const int c4 = int(gid % (d / 4)) * 4;  // first of the 4 dims
-  const int h = c4 / DH;
+  const int t = int(gid / (d / 8));
+  const int c8 = int(gid % (d / 8)) * 8;  // first of the 8 dims
+  const int h = c8 / DH;
+  const float* lrow = lses + size_t(h) * S + t;  // chunk c at lrow[c * H * S]
+  const size_t lstep = size_t(H) * S;
   float mx = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) mx = fmaxf(mx, lses[(size_t(c) * H + h) * S + t]);
+  for (int c = 0; c < n_chunks; ++c) mx = fmaxf(mx, lrow[c * lstep]);
   float z = 0.f;
-  for (int c = 0; c < n_chunks; ++c) z += exp2_fast((lses[(size_t(c) * H + h) * S + t] - mx) * kLog2e);
+  for (int c = 0; c < n_chunks; ++c) z += exp2_fast((lrow[c * lstep] - mx) * kLog2e);
   const float lz = mx + __log2f(z) * 0.6931471805599453f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < n_chunks; ++c) {
-    const float w = exp2_fast((lses[(size_t(c) * H + h) * S + t] - lz) * kLog2e);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(o_parts + (size_t(c) * S + t) * d + c4);
-    acc += w * o;
+  const float* orow = o_parts + size_t(t) * d + c8;  // chunk c at orow[c * S * d]
+  const size_t ostep = size_t(S) * d;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < n_chunks; c0 += 4) {
+    f32x4 o0[4], o1[4];
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (c0 + i < n_chunks) {
+        const float* p = orow + (c0 + i) * ostep;
+        o0[i] = *reinterpret_cast<const f32x4*>(p);
+        o1[i] = *reinterpret_cast<const f32x4*>(p + 4);
+        w[i] = exp2_fast((lrow[(c0 + i) * lstep] - lz) * kLog2e);
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (c0 + i < n_chunks) {
+        acc0 += w[i] * o0[i];
+        acc1 += w[i] * o1[i];
+      }
   }
-  u32x2 wv;
-  wv[0] = pack_bf2(acc[0], acc[1]);
-  wv[1] = pack_bf2(acc[2], acc[3]);
-  *reinterpret_cast<u32x2*>(out + size_t(t) * ld_out + c4) = wv;
+  // two 8-byte stores: ld_out need only be a multiple of 4
+  u32x2 w0, w1;
+  w0[0] = pack_bf2(acc0[0], acc0[1]);
+  w0[1] = pack_bf2(acc0[2], acc0[3]);
+  w1[0] = pack_bf2(acc1[0], acc1[1]);
+  w1[1] = pack_bf2(acc1[2], acc1[3]);
+  u32x2* dst = reinterpret_cast<u32x2*>(out + size_t(t) * ld_out + c8);
+  dst[0] = w0;
+  dst[1] = w1;
 }
 
 // one head's K and V fit in an XCD's 4 MB L2
@@ -426,7 +449,7 @@ hipError_t launch_attention_split(const bf16_t* qkv, bf16_t* out, int S, int H, 
 hipError_t launch_attention_merge(const float* o_parts, const float* lses, int n_chunks, int S, int H, int DH,
                                   bf16_t* out, int ld_out, hipStream_t st) {
   if (S == 0) return hipSuccess;
-  const long long total = (long long)S * (H * DH / 4);
+  const long long total = (long long)S * (H * DH / 8);
   attention_merge_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(o_parts, lses, n_chunks, S, H, DH, out,
                                                                            ld_out);
   return hipGetLastError();

@@ -215,6 +215,26 @@ def test_attention_partial_and_merge(gpu_lib, S, H, Dh, bounds):
     assert np.all(g[:, d:] == 0)  # columns past H*Dh untouched
 
 
+def test_attention_merge_row_stride_multiple_of_four(gpu_lib):
+    """ld_out = H*Dh + 4: the merge's stores need only 8-byte alignment."""
+    import torch
+    B = gpu_lib
+    S, H, Dh, bounds = 77, 2, 64, [0, 30, 77]
+    d = H * Dh
+    qkv = _qkv_for_attention(S, H, Dh, 36)
+    qd = dev_bf16(qkv)
+    C = len(bounds) - 1
+    o_parts = torch.empty(C, S, d, dtype=torch.float32, device="cuda")
+    lses = torch.empty(C, H, S, dtype=torch.float32, device="cuda")
+    for c, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        B.attention_partial(qd, H, Dh, a, b, o_part=o_parts[c], lse=lses[c])
+    out = torch.zeros(S, d + 4, dtype=torch.bfloat16, device="cuda")
+    B.attention_merge(o_parts, lses, out, H, Dh)
+    g = host(out)
+    assert_parity(g[:, :d], O.attention(qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:], H, Dh), "merge ld_out = d + 4")
+    assert np.all(g[:, d:] == 0)
+
+
 def test_attention_chunked_flux_eight_chunks(gpu_lib):
     """The pages' 8-way split of the Flux sequence (8 x 576 keys), merged on one GPU."""
     import torch
