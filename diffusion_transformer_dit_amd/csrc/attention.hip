@@ -113,7 +113,7 @@ __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 // With PARTIAL, blockIdx.z selects one of gridDim.z consecutive key chunks
 // of kv_chunk tokens inside [kv_begin, kv_end) and its output slices
 // (out_f32 + z*S*H*DH, lse + z*H*S): a split of the keys over more
-// workgroups when S/128 x H workgroups cannot fill the chip.
+// workgroups when one workgroup per query block and head cannot fill the chip.
 // NW waves per workgroup (32 NW queries): 8 (one workgroup per CU) or 4 (two).
 template <int DH, bool PARTIAL, int NW>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)

@@ -157,8 +157,8 @@ int dit_attention_merge(const float* o_parts, const float* lses, int64_t n_chunk
  * equal chunks (n_chunks in [1, 64]; chunks are ceil(S / n_chunks) tokens,
  * so fewer may result, never an empty one): the partials of all chunks in
  * one launch, then dit_attention_merge's weighting into out (bf16, row stride
- * ld_out).  For head counts too small to fill the chip with one workgroup
- * per 128 queries and head (e.g. one GPU's heads after an all-to-all from
+ * ld_out).  For head counts too small to fill the chip with workgroups of
+ * 128 or 256 queries of one head (e.g. one GPU's heads after an all-to-all from
  * sequence to head sharding, the Flux page, section 5): the chunks give
  * n_chunks times as many workgroups.  o_parts [n_chunks, S, H*Dh] fp32 and
  * lses [n_chunks, H, S] fp32 are caller-owned scratch. */
