@@ -401,7 +401,9 @@ gemm_bf16_tn_kernel(GemmGroup<Epi, NP> grp) {
     } else if (k >= 1) {
       mfmas();
     }
-    sync(ahead);
+    // phase 2 needs no wait: every wave's loads of slice k landed before the
+    // phase-1 barrier, and no slot is refilled before the next one
+    block_barrier();
     if (k < KT) {
       if (group == 0) {
         mfmas();
