@@ -636,12 +636,12 @@ extern "C" int dit_stack_create(dit_stack** out) {
 
 extern "C" int dit_stack_destroy(dit_stack* st) {
   if (!st) return DIT_OK;
-  if (st->probe_buf) hipFree(st->probe_buf);
-  if (st->mod_ptrs) hipFree(st->mod_ptrs);
-  if (st->mods) hipFree(st->mods);
-  if (st->exec) hipGraphExecDestroy(st->exec);
-  if (st->graph) hipGraphDestroy(st->graph);
-  if (st->cap) hipStreamDestroy(st->cap);
+  if (st->probe_buf) (void)hipFree(st->probe_buf);
+  if (st->mod_ptrs) (void)hipFree(st->mod_ptrs);
+  if (st->mods) (void)hipFree(st->mods);
+  if (st->exec) (void)hipGraphExecDestroy(st->exec);
+  if (st->graph) (void)hipGraphDestroy(st->graph);
+  if (st->cap) (void)hipStreamDestroy(st->cap);
   delete st;
   return DIT_OK;
 }
@@ -711,7 +711,7 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
                   "hipDeviceGetAttribute");
     if (st->wall_khz <= 0) return fail(DIT_ERR_HIP, "device reports no wall-clock rate");
     const size_t bytes = size_t(P.n_single) * kProbeChannels * 2 * sizeof(unsigned long long);
-    if (st->probe_buf) hipFree(st->probe_buf);
+    if (st->probe_buf) (void)hipFree(st->probe_buf);
     st->probe_buf = nullptr;
     DIT_CHECK_HIP(hipMalloc(&st->probe_buf, bytes), "hipMalloc");
     DIT_CHECK_HIP(hipMemset(st->probe_buf, 0, bytes), "hipMemset");
@@ -732,8 +732,8 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
   for (int b = 0; b < P.n_single; ++b)
     tab[n_dm + b] = P.singles[b].w_mod, tab[n_mats + n_dm + b] = P.singles[b].b_mod;
   const size_t n_mod = size_t(n_dm) * 6 * D.d + size_t(P.n_single) * 3 * D.d;
-  if (st->mod_ptrs) hipFree(st->mod_ptrs);
-  if (st->mods) hipFree(st->mods);
+  if (st->mod_ptrs) (void)hipFree(st->mod_ptrs);
+  if (st->mods) (void)hipFree(st->mods);
   st->mod_ptrs = nullptr;
   st->mods = nullptr;
   DIT_CHECK_HIP(hipMalloc(reinterpret_cast<void**>(&st->mod_ptrs), tab.size() * sizeof(void*)), "hipMalloc");
@@ -777,14 +777,14 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
   hipGraph_t g = nullptr;
   hipError_t e = hipStreamEndCapture(st->cap, &g);
   if (brc != DIT_OK) {
-    if (g) hipGraphDestroy(g);
+    if (g) (void)hipGraphDestroy(g);
     return brc;
   }
   if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
   hipGraphExec_t ex = nullptr;
   e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
   if (e != hipSuccess) {
-    hipGraphDestroy(g);
+    (void)hipGraphDestroy(g);
     return hip_fail(e, "hipGraphInstantiate");
   }
   st->graph = g;
