@@ -307,7 +307,8 @@ def test_attention_partial_rejects_bad_ranges(gpu_lib):
 
 
 # ------------------------------------------------------------ linear1 + GELU
-@pytest.mark.parametrize("S,d,mlp", [(300, 256, 1024), (4608, 3072, 12288), (97, 128, 192)])
+# (300, 8192, 8192): the largest dim the row kernels accept
+@pytest.mark.parametrize("S,d,mlp", [(300, 256, 1024), (4608, 3072, 12288), (97, 128, 192), (300, 8192, 8192)])
 def test_linear1_gelu(gpu_lib, S, d, mlp):
     import torch
     u = DI.draw(41, (S, d), 1.0)
@@ -325,7 +326,8 @@ def test_linear1_gelu(gpu_lib, S, d, mlp):
 
 
 # ------------------------------------------------------------ linear2 + gated residual
-@pytest.mark.parametrize("S,d,mlp", [(300, 256, 1024), (4608, 3072, 12288), (97, 128, 192), (16384, 1536, 8960)])
+@pytest.mark.parametrize("S,d,mlp", [(300, 256, 1024), (4608, 3072, 12288), (97, 128, 192), (16384, 1536, 8960),
+                                   (300, 8192, 8192)])
 def test_linear2_gated_residual(gpu_lib, S, d, mlp):
     cat = DI.draw(51, (S, d + mlp), 1.0)
     w2 = DI.draw(52, (d, d + mlp), 0.02)
