@@ -21,7 +21,7 @@ def _vec(seed, n, sigma):
 
 
 # ------------------------------------------------------------ modulation GEMV
-@pytest.mark.parametrize("d,tdim", [(256, 256), (3072, 3072), (1536, 1536), (64, 40)])
+@pytest.mark.parametrize("d,tdim", [(256, 256), (3072, 3072), (1536, 1536), (64, 40), (8192, 8192)])
 def test_modulation(gpu_lib, d, tdim):
     temb = DI.draw(11, (tdim,), 1.0)
     w = DI.draw(12, (3 * d, tdim), 0.02)
