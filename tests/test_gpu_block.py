@@ -233,6 +233,41 @@ def test_stack_replay_equals_eager_bitwise(gpu_lib):
     st.close()
 
 
+def test_stack_replay_equals_eager_bitwise_flux_shape(gpu_lib):
+    """At the Flux shape the stack takes the paths the small shapes do not
+    (batched 6-chunk modulation, q/k RMSNorm + RoPE in linear1's epilogue,
+    8-wave attention): 3 blocks x 2 steps replayed twice, each step bitwise
+    the eager block forwards.  Inputs are seeded device draws; no oracle."""
+    import torch
+    B = gpu_lib
+    shape = DI.FLUX
+    S, d, mlp, Dh = shape.seq_len, shape.dim, shape.mlp_hidden, shape.head_dim
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    rn = lambda *sz, s=0.02: (torch.randn(*sz, generator=g, device="cuda") * s).to(torch.bfloat16)
+    blocks = [B.BlockWeights(rn(3 * d, d), rn(3 * d), rn(3 * d + mlp, d), rn(3 * d + mlp), rn(d, d + mlp), rn(d),
+                             torch.rand(Dh, generator=g, device="cuda") + 0.5,
+                             torch.rand(Dh, generator=g, device="cuda") + 0.5) for _ in range(3)]
+    x = rn(S, d, s=1.0)
+    tembs = rn(2, d, s=1.0)
+    _, rc, rs = rope_dev(B, shape)
+    cfg = cfg_of(B, shape)
+    ws = B.alloc_workspace(B.stack_workspace_bytes(cfg))
+    out = torch.empty(2, S, d, dtype=torch.bfloat16, device="cuda")
+    st = B.Stack()
+    wse = B.alloc_workspace(B.block_workspace_bytes(cfg))
+    for rep in range(2):
+        st.replay(cfg, blocks, x, tembs, rc, rs, out, ws)
+        for s in range(2):
+            cur = x.clone()
+            for b in blocks:
+                B.block_forward(cfg, b, cur, tembs[s].contiguous(), rc, rs, y=cur, workspace=wse)
+            torch.cuda.synchronize()
+            assert torch.isfinite(out[s].float()).all()
+            assert torch.equal(cur, out[s]), f"replay {rep} step {s}"
+    st.close()
+
+
 def test_stack_all_gates_zero_returns_input(gpu_lib):
     import torch
     B = gpu_lib
