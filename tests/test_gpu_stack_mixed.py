@@ -85,6 +85,46 @@ def test_mixed_stack_replay_equals_eager_bitwise(gpu_lib):
         assert np.array_equal(host(cur), out[s]), s
 
 
+def test_mixed_stack_replay_equals_eager_bitwise_flux_shape(gpu_lib):
+    """The Flux composition at the Flux shape (512 text + 4096 image tokens):
+    1 two-stream + 2 single-stream blocks x 2 steps, replayed twice, each
+    step bitwise the eager block forwards.  Seeded device draws; no oracle."""
+    import torch
+    B = gpu_lib
+    shape = DI.FLUX
+    S, d, mlp, Dh, txt = shape.seq_len, shape.dim, shape.mlp_hidden, shape.head_dim, shape.text_tokens
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    rn = lambda *sz, s=0.02: (torch.randn(*sz, generator=g, device="cuda") * s).to(torch.bfloat16)
+    nw = lambda: torch.rand(Dh, generator=g, device="cuda") + 0.5
+    stream = lambda: B.StreamWeights(rn(6 * d, d), rn(6 * d), rn(3 * d, d), rn(3 * d), nw(), nw(), rn(d, d), rn(d),
+                                     rn(mlp, d), rn(mlp), rn(d, mlp), rn(d))
+    doubles = [(stream(), stream())]
+    singles = [B.BlockWeights(rn(3 * d, d), rn(3 * d), rn(3 * d + mlp, d), rn(3 * d + mlp), rn(d, d + mlp), rn(d),
+                              nw(), nw()) for _ in range(2)]
+    x = rn(S, d, s=1.0)
+    tembs = rn(2, d, s=1.0)
+    _, rc, rs = rope_dev(B, shape)
+    cfg = cfg_of(B, shape)
+    ws = B.alloc_workspace(B.stack_mixed_workspace_bytes(cfg))
+    wsm = B.alloc_workspace(B.mmdit_block_workspace_bytes(cfg))
+    wsb = B.alloc_workspace(B.block_workspace_bytes(cfg))
+    out = torch.empty(2, S, d, dtype=torch.bfloat16, device="cuda")
+    st = B.Stack()
+    for rep in range(2):
+        st.replay_mixed(cfg, txt, doubles, singles, x, tembs, rc, rs, out, ws)
+        for s in range(2):
+            cur = x.clone()
+            for t, i in doubles:
+                B.mmdit_block_forward(cfg, txt, t, i, cur, tembs[s].contiguous(), rc, rs, y=cur, workspace=wsm)
+            for b in singles:
+                B.block_forward(cfg, b, cur, tembs[s].contiguous(), rc, rs, y=cur, workspace=wsb)
+            torch.cuda.synchronize()
+            assert torch.isfinite(out[s].float()).all()
+            assert torch.equal(cur, out[s]), f"replay {rep} step {s}"
+    st.close()
+
+
 def test_mixed_stack_skipped_step(gpu_lib):
     B = gpu_lib
     doubles, singles = _weights(B, 1, 1)
