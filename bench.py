@@ -74,6 +74,23 @@ def load_traffic():
     return t.get("bytes_per_launch")
 
 
+def load_launch_gaps():
+    """Kernels per block and the gaps between kernels inside the replayed
+    steps, from the committed summary of a rocprofv3 kernel trace of this
+    bench (written by --trace-summary), or None when it is absent."""
+    path = os.path.join(ROOT, "profiles", "flux_stack_launch_gaps.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    keep = ("kernels_per_block", "kernels_per_step", "gap_us_per_step_mean", "mean_gap_us", "max_gap_us",
+            "gap_frac", "steps")
+    out = {k: t.get(k) for k in keep}
+    out["source"] = "profiles/flux_stack_launch_gaps.json (rocprofv3 kernel trace)"
+    return out
+
+
 def time_launches(fn, iters, warm=2):
     import torch
     for _ in range(warm):
@@ -118,7 +135,8 @@ def time_graph(fn, iters, replays=3):
 
 
 KERNEL_NAMES = ("modulation", "block_modulate_norm", "modulate_norm", "linear1_gelu", "qk_rmsnorm_rope",
-                "attention", "linear2_gated_residual", "gated_residual", "copy", "block_forward", "other_blocks")
+                "attention", "linear2_gated_residual", "gated_residual", "copy", "block_forward", "other_blocks",
+                "config_blocks", "ceilings")
 
 
 def block_sequence_times(B, blocks, x_in, temb, rc, rs, iters, only=None):
@@ -283,9 +301,197 @@ def other_block_times(B, g, dev, reps=3):
     return res
 
 
+def block_flop(S_, d, H_, dh, mlp):
+    """Algorithmic flops of one single-stream block forward: linear1, linear2,
+    attention (QK^T and PV) and the modulation GEMV."""
+    return 2.0 * S_ * d * (3 * d + mlp) + 2.0 * S_ * (d + mlp) * d + 4.0 * H_ * S_ * S_ * dh + 2.0 * 3 * d * d
+
+
+def config_block_times(B, g, dev, reps=3):
+    """One single-stream block forward at the other configurations of the
+    workload list, captured in a graph and replayed: the tiny block (S=256,
+    d=256, 4x64, MLP 1024, 2D RoPE on 16x16) and the long-sequence video
+    block (S=16384, d=1536, 12x128, MLP 8960, 3D RoPE on 16x32x32)."""
+    import torch
+    import dit_inputs as DI
+    res = {}
+    for name, sh in (("tiny_block", DI.TINY), ("video_block", DI.VIDEO)):
+        d, mlp, dh, H_, S_ = sh.dim, sh.mlp_hidden, sh.head_dim, sh.num_heads, sh.seq_len
+        rnd = lambda shape, sigma=0.02: (torch.randn(shape, generator=g, device=dev) * sigma).to(torch.bfloat16)
+        w = B.BlockWeights(rnd((3 * d, d)), rnd((3 * d,)), rnd((3 * d + mlp, d)), rnd((3 * d + mlp,)),
+                           rnd((d, d + mlp)), rnd((d,)), torch.ones(dh, device=dev), torch.ones(dh, device=dev))
+        cfg = B.make_config(S_, d, H_, dh, mlp)
+        ws = B.alloc_workspace(B.block_workspace_bytes(cfg))
+        pos = torch.from_numpy(DI.positions(sh)).to(dev)
+        rc, rs = B.rope_table(pos, list(sh.rope_axes_dims), dh)
+        x = rnd((S_, d), 1.0)
+        temb = rnd((d,), 1.0)
+        y = torch.empty_like(x)
+        n = 64 if S_ <= 1024 else 4
+        ms = time_graph(lambda i: B.block_forward(cfg, w, x, temb, rc, rs, y=y, workspace=ws), n, reps)
+        flop = block_flop(S_, d, H_, dh, mlp)
+        tfl = flop / (ms * 1e-3) / 1e12
+        res[name] = dict(S=S_, dim=d, heads=H_, head_dim=dh, mlp_hidden=mlp, ms=round(ms, 4),
+                         gflop=round(flop / 1e9, 2), tflops=round(tfl, 1), frac=round(tfl / BF16_PEAK_TFLOPS, 4))
+        del w, ws, x, y
+    torch.cuda.synchronize()
+    return res
+
+
+def ceiling_times(B, g, dev, reps=3):
+    """What the chip delivers: the streaming copy at the chain's sizes (12
+    rotating buffer sets, more than the 256 MB last-level cache) and at 1
+    and 4 GiB, and bf16 MFMA throughput with fixed and with changing
+    operands.  Copy GB/s count bytes read plus bytes written."""
+    import torch
+    res = {"copy": {}, "mfma": {}}
+    for label, nbytes, nrot in (("56.6MB_moved", S * D * 2, 12), ("84.9MB_moved", S * D * 3, 12),
+                                ("1GiB_moved", 1 << 29, 1), ("4GiB_moved", 1 << 31, 1)):
+        srcs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nrot)]
+        dsts = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nrot)]
+        for t in srcs:
+            t.random_(0, 255, generator=g)
+        n = max(4 * nrot, 8)
+        ms = time_graph(lambda i: B.probe_copy(srcs[i % nrot], dsts[i % nrot]), n, reps)
+        res["copy"][label] = dict(bytes_moved=2 * nbytes, us=round(ms * 1e3, 2),
+                                  gbs=round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+                                  frac_of_8TBs=round(2 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        del srcs, dsts
+        torch.cuda.synchronize()
+    nwg, iters = 2 * 256, 20000
+    out = torch.empty(nwg * 256, dtype=torch.float32, device=dev)
+    flop = nwg * 4.0 * iters * 16 * 16384
+    for label, vary in (("fixed_operands", 0), ("changing_operands", 1)):
+        ms = time_graph(lambda i: B.probe_mfma(out, nwg, iters, vary), 2, reps)
+        tfl = flop / (ms * 1e-3) / 1e12
+        res["mfma"][label] = dict(tflops=round(tfl, 1), frac=round(tfl / BF16_PEAK_TFLOPS, 4),
+                                  ms=round(ms, 3))
+    res["mfma"]["shape"] = (f"{nwg} workgroups x 4 waves x {iters} x 16 v_mfma_f32_16x16x32_bf16, "
+                            "16 independent accumulators per wave")
+    return res
+
+
+def host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return model, avail
+
+
+def trace_summary(path, n_blocks=57):
+    """Kernels per step and per block and the gaps between consecutive
+    kernels inside each replayed step of the 57-block stack, from a
+    rocprofv3 kernel trace (CSV).  A step starts at each launch of the
+    batched modulation kernel and holds the launches up to the next one that
+    is not a block kernel (copies, probes, other legs)."""
+    import csv
+    import glob
+    if os.path.isdir(path):
+        cands = sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True))
+        if not cands:
+            raise SystemExit(f"no *kernel_trace.csv under {path}")
+        path = cands[0]
+    with open(path) as f:
+        rows = list(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    block_kernels = ("gemm_bf16_tn_kernel", "attention_fwd_kernel", "ln_modulate_kernel", "qk_rmsnorm_rope_kernel",
+                     "mod_gemv")
+    is_block = lambda name: any(k in name for k in block_kernels)
+    steps = []
+    i = 0
+    while i < len(rows):
+        if "mod_gemv_multi_kernel" in rows[i]["Kernel_Name"]:
+            j = i + 1
+            while j < len(rows) and is_block(rows[j]["Kernel_Name"]) and \
+                    "mod_gemv_multi_kernel" not in rows[j]["Kernel_Name"]:
+                j += 1
+            steps.append(rows[i:j])
+            i = j
+        else:
+            i += 1
+    # only the plain (unprobed) 57-block replays: a probed step interleaves stamp kernels
+    want = [st for st in steps if (len(st) - 1) % n_blocks == 0 and (len(st) - 1) // n_blocks in (5, 6)]
+    if not want:
+        raise SystemExit("no replayed step of the stack found in the trace")
+    out = []
+    for st in want:
+        t0, t1 = int(st[0]["Start_Timestamp"]), int(st[-1]["End_Timestamp"])
+        gaps = [int(b["Start_Timestamp"]) - int(a["End_Timestamp"]) for a, b in zip(st, st[1:])]
+        busy = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in st)
+        out.append(dict(kernels=len(st), kernels_per_block=(len(st) - 1) / n_blocks, span_us=(t1 - t0) / 1e3,
+                        busy_us=busy / 1e3, gap_us=sum(gaps) / 1e3, max_gap_us=max(gaps) / 1e3,
+                        mean_gap_us=sum(gaps) / len(gaps) / 1e3, negative_gaps=sum(1 for x in gaps if x < 0)))
+    agg = dict(source=os.path.relpath(path), steps=len(out), kernels_per_step=out[0]["kernels"],
+               kernels_per_block=out[0]["kernels_per_block"],
+               span_us_mean=round(sum(o["span_us"] for o in out) / len(out), 1),
+               gap_us_per_step_mean=round(sum(o["gap_us"] for o in out) / len(out), 1),
+               mean_gap_us=round(sum(o["mean_gap_us"] for o in out) / len(out), 3),
+               max_gap_us=round(max(o["max_gap_us"] for o in out), 3),
+               gap_frac=round(sum(o["gap_us"] for o in out) / sum(o["span_us"] for o in out), 5),
+               per_step=[{k: (round(v, 3) if isinstance(v, float) else v) for k, v in o.items()} for o in out])
+    return agg
+
+
+def cpu_oracle_per_config():
+    """The oracle's time per workload on the host cores: the tiny block and
+    the chain ops in full, the video block on two sampled query-row counts
+    (every key and value computed) extrapolated linearly to all rows, and
+    the 57 x 50 stack extrapolated from the Flux block (labelled)."""
+    import numpy as np
+    import dit_inputs as DI
+    from oracle import dit_oracle as O
+    res = {}
+
+    def timed(fn, reps=1):
+        best = None
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+        return best
+
+    sh = DI.TINY
+    w = DI.block_weights(sh)
+    x, temb = DI.block_activations(sh)
+    pos = DI.positions(sh)
+    res["tiny_block_ms"] = round(1e3 * timed(lambda: O.block_forward(sh, w, x, temb, pos), 3), 2)
+    ch = DI.chain_inputs()
+    res["chain_modulate_norm_ms"] = round(1e3 * timed(
+        lambda: O.layer_norm_modulate(ch["x"], ch["shift"], ch["scale"], 1e-6), 2), 1)
+    res["chain_gated_residual_ms"] = round(1e3 * timed(lambda: O.gated_residual(ch["x"], ch["gate"], ch["h"]), 2), 1)
+    sh = DI.VIDEO
+    w = DI.block_weights(sh)
+    x, temb = DI.block_activations(sh)
+    pos = DI.positions(sh)
+    pts = {}
+    for r in (256, 1024):
+        rows = np.arange(0, sh.seq_len, sh.seq_len // r)[:r]
+        pts[r] = timed(lambda: O.block_forward(sh, w, x, temb, pos, rows=rows))
+    slope = (pts[1024] - pts[256]) / (1024 - 256)
+    res["video_block"] = dict(ms_256_rows=round(pts[256] * 1e3, 1), ms_1024_rows=round(pts[1024] * 1e3, 1),
+                              ms_all_rows_extrapolated=round((pts[1024] + slope * (sh.seq_len - 1024)) * 1e3, 1),
+                              note="linear in the number of query rows; K and V always cover all 16384 tokens")
+    return res
+
+
 def kernel_phase(B, g, dev, blocks, x_in, temb, rc, rs, it, only=None):
     """Block-sequence times of the six block kernels plus the HBM-rate loops."""
-    k = block_sequence_times(B, blocks, x_in, temb, rc, rs, it, only)
+    seq_names = ("modulation", "block_modulate_norm", "linear1_gelu", "qk_rmsnorm_rope", "attention",
+                 "linear2_gated_residual")
+    k = {}
+    if only is None or any(n in only for n in seq_names):
+        k = block_sequence_times(B, blocks, x_in, temb, rc, rs, it, only)
     k2, warm = hbm_kernel_times(B, g, dev, it, only)
     k.update(k2)
     if only is not None and "block_forward" in only:
@@ -312,6 +518,7 @@ def cpu_baseline():
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    model, avail = host_cpu()
     shape = DI.FLUX
     w = DI.block_weights(shape)
     x, temb = DI.block_activations(shape)
@@ -322,7 +529,9 @@ def cpu_baseline():
     assert np.all(np.isfinite(y))
     return dict(value=round(dt * 1000.0, 1), unit="ms per block", cores=int(threads), kind="oracle",
                 sample="one full Flux-shape block forward (S=4608, d=3072, 24x128, MLP 12288) "
-                       "in numpy float64, BLAS threads = cores; 1 of the 57 blocks of a step")
+                       "in numpy float64, BLAS threads = cores; 1 of the 57 blocks of a step",
+                cpu_model=model, cpus_available=avail,
+                stack_57x50_extrapolated_s=round(dt * 57 * 50, 1))
 
 
 def main():
@@ -333,10 +542,16 @@ def main():
     ap.add_argument("--blocks", type=int, default=57)
     ap.add_argument("--kernel-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-summary", default=None,
+                    help="summarise a rocprofv3 kernel trace (CSV file or output folder) of a bench run: kernels "
+                         "per block and launch gaps inside the replayed steps; prints JSON and exits")
     ap.add_argument("--kernels-only", default=None,
                     help="comma list of kernels (%s): time only these, no stack replay (for profiler runs)"
                          % ",".join(KERNEL_NAMES))
     args = ap.parse_args()
+    if args.trace_summary:
+        print(json.dumps(trace_summary(args.trace_summary, args.blocks)), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the block's multi-GPU sharding is a design, not built)", file=sys.stderr)
@@ -372,6 +587,10 @@ def main():
         out = {"kernels_us": {n: round(v * 1e3, 2) for n, v in k.items()}}
         if "other_blocks" in only:
             out["other_blocks"] = other_block_times(B, g, dev)
+        if "config_blocks" in only:
+            out["config_blocks"] = config_block_times(B, g, dev)
+        if "ceilings" in only:
+            out["ceilings"] = ceiling_times(B, g, dev)
         print(json.dumps(out), flush=True)
         return 0
 
@@ -388,7 +607,7 @@ def main():
     pos = torch.from_numpy(DI.positions(DI.FLUX)).to(dev)
     rc, rs = B.rope_table(pos, list(DI.FLUX.rope_axes_dims), DH)
     cfg = B.make_config(S, D, H, DH, MLP)
-    ws = B.alloc_workspace(B.stack_workspace_bytes(cfg))
+    ws = B.alloc_workspace(B.stack_workspace_bytes(cfg, nb))
     out = torch.empty(max(n_total, 1), S, D, dtype=torch.bfloat16, device=dev)
     st = B.Stack()
     torch.cuda.synchronize()
@@ -418,7 +637,7 @@ def main():
     # the replay, as the kernels run there
     stp = B.Stack()
     stp.set_probe(B.Stack.KERNELS)
-    wsp = B.alloc_workspace(B.stack_workspace_bytes(cfg))
+    wsp = B.alloc_workspace(B.stack_workspace_bytes(cfg, nb))
     stp.replay(cfg, blocks, x_in, temb[:max(args.warmup, 1)], rc, rs, out[:max(args.warmup, 1)], wsp)
     stp.probe_ms(nb)  # discards the warmup steps
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -463,8 +682,6 @@ def main():
     for v in kernels.values():
         for kk in list(v):
             v[kk] = round(v[kk], 4 if kk == "frac" else 2)
-    sum_kernels_ms = sum(k[n] for n in ("modulation", "block_modulate_norm", "linear1_gelu", "qk_rmsnorm_rope",
-                                        "attention", "linear2_gated_residual"))
 
     g1 = tf(GEMM1_FLOP, k["linear1_gelu"])
     traffic = load_traffic()
@@ -493,8 +710,7 @@ def main():
                      "frac": round(g1 / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "flop_per_launch": GEMM1_FLOP},
         "kernels": kernels,
-        # share of the replayed step not covered by the six kernels' in-graph times
-        "graph_gap_frac": round(1.0 - sum_kernels_ms / ms_block, 4),
+        "launch_gaps": load_launch_gaps(),
         "ms_per_step_probed": round(ms_step_probed, 3),
         "timing_note": ("per-kernel times: device wall-clock stamps captured around every kernel of every "
                         "block in a second replay of the same timed steps (ms_per_step_probed), stamp overhead "
@@ -557,7 +773,7 @@ def main():
                                  randn((MLP, D), 0.02), randn((MLP,), 0.02), randn((D, MLP), 0.02), randn((D,), 0.02))
     fdoubles = [(sw(), sw()) for _ in range(nd_)]
     fsingles = blocks[:ns_]
-    wsf = B.alloc_workspace(B.stack_mixed_workspace_bytes(cfg))
+    wsf = B.alloc_workspace(B.stack_mixed_workspace_bytes(cfg, DI.FLUX.text_tokens, nd_, ns_))
     outf = torch.empty(4, S, D, dtype=torch.bfloat16, device=dev)
     stf = B.Stack()
     stf.replay_mixed(cfg, DI.FLUX.text_tokens, fdoubles, fsingles, x_in, temb[:1], rc, rs, outf[:1], wsf)
@@ -582,10 +798,29 @@ def main():
         v["note"] = "one block forward captured in a graph and replayed (same weights each replay)"
     result["other_blocks"] = ob
     log("other blocks: " + ", ".join(f"{n} {v['ms']:.3f} ms ({v['tflops']} TFLOP/s)" for n, v in ob.items()))
+    cb = config_block_times(B, g, dev)
+    cb["note"] = "single-stream block forward captured in a graph and replayed; frac of 2.5 PFLOP/s"
+    result["config_blocks"] = cb
+    log("config blocks: " + ", ".join(f"{n} {v['ms']:.4f} ms ({v['tflops']} TFLOP/s)"
+                                      for n, v in cb.items() if isinstance(v, dict)))
+    ce = ceiling_times(B, g, dev)
+    result["ceilings"] = ce
+    cpy_n, cpy_g = ce["copy"]["56.6MB_moved"]["gbs"], ce["copy"]["84.9MB_moved"]["gbs"]
+    kernels["modulate_norm"]["frac_of_copy_same_size"] = round(kernels["modulate_norm"]["gbs"] / cpy_n, 4)
+    kernels["gated_residual"]["frac_of_copy_same_size"] = round(kernels["gated_residual"]["gbs"] / cpy_g, 4)
+    kernels["modulate_norm"]["frac_of_copy_4GiB"] = round(kernels["modulate_norm"]["gbs"] /
+                                                          ce["copy"]["4GiB_moved"]["gbs"], 4)
+    kernels["gated_residual"]["frac_of_copy_4GiB"] = round(kernels["gated_residual"]["gbs"] /
+                                                           ce["copy"]["4GiB_moved"]["gbs"], 4)
+    log("ceilings: copy " + ", ".join(f"{n} {v['gbs']} GB/s" for n, v in ce["copy"].items()) + "; mfma "
+        + ", ".join(f"{n} {v['tflops']} TFLOP/s" for n, v in ce["mfma"].items() if isinstance(v, dict)))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one Flux block ...")
         result["cpu_baseline"] = cpu_baseline()
         log(f"cpu oracle: {result['cpu_baseline']['value']} ms/block on {result['cpu_baseline']['cores']} threads")
+        log("timing the CPU oracle on the other workloads ...")
+        result["cpu_oracle_per_config"] = cpu_oracle_per_config()
+        log(f"cpu oracle per config: {result['cpu_oracle_per_config']}")
     st.close()
     print(json.dumps(result), flush=True)
     return 0

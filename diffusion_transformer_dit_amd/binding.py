@@ -65,18 +65,21 @@ SIGNATURES = {
     "dit_sequential_block_forward": ([VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
     "dit_stack_create": ([VP], ctypes.c_int),
     "dit_stack_destroy": ([VP], ctypes.c_int),
-    "dit_stack_workspace_bytes": ([VP], SZ),
+    "dit_stack_workspace_bytes": ([VP, ctypes.c_int], SZ),
     "dit_stack_replay": ([VP, VP, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
     "dit_attention_partial": ([VP, I64, I64, I64, I64, I64, VP, VP, VP], ctypes.c_int),
     "dit_attention_merge": ([VP, VP, I64, I64, I64, I64, VP, I64, VP], ctypes.c_int),
     "dit_attention_split": ([VP, VP, I64, I64, I64, I64, I64, VP, VP, VP], ctypes.c_int),
     "dit_stack_replay_cached": ([VP, VP, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP, VP, VP, SZ, VP, VP, VP],
                                 ctypes.c_int),
-    "dit_stack_mixed_workspace_bytes": ([VP], SZ),
+    "dit_stack_mixed_workspace_bytes": ([VP, I64, ctypes.c_int, ctypes.c_int], SZ),
     "dit_stack_replay_mixed": ([VP, VP, I64, VP, VP, ctypes.c_int, VP, ctypes.c_int, VP, VP, ctypes.c_int, VP, VP,
                                 VP, VP, SZ, VP, VP, VP], ctypes.c_int),
     "dit_stack_set_probe": ([VP, ctypes.c_uint32], ctypes.c_int),
     "dit_stack_probe_ms": ([VP, VP, ctypes.c_int], ctypes.c_int),
+    "dit_stack_graph_info": ([VP, VP, VP], ctypes.c_int),
+    "dit_probe_copy": ([VP, VP, SZ, VP], ctypes.c_int),
+    "dit_probe_mfma": ([VP, I64, I64, I32, VP], ctypes.c_int),
     "dit_last_error": ([], ctypes.c_char_p),
     "dit_version": ([], ctypes.c_char_p),
 }
@@ -378,12 +381,13 @@ def block_workspace_bytes(cfg: BlockConfig) -> int:
     return int(_lib.dit_block_workspace_bytes(ctypes.byref(cfg)))
 
 
-def stack_workspace_bytes(cfg: BlockConfig) -> int:
-    return int(_lib.dit_stack_workspace_bytes(ctypes.byref(cfg)))
+def stack_workspace_bytes(cfg: BlockConfig, n_blocks: int) -> int:
+    return int(_lib.dit_stack_workspace_bytes(ctypes.byref(cfg), int(n_blocks)))
 
 
-def stack_mixed_workspace_bytes(cfg: BlockConfig) -> int:
-    return int(_lib.dit_stack_mixed_workspace_bytes(ctypes.byref(cfg)))
+def stack_mixed_workspace_bytes(cfg: BlockConfig, txt_len: int, n_double: int, n_single: int) -> int:
+    return int(_lib.dit_stack_mixed_workspace_bytes(ctypes.byref(cfg), int(txt_len), int(n_double),
+                                                    int(n_single)))
 
 
 def alloc_workspace(nbytes: int, device="cuda"):
@@ -406,6 +410,26 @@ def block_forward(cfg, weights: BlockWeights, x, temb, rope_cos, rope_sin, y=Non
     _check(_lib.dit_block_forward(ctypes.byref(cfg), ctypes.byref(weights.c), _p(x), _p(temb), _p(rope_cos),
                                   _p(rope_sin), _p(y), _p(workspace), workspace.numel(), _stream(stream)))
     return y
+
+
+def probe_copy(src, dst, stream=None):
+    """Ceiling probe: streaming copy of src into dst (same byte size, disjoint)."""
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous GPU tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same byte size")
+    _check(_lib.dit_probe_copy(_p(src), _p(dst), nbytes, _stream(stream)))
+    return dst
+
+
+def probe_mfma(out, n_workgroups, iters, vary_operands, stream=None):
+    """Ceiling probe: n_workgroups x 4 waves x iters x 16 bf16 MFMAs of 16384 flop."""
+    _need(out, F32T, "out", 1)
+    if out.numel() < n_workgroups * 256:
+        raise ValueError("out needs n_workgroups * 256 floats")
+    _check(_lib.dit_probe_mfma(_p(out), n_workgroups, iters, 1 if vary_operands else 0, _stream(stream)))
+    return out
 
 
 class Stack:
@@ -436,6 +460,12 @@ class Stack:
             mask |= 1 << self.KERNELS.index(k)
         _check(_lib.dit_stack_set_probe(self.handle, mask))
         self._probe = tuple(kernels)
+
+    def graph_info(self):
+        """(kernel nodes, all nodes) of the captured graph."""
+        k, n = ctypes.c_int(), ctypes.c_int()
+        _check(_lib.dit_stack_graph_info(self.handle, ctypes.byref(k), ctypes.byref(n)))
+        return k.value, n.value
 
     def probe_ms(self, n_blocks):
         """{kernel: [mean ms per block]} over the probed steps since the previous

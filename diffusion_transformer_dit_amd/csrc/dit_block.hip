@@ -168,8 +168,8 @@ int enqueue_block(const Dims& D, const dit_block_config* cfg, const dit_block_we
   if (dit::linear1_fuses_qk(D.S, D.d, D.mlp, D.Dh)) {
     // the q/k RMSNorm + RoPE runs in linear1's epilogue (kernel 3 is empty)
     DIT_CHECK_HIP(pre(2), "probe");
-    DIT_CHECK_HIP(dit::launch_linear1_qk(u, w->w1, w->b1, qkv, cat, D.S, D.d, D.mlp, w->q_norm_w, w->k_norm_w,
-                                         rcos, rsin, cfg->qk_eps, st), "linear1_qk");
+    DIT_CHECK_HIP(dit::launch_linear1_qk(u, w->w1, w->b1, qkv, cat, D.S, D.d, D.mlp, D.Dh, w->q_norm_w,
+                                         w->k_norm_w, rcos, rsin, cfg->qk_eps, st), "linear1_qk");
     DIT_CHECK_HIP(post(2), "probe");
     DIT_CHECK_HIP(pre(3), "probe");
     DIT_CHECK_HIP(post(3), "probe");
@@ -261,7 +261,7 @@ int enqueue_mmdit(const Dims& D, int T, const dit_block_config* cfg, const dit_s
                             cfg->qk_eps};
   }
   if (dit::bias_act_fuses_qk(qa, n, D.Dh)) {
-    DIT_CHECK_HIP(dit::launch_bias_act_qk_group(qa, qn, n, st), "qkv_qk");
+    DIT_CHECK_HIP(dit::launch_bias_act_qk_group(qa, qn, n, D.Dh, st), "qkv_qk");
   } else {
     DIT_CHECK_HIP(dit::launch_bias_act_group(qa, n, st), "qkv");
     for (int i = 0; i < n; ++i)
@@ -545,11 +545,10 @@ struct dit_stack {
   int probe_blocks = 0;
   long long probe_replays = 0;         // probed graph launches since the last read
   int wall_khz = 0;                    // device wall-clock rate
-  unsigned long long* probe_buf = nullptr;  // device [n_blocks][kProbeChannels][2]
-  // modulation of every block in one launch per block kind: device tables
-  // of the W_mod / b_mod pointers and the vectors (two-stream blocks first)
-  const dit_bf16** mod_ptrs = nullptr;
-  float* mods = nullptr;
+  unsigned long long* probe_buf = nullptr;  // in the caller's workspace: [n_blocks][kProbeChannels][2]
+  // host copy of the table of the blocks' W_mod / b_mod pointers (two-stream
+  // blocks first), staged into the caller's workspace before every replay
+  std::vector<const dit_bf16*> mod_tab;
 };
 
 namespace {
@@ -566,20 +565,32 @@ struct StackPlan {
 
 // Workspace of a stack: the per-block scratch (the larger of the two block
 // kinds when the plan has two-stream blocks), then the activation carried
-// from block to block and the staged temb.
+// from block to block, the staged temb, every block's modulation vectors
+// (two-stream blocks' present streams first, 6d floats each, then 3d per
+// single-stream block), the table of their W_mod / b_mod pointers and the
+// timing-probe counters of the single-stream blocks.
 struct StackWs {
-  size_t xbuf, tbuf, end;
+  size_t xbuf, tbuf, mods, tab, probe, end;
+  int n_streams, n_dm, n_mats;
 };
 
-StackWs stack_ws(const Dims& D, bool mixed) {
+StackWs stack_ws(const Dims& D, int64_t T, int n_double, int n_single) {
+  const bool mixed = n_double > 0;
   size_t o = layout(D).block_end;
   if (mixed) o = std::max(o, mm_layout(D).end);
   StackWs W;
-  W.xbuf = o; o = align256(o + size_t(D.S) * D.d * 2);
-  W.tbuf = o; o = align256(o + size_t(D.tdim) * 2);
+  W.n_streams = mixed ? int(T > 0) + int(T < D.S) : 0;
+  W.n_dm = n_double * W.n_streams;
+  W.n_mats = W.n_dm + n_single;
+  W.xbuf = o;  o = align256(o + size_t(D.S) * D.d * 2);
+  W.tbuf = o;  o = align256(o + size_t(D.tdim) * 2);
+  W.mods = o;  o = align256(o + (size_t(W.n_dm) * 6 * D.d + size_t(n_single) * 3 * D.d) * sizeof(float));
+  W.tab = o;   o = align256(o + size_t(2) * W.n_mats * sizeof(void*));
+  W.probe = o; o = align256(o + size_t(n_single) * kProbeChannels * 2 * sizeof(unsigned long long));
   W.end = o;
   return W;
 }
+StackWs stack_ws(const Dims& D, const StackPlan& P) { return stack_ws(D, P.T, P.n_double, P.n_single); }
 
 std::vector<uintptr_t> make_key(const dit_block_config* cfg, const StackPlan& P, const dit_bf16* x_in,
                                 const float* rcos, const float* rsin, void* ws, size_t ws_bytes, uint32_t probe_mask) {
@@ -636,9 +647,6 @@ extern "C" int dit_stack_create(dit_stack** out) {
 
 extern "C" int dit_stack_destroy(dit_stack* st) {
   if (!st) return DIT_OK;
-  if (st->probe_buf) (void)hipFree(st->probe_buf);
-  if (st->mod_ptrs) (void)hipFree(st->mod_ptrs);
-  if (st->mods) (void)hipFree(st->mods);
   if (st->exec) (void)hipGraphExecDestroy(st->exec);
   if (st->graph) (void)hipGraphDestroy(st->graph);
   if (st->cap) (void)hipStreamDestroy(st->cap);
@@ -646,16 +654,18 @@ extern "C" int dit_stack_destroy(dit_stack* st) {
   return DIT_OK;
 }
 
-extern "C" size_t dit_stack_workspace_bytes(const dit_block_config* cfg) {
+extern "C" size_t dit_stack_workspace_bytes(const dit_block_config* cfg, int n_blocks) {
   Dims D;
-  if (dims_of(cfg, &D)) return 0;
-  return stack_ws(D, false).end;
+  if (dims_of(cfg, &D) || n_blocks <= 0) return 0;
+  return stack_ws(D, 0, 0, n_blocks).end;
 }
 
-extern "C" size_t dit_stack_mixed_workspace_bytes(const dit_block_config* cfg) {
+extern "C" size_t dit_stack_mixed_workspace_bytes(const dit_block_config* cfg, int64_t txt_len, int n_double,
+                                                  int n_single) {
   Dims D;
-  if (dims_of(cfg, &D)) return 0;
-  return stack_ws(D, true).end;
+  if (dims_of(cfg, &D) || n_double < 0 || n_single < 0 || n_double + n_single <= 0) return 0;
+  if (n_double > 0 && (txt_len < 0 || txt_len > D.S)) return 0;
+  return stack_ws(D, n_double > 0 ? txt_len : 0, n_double, n_single).end;
 }
 
 namespace {
@@ -685,7 +695,7 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
   }
   if (!x_in || !temb_steps || !rope_cos || !rope_sin || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
   if ((rc = check_aligned({x_in, temb_steps, rope_cos, rope_sin, out}))) return rc;
-  const StackWs W = stack_ws(D, P.n_double > 0);
+  const StackWs W = stack_ws(D, P);
   if (!workspace || ws_bytes < W.end) return fail(DIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, W.end);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(DIT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (st->probe_mask && P.n_double > 0)
@@ -710,20 +720,20 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
     DIT_CHECK_HIP(hipDeviceGetAttribute(&st->wall_khz, hipDeviceAttributeWallClockRate, dev),
                   "hipDeviceGetAttribute");
     if (st->wall_khz <= 0) return fail(DIT_ERR_HIP, "device reports no wall-clock rate");
-    const size_t bytes = size_t(P.n_single) * kProbeChannels * 2 * sizeof(unsigned long long);
-    if (st->probe_buf) (void)hipFree(st->probe_buf);
-    st->probe_buf = nullptr;
-    DIT_CHECK_HIP(hipMalloc(&st->probe_buf, bytes), "hipMalloc");
-    DIT_CHECK_HIP(hipMemset(st->probe_buf, 0, bytes), "hipMemset");
+    st->probe_buf = reinterpret_cast<unsigned long long*>(ws + W.probe);
+    DIT_CHECK_HIP(hipMemsetAsync(st->probe_buf, 0,
+                                 size_t(P.n_single) * kProbeChannels * 2 * sizeof(unsigned long long), s),
+                  "hipMemsetAsync");
     st->probe_blocks = P.n_single;
     st->probe_replays = 0;
   }
   // Every block's modulation depends on temb only: one launch per block kind
-  // computes them all at the start of the step.  Tables: W_mod pointers of
+  // computes them all at the start of the step.  Table: W_mod pointers of
   // the two-stream blocks' present streams (text first), then of the
   // single-stream blocks; the b_mod pointers after them in the same order.
-  const int n_streams = (P.n_double > 0) ? int(P.T > 0) + int(P.T < D.S) : 0;
-  const int n_dm = P.n_double * n_streams, n_mats = n_dm + P.n_single;
+  // Its host copy stays with the stack; run_steps stages it into the
+  // workspace on the caller's stream before the steps of every replay.
+  const int n_dm = W.n_dm, n_mats = W.n_mats;
   std::vector<const dit_bf16*> tab(2 * size_t(n_mats));
   for (int b = 0, m = 0; b < P.n_double; ++b) {
     if (P.T > 0) tab[m] = P.txt[b].w_mod, tab[n_mats + m] = P.txt[b].b_mod, ++m;
@@ -731,30 +741,23 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
   }
   for (int b = 0; b < P.n_single; ++b)
     tab[n_dm + b] = P.singles[b].w_mod, tab[n_mats + n_dm + b] = P.singles[b].b_mod;
-  const size_t n_mod = size_t(n_dm) * 6 * D.d + size_t(P.n_single) * 3 * D.d;
-  if (st->mod_ptrs) (void)hipFree(st->mod_ptrs);
-  if (st->mods) (void)hipFree(st->mods);
-  st->mod_ptrs = nullptr;
-  st->mods = nullptr;
-  DIT_CHECK_HIP(hipMalloc(reinterpret_cast<void**>(&st->mod_ptrs), tab.size() * sizeof(void*)), "hipMalloc");
-  DIT_CHECK_HIP(hipMemcpy(st->mod_ptrs, tab.data(), tab.size() * sizeof(void*), hipMemcpyHostToDevice), "hipMemcpy");
-  DIT_CHECK_HIP(hipMalloc(reinterpret_cast<void**>(&st->mods), n_mod * sizeof(float)), "hipMalloc");
-  float* mods_d = st->mods;                                  // [n_dm][6d]
-  float* mods_s = st->mods + size_t(n_dm) * 6 * D.d;         // [n_single][3d]
+  const dit_bf16** mod_ptrs = reinterpret_cast<const dit_bf16**>(ws + W.tab);
+  float* mods_d = reinterpret_cast<float*>(ws + W.mods);     // [n_dm][6d]
+  float* mods_s = mods_d + size_t(n_dm) * 6 * D.d;           // [n_single][3d]
+  const int n_streams = W.n_streams;
 
   DIT_CHECK_HIP(hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
   int brc = DIT_OK;
   hipError_t me = hipSuccess;
   if (n_dm > 0)
-    me = dit::launch_modulation_multi(tbuf, st->mod_ptrs, st->mod_ptrs + n_mats, mods_d, n_dm, 6 * D.d, D.tdim,
-                                      st->cap);
+    me = dit::launch_modulation_multi(tbuf, mod_ptrs, mod_ptrs + n_mats, mods_d, n_dm, 6 * D.d, D.tdim, st->cap);
   if (me == hipSuccess && P.n_single > 0) {
     // probes: kernel 0 of block 0 brackets the whole batched launch
     const bool pb = (st->probe_mask & 1u) != 0;
     if (pb) me = dit::launch_probe_stamp(st->probe_buf, 0, st->cap);
     if (me == hipSuccess)
-      me = dit::launch_modulation_multi(tbuf, st->mod_ptrs + n_dm, st->mod_ptrs + n_mats + n_dm, mods_s,
-                                        P.n_single, 3 * D.d, D.tdim, st->cap);
+      me = dit::launch_modulation_multi(tbuf, mod_ptrs + n_dm, mod_ptrs + n_mats + n_dm, mods_s, P.n_single,
+                                        3 * D.d, D.tdim, st->cap);
     if (me == hipSuccess && pb) me = dit::launch_probe_stamp(st->probe_buf, 1, st->cap);
   }
   if (me != hipSuccess) brc = hip_fail(me, "modulation");
@@ -790,6 +793,7 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
   st->graph = g;
   st->exec = ex;
   st->key = key;
+  st->mod_tab = std::move(tab);
   return DIT_OK;
 }
 
@@ -814,13 +818,18 @@ int check_schedule(int n_steps, const uint8_t* fresh, const float* t_steps) {
 // computed outputs by a first-order finite difference in t (a copy of the
 // last one while only one exists).  With chain, the step's result is also
 // the next step's input.
-int run_steps(dit_stack* st, const Dims& D, bool chain, bool mixed, const dit_bf16* x_in, const dit_bf16* temb_steps,
-              int n_steps, dit_bf16* out, unsigned char* ws, const uint8_t* fresh, const float* t_steps,
-              hipStream_t s) {
-  const StackWs W = stack_ws(D, mixed);
+int run_steps(dit_stack* st, const Dims& D, bool chain, const StackPlan& P, const dit_bf16* x_in,
+              const dit_bf16* temb_steps, int n_steps, dit_bf16* out, unsigned char* ws, const uint8_t* fresh,
+              const float* t_steps, hipStream_t s) {
+  const StackWs W = stack_ws(D, P);
   dit_bf16* xbuf = reinterpret_cast<dit_bf16*>(ws + W.xbuf);
   dit_bf16* tbuf = reinterpret_cast<dit_bf16*>(ws + W.tbuf);
   const size_t act = size_t(D.S) * D.d;
+  // the modulation weight table the graph reads (a few bytes per block): the
+  // host copy lives as long as the stack, so the copy may run asynchronously
+  if (n_steps > 0 && !st->mod_tab.empty())
+    DIT_CHECK_HIP(hipMemcpyAsync(ws + W.tab, st->mod_tab.data(), st->mod_tab.size() * sizeof(void*),
+                                 hipMemcpyHostToDevice, s), "stage modulation table");
   int fa = -1, fb = -1;  // the last two computed steps
   auto tt = [&](int i) { return t_steps ? double(t_steps[i]) : double(i); };
   for (int step = 0; step < n_steps; ++step) {
@@ -853,7 +862,7 @@ int replay_plan(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
   Dims D;
   if ((rc = stack_setup(st, cfg, P, x_in, temb_steps, n_steps, rope_cos, rope_sin, out, workspace, ws_bytes, s, &D)))
     return rc;
-  return run_steps(st, D, (cfg->flags & DIT_STACK_CHAIN) != 0, P.n_double > 0, x_in, temb_steps, n_steps, out,
+  return run_steps(st, D, (cfg->flags & DIT_STACK_CHAIN) != 0, P, x_in, temb_steps, n_steps, out,
                    static_cast<unsigned char*>(workspace), fresh, t_steps, s);
 }
 }  // namespace
@@ -929,6 +938,46 @@ extern "C" int dit_stack_probe_ms(dit_stack* st, float* ms, int n_blocks) {
       ms[size_t(b) * 6 + k] =
           (st->probe_mask >> k & 1u) ? float((double(c[2 * k + 1]) - overhead) * per_tick_ms) : -1.f;
   }
+  return DIT_OK;
+}
+
+extern "C" int dit_stack_graph_info(dit_stack* st, int* n_kernel_nodes, int* n_nodes) {
+  if (!st || !n_kernel_nodes || !n_nodes) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if (!st->graph) return fail(DIT_ERR_INVALID_ARG, "the stack has not been captured yet");
+  size_t n = 0;
+  DIT_CHECK_HIP(hipGraphGetNodes(st->graph, nullptr, &n), "hipGraphGetNodes");
+  std::vector<hipGraphNode_t> nodes(n);
+  if (n) DIT_CHECK_HIP(hipGraphGetNodes(st->graph, nodes.data(), &n), "hipGraphGetNodes");
+  int k = 0;
+  for (size_t i = 0; i < n; ++i) {
+    hipGraphNodeType t;
+    DIT_CHECK_HIP(hipGraphNodeGetType(nodes[i], &t), "hipGraphNodeGetType");
+    if (t == hipGraphNodeTypeKernel) ++k;
+  }
+  *n_kernel_nodes = k;
+  *n_nodes = int(n);
+  return DIT_OK;
+}
+
+// ============================================================== ceiling probes
+extern "C" int dit_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return DIT_OK;
+  if (!src || !dst) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if (bytes % 16 != 0) return fail(DIT_ERR_INVALID_ARG, "bytes=%zu must be a multiple of 16", bytes);
+  if (int rc = check_aligned({src, dst})) return rc;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) return fail(DIT_ERR_INVALID_ARG, "src and dst overlap");
+  DIT_CHECK_HIP(dit::launch_probe_copy(src, dst, bytes, as_stream(stream)), "probe_copy");
+  return DIT_OK;
+}
+
+extern "C" int dit_probe_mfma(float* out, int64_t n_workgroups, int64_t iters, int32_t vary_operands, void* stream) {
+  if (!out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if (n_workgroups < 1 || n_workgroups > (1 << 20) || iters < 1 || iters > (1 << 24))
+    return fail(DIT_ERR_INVALID_ARG, "n_workgroups=%lld iters=%lld", (long long)n_workgroups, (long long)iters);
+  if (int rc = check_aligned({out})) return rc;
+  DIT_CHECK_HIP(dit::launch_probe_mfma(out, int(n_workgroups), int(iters), vary_operands ? 1 : 0, as_stream(stream)),
+                "probe_mfma");
   return DIT_OK;
 }
 

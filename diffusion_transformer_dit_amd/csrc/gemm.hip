@@ -127,9 +127,11 @@ struct EpiLinear1 {
 };
 
 // linear1 whose q and k columns also get the per-head RMSNorm (weights qw,
-// kw over the 128 dims of a head) and the RoPE rotation of adjacent dim
-// pairs (tables [S, 64]) before they are stored: the whole head of a row is
-// in one wave when the wave owns 128 columns (the 256x256 tile).
+// kw over the head_dim dims of a head) and the RoPE rotation of adjacent dim
+// pairs (tables [S, head_dim/2]) before they are stored, so q and k are
+// rounded to bf16 once, after both: a wave that owns 128 columns (the tiles
+// with WN == 128) holds whole heads of every row it covers, one head of 128
+// or two of 64.
 struct EpiLinear1QK : EpiLinear1 {
   static constexpr bool kHeadNorm = true;
   const float* qw;
@@ -137,17 +139,23 @@ struct EpiLinear1QK : EpiLinear1 {
   const float* rcos;
   const float* rsin;
   float eps;
-  // Rows row_base + 16 i (i < FM) of the 128-column head starting at column
-  // colw (< 2d); lane columns 4*fk + 16 j + (0..3) of block j.
+  int head_dim;  // 64 or 128
+  // Rows row_base + 16 i (i < FM) of the 128 columns starting at colw (<
+  // 2d, a multiple of 64); lane columns 4*fk + 16 j + (0..3) of block j.
+  // With head_dim 64, blocks j < 4 and j >= 4 are two heads; the q | k
+  // boundary (column d) may fall between them.
   template <int FM, int FN>
   __device__ __forceinline__ void store_head(int row_base, int colw, int fk, const f32x4 (&acc)[FM][FN]) const {
-    static_assert(FN == 8, "one head of 128 columns per wave");
-    const float* w = colw < d ? qw : kw;
+    static_assert(FN == 8, "128 columns per wave");
+    const int hm = head_dim - 1;       // column inside the head = c & hm
+    const int half = head_dim >> 1;    // RoPE table row length
+    const float inv_hd = head_dim == 128 ? (1.0f / 128.0f) : (1.0f / 64.0f);
     f32x4 wv[FN], bv[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int c = j * 16 + 4 * fk;  // column inside the head
-      wv[j] = *reinterpret_cast<const f32x4*>(w + c);
+      const int c = j * 16 + 4 * fk;  // column inside the wave's 128
+      const float* w = colw + c < d ? qw : kw;
+      wv[j] = *reinterpret_cast<const f32x4*>(w + (c & hm));
       bv[j] = bias ? load_bf4(bias + colw + c) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
@@ -155,22 +163,31 @@ struct EpiLinear1QK : EpiLinear1 {
       const int row = row_base + 16 * i;
       const int rc = min(row, M - 1);
       f32x4 z[FN];
-      float ss = 0.f;
+      float s0 = 0.f, s1 = 0.f;  // sums of squares over blocks 0..3 and 4..7
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         z[j] = acc[i][j] + bv[j];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ss = fmaf(z[j][e], z[j][e], ss);
+        for (int e = 0; e < 4; ++e) {
+          if (j < 4) s0 = fmaf(z[j][e], z[j][e], s0);
+          else s1 = fmaf(z[j][e], z[j][e], s1);
+        }
       }
-      // the row's 128 values sit in lanes fr + 16 fk, fk = 0..3
-      ss += __shfl_xor(ss, 16, 64);
-      ss += __shfl_xor(ss, 32, 64);
-      const float r = __frsqrt_rn(ss * (1.0f / 128.0f) + eps);
+      // a row's 128 values sit in lanes fr + 16 fk, fk = 0..3
+      s0 += __shfl_xor(s0, 16, 64);
+      s0 += __shfl_xor(s0, 32, 64);
+      s1 += __shfl_xor(s1, 16, 64);
+      s1 += __shfl_xor(s1, 32, 64);
+      if (head_dim == 128) s0 = s1 = s0 + s1;
+      const float r0 = __frsqrt_rn(s0 * inv_hd + eps);
+      const float r1 = __frsqrt_rn(s1 * inv_hd + eps);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int c = j * 16 + 4 * fk;
-        const f32x2 cs = *reinterpret_cast<const f32x2*>(rcos + size_t(rc) * 64 + c / 2);
-        const f32x2 sn = *reinterpret_cast<const f32x2*>(rsin + size_t(rc) * 64 + c / 2);
+        const int ch = c & hm;  // column inside the head
+        const float r = j < 4 ? r0 : r1;
+        const f32x2 cs = *reinterpret_cast<const f32x2*>(rcos + size_t(rc) * half + ch / 2);
+        const f32x2 sn = *reinterpret_cast<const f32x2*>(rsin + size_t(rc) * half + ch / 2);
         f32x4 n;
 #pragma unroll
         for (int e = 0; e < 4; ++e) n[e] = z[j][e] * r * wv[j][e];
@@ -436,6 +453,7 @@ gemm_bf16_tn_kernel(GemmGroup<Epi, NP> grp) {
 // ------------------------------------------------------------------ tile choice
 using T288x192 = TileCfg<288, 192, 2, 4, 4>;  // 8 waves of 144 x 48; groups own 144-row halves
 using T256 = TileCfg<256, 256, 4, 2, 4>;      // 8 waves of 64 x 128; groups own 128-row halves
+using T128x256 = TileCfg<128, 256, 4, 2, 4>;  // 8 waves of 32 x 128 (whole heads per wave, small M)
 using T128 = TileCfg<128, 128, 4, 2, 4>;      // 8 waves of 32 x 64
 
 int num_cus() {
@@ -452,20 +470,23 @@ int num_cus() {
 
 void prepare_device() { (void)num_cus(); }
 
-enum TileKind { K288x192 = 0, K256 = 1, K128 = 2 };
+enum TileKind { K288x192 = 0, K256 = 1, K128 = 2, K128x256 = 3 };
 
 // Pick the tile that minimises rounds-of-workgroups x tile area / efficiency
 // (a proxy for the time of the busiest CU) over the tiles of all problems of
-// one launch.
-static TileKind choose_tile(const int* Ms, const int* Ns, int np) {
+// one launch.  head_tiles restricts the choice to the tiles whose waves own
+// 128 columns (whole heads: the fused q/k RMSNorm + RoPE epilogue).
+static TileKind choose_tile(const int* Ms, const int* Ns, int np, bool head_tiles = false) {
   const int cus = num_cus();
-  struct Opt { TileKind k; int bm, bn; double eff; } opts[] = {
+  struct Opt { TileKind k; int bm, bn; double eff; bool heads; } opts[] = {
       // per-tile efficiency measured at the Flux shape (288x192 waves hold a
       // thinner 144 x 48 sub-tile and run at 0.87 of the 256x256 rate)
-      {K288x192, 288, 192, 0.87}, {K256, 256, 256, 1.0}, {K128, 128, 128, 0.6}};
-  TileKind best = K128;
+      {K288x192, 288, 192, 0.87, false}, {K256, 256, 256, 1.0, true}, {K128, 128, 128, 0.6, false},
+      {K128x256, 128, 256, 0.75, true}};
+  TileKind best = head_tiles ? K128x256 : K128;
   double best_cost = 1e300;
   for (const Opt& o : opts) {
+    if (head_tiles && !o.heads) continue;
     long long tiles = 0;
     for (int i = 0; i < np; ++i) tiles += (long long)((Ms[i] + o.bm - 1) / o.bm) * ((Ns[i] + o.bn - 1) / o.bn);
     const long long rounds = (tiles + cus - 1) / cus;
@@ -547,13 +568,14 @@ hipError_t launch_linear1(const bf16_t* u, const bf16_t* w1, const bf16_t* b1, b
 }
 
 bool linear1_fuses_qk(int S, int d, int mlp, int DH) {
-  return DH == 128 && S > 0 && choose_tile(S, 3 * d + mlp) == K256;
+  (void)mlp;
+  return (DH == 128 || DH == 64) && S > 0 && d % 64 == 0;
 }
 
 hipError_t launch_linear1_qk(const bf16_t* u, const bf16_t* w1, const bf16_t* b1, bf16_t* qkv, bf16_t* cat,
-                             int S, int d, int mlp, const float* qw, const float* kw, const float* rcos,
+                             int S, int d, int mlp, int DH, const float* qw, const float* kw, const float* rcos,
                              const float* rsin, float eps, hipStream_t st) {
-  if (!linear1_fuses_qk(S, d, mlp, 128)) return hipErrorInvalidValue;
+  if (!linear1_fuses_qk(S, d, mlp, DH)) return hipErrorInvalidValue;
   EpiLinear1QK e;
   static_cast<EpiLinear1&>(e) = EpiLinear1{b1, qkv, cat, S, 3 * d + mlp, 3 * d, d, 3 * d, d + mlp, d};
   e.qw = qw;
@@ -561,7 +583,10 @@ hipError_t launch_linear1_qk(const bf16_t* u, const bf16_t* w1, const bf16_t* b1
   e.rcos = rcos;
   e.rsin = rsin;
   e.eps = eps;
-  return launch_tile<T256>(u, w1, S, 3 * d + mlp, d, e, st);
+  e.head_dim = DH;
+  const int N = 3 * d + mlp;
+  if (choose_tile(&S, &N, 1, true) == K256) return launch_tile<T256>(u, w1, S, N, d, e, st);
+  return launch_tile<T128x256>(u, w1, S, N, d, e, st);
 }
 
 hipError_t launch_linear2(const bf16_t* cat, const bf16_t* w2, const bf16_t* b2, const bf16_t* x,
@@ -583,19 +608,16 @@ hipError_t launch_bias_act_group(const BiasActArgs* a, int np, hipStream_t st) {
 }
 
 bool bias_act_fuses_qk(const BiasActArgs* a, int np, int DH) {
-  if (DH != 128 || np < 1 || np > 2) return false;
-  int Ms[2], Ns[2];
-  for (int i = 0; i < np; ++i) {
-    if (a[i].qk_dim % 128 != 0 || 2 * a[i].qk_dim > a[i].n_plain) return false;
-    Ms[i] = a[i].M;
-    Ns[i] = a[i].N;
-  }
-  return choose_tile(Ms, Ns, np) == K256;
+  if ((DH != 128 && DH != 64) || np < 1 || np > 2) return false;
+  for (int i = 0; i < np; ++i)
+    if (a[i].qk_dim % 64 != 0 || 2 * a[i].qk_dim > a[i].n_plain) return false;
+  return true;
 }
 
-hipError_t launch_bias_act_qk_group(const BiasActArgs* a, const QKNormArgs* q, int np, hipStream_t st) {
-  if (!bias_act_fuses_qk(a, np, 128)) return hipErrorInvalidValue;
+hipError_t launch_bias_act_qk_group(const BiasActArgs* a, const QKNormArgs* q, int np, int DH, hipStream_t st) {
+  if (!bias_act_fuses_qk(a, np, DH)) return hipErrorInvalidValue;
   GemmProblem<EpiLinear1QK> ps[2];
+  int Ms[2], Ns[2];
   for (int i = 0; i < np; ++i) {
     EpiLinear1QK e;
     static_cast<EpiLinear1&>(e) = bias_act_epi(a[i]);
@@ -604,9 +626,13 @@ hipError_t launch_bias_act_qk_group(const BiasActArgs* a, const QKNormArgs* q, i
     e.rcos = q[i].rcos;
     e.rsin = q[i].rsin;
     e.eps = q[i].eps;
+    e.head_dim = DH;
     ps[i] = GemmProblem<EpiLinear1QK>{a[i].A, a[i].W, a[i].M, a[i].N, a[i].K, e};
+    Ms[i] = a[i].M;
+    Ns[i] = a[i].N;
   }
-  return launch_tile_group<T256>(ps, np, st);
+  if (choose_tile(Ms, Ns, np, true) == K256) return launch_tile_group<T256>(ps, np, st);
+  return launch_tile_group<T128x256>(ps, np, st);
 }
 
 hipError_t launch_gated_group(const GatedArgs* a, int np, hipStream_t st) {

@@ -41,11 +41,12 @@ hipError_t launch_rope_table(const int32_t* pos, int S, int n_axes, const int32_
 // linear1: z = u W1^T + b1; cols < 3d -> qkv[S,3d]; cols >= 3d -> gelu -> cat[:, d + ...]
 hipError_t launch_linear1(const bf16_t* u, const bf16_t* w1, const bf16_t* b1, bf16_t* qkv,
                           bf16_t* cat, int S, int d, int mlp, hipStream_t st);
-// linear1 with the q/k RMSNorm + RoPE fused into its epilogue; only for the
-// shapes where linear1_fuses_qk() holds (head_dim 128, 256x256 tiles)
+// linear1 with the q/k RMSNorm + RoPE fused into its epilogue (q and k are
+// rounded to bf16 once, after both); for the shapes where linear1_fuses_qk()
+// holds (head_dim 64 or 128, dim % 64 == 0)
 bool linear1_fuses_qk(int S, int d, int mlp, int DH);
 hipError_t launch_linear1_qk(const bf16_t* u, const bf16_t* w1, const bf16_t* b1, bf16_t* qkv, bf16_t* cat,
-                             int S, int d, int mlp, const float* qw, const float* kw, const float* rcos,
+                             int S, int d, int mlp, int DH, const float* qw, const float* kw, const float* rcos,
                              const float* rsin, float eps, hipStream_t st);
 // linear2: y = x + gate * (cat W2^T + b2)
 hipError_t launch_linear2(const bf16_t* cat, const bf16_t* w2, const bf16_t* b2, const bf16_t* x,
@@ -65,7 +66,7 @@ struct BiasActArgs {
   bf16_t* gelu;
   int ld_gelu, gelu_col0, qk_dim;
 };
-// per-head RMSNorm + RoPE of the q and k columns (tables [M, 64] for these rows)
+// per-head RMSNorm + RoPE of the q and k columns (tables [M, head_dim/2] for these rows)
 struct QKNormArgs {
   const float* qw;
   const float* kw;
@@ -85,7 +86,7 @@ struct GatedArgs {
 };
 hipError_t launch_bias_act_group(const BiasActArgs* a, int np, hipStream_t st);
 bool bias_act_fuses_qk(const BiasActArgs* a, int np, int DH);
-hipError_t launch_bias_act_qk_group(const BiasActArgs* a, const QKNormArgs* q, int np, hipStream_t st);
+hipError_t launch_bias_act_qk_group(const BiasActArgs* a, const QKNormArgs* q, int np, int DH, hipStream_t st);
 hipError_t launch_gated_group(const GatedArgs* a, int np, hipStream_t st);
 // the same with an fp32 output y32[i] [M, N] (a[i].y unused) ...
 hipError_t launch_gated_f32out_group(const GatedArgs* a, float* const* y32, int np, hipStream_t st);
@@ -114,5 +115,10 @@ hipError_t launch_extrapolate(const bf16_t* a, const bf16_t* b, float w, bf16_t*
 
 // timing probe channel ch[2]: finish == 0 stamps ch[0], else ch[1] += now - ch[0]
 hipError_t launch_probe_stamp(unsigned long long* ch, int finish, hipStream_t st);
+
+// ceiling probes: a streaming copy of `bytes` (a multiple of 16) and
+// n_workgroups x 4 waves x iters x 16 bf16 MFMAs (out: n_workgroups*256 floats)
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+hipError_t launch_probe_mfma(float* out, int n_workgroups, int iters, int vary, hipStream_t st);
 
 }  // namespace dit

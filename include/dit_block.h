@@ -19,12 +19,18 @@
  *     the HIP or PyTorch allocators is); others give DIT_ERR_INVALID_ARG.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on `stream` and returns; none
- *     synchronises the host, and none allocates device memory, with two
- *     exceptions: the first replay of a stack (its capture) allocates the
- *     stack's own small buffers and copies a table of weight pointers to
- *     the device synchronously, and dit_stack_probe_ms synchronises the
- *     device.  The caller owns every other buffer, the workspace and the
- *     stream.
+ *     synchronises the host or allocates device memory.  The caller owns
+ *     every buffer, the workspace and the stream.  The one exception is a
+ *     block stack: it owns its captured graph (whose instantiation the HIP
+ *     runtime backs with memory of its own) and the stream it captures on;
+ *     everything the graph reads or writes lives in the caller's workspace.
+ *     dit_stack_probe_ms (a diagnostic) synchronises the device.
+ *   - The single-call entry points (everything except the stack replays)
+ *     may be captured by the caller into its own graph: they enqueue only
+ *     kernel launches on `stream` (the capture rules of the Flux page,
+ *     section 1.2: no allocation and no host synchronisation inside a
+ *     captured region).  A stack replay launches a graph of its own and
+ *     returns DIT_ERR_CAPTURE on a capturing stream.
  *   - Every call returns DIT_OK (0) or an error code.  Arguments are checked
  *     before any HIP call; on error nothing is enqueued and dit_last_error()
  *     returns a message (thread-local).  HIP launch failures give DIT_ERR_HIP.
@@ -100,8 +106,12 @@ int dit_modulation(const dit_bf16* temb, const dit_bf16* w_mod, const dit_bf16* 
 int dit_modulate_norm(const dit_bf16* x, const float* shift, const float* scale,
                       dit_bf16* out, int64_t rows, int64_t cols, float eps, void* stream);
 
-/* Gated residual: y[r,c] = x[r,c] + gate[c] * h[r,c]; x, h, y [rows, cols]
- * bf16 (y may equal x or h); gate [cols] fp32.  cols % 8 == 0, cols <= 8192. */
+/* Gated residual, the last step of the block's adaLN tail (the Flux page,
+ * section 1.1, counts it among the elementwise ops between the GEMMs that
+ * compilation fuses): y[r,c] = x[r,c] + gate[c] * h[r,c]; x, h, y [rows,
+ * cols] bf16 (y may equal x or h); gate [cols] fp32, the third modulation
+ * vector.  fp32 arithmetic, one bf16 rounding at the store.  cols % 8 == 0,
+ * cols <= 8192. */
 int dit_gated_residual(const dit_bf16* x, const dit_bf16* h, const float* gate,
                        dit_bf16* y, int64_t rows, int64_t cols, void* stream);
 
@@ -184,15 +194,33 @@ int dit_rope_table(const int32_t* positions, int64_t seq_len, int32_t n_axes,
 
 /* ---- whole block --------------------------------------------------------- */
 
-/* Bytes of workspace dit_block_forward needs (0 on an invalid config). */
+/* Bytes of workspace dit_block_forward needs (0 on an invalid config):
+ * fp32 modulation vectors [3d], then bf16 u [S, d], q|k|v [S, 3d] and the
+ * concat buffer [S, d + mlp] (attention output | GELU output), each section
+ * 256-byte aligned; 255 MB at the Flux shape of the page "ChituDiffusion:
+ * torch.compile and CUDA Graph on Flux.1-dev", section 2 (S = 4608,
+ * d = 3072, MLP 12288). */
 size_t dit_block_workspace_bytes(const dit_block_config* cfg);
 
-/* One block forward: modulation GEMV, LayerNorm+modulate, linear1+GELU,
- * QK RMSNorm+RoPE, attention, linear2+gated residual; six launches on
- * `stream`.  x, y [S, d] bf16 (y may equal x: the block then runs in place);
+/* One Flux single-stream block forward (the block profiled in section 2 of
+ * the Flux page above; its adaLN modulation, LayerNorm and GELU are the ops
+ * of section 1.1, RoPE the complex rotation of section 3.1, attention the
+ * exact flash / sdpa attention of sections 2 and 4):
+ *   shift|scale|gate = W_mod SiLU(temb) + b_mod
+ *   u = LN(x)(1 + scale) + shift
+ *   q|k|v|g = u W1^T + b1;  q, k <- per-head RMSNorm, then RoPE
+ *   o = softmax(q k^T / sqrt(Dh)) v per head
+ *   y = x + gate * ([o | GELU_tanh(g)] W2^T + b2)
+ * Five launches on `stream`: modulation, LayerNorm+modulate, linear1 (whose
+ * epilogue also does the q/k RMSNorm + RoPE, so q and k are rounded to bf16
+ * once), attention, linear2 with the gated residual.
+ * x, y [S, d] bf16 (y may equal x: the block then runs in place);
  * temb [temb_dim] bf16; rope_cos/sin [S, head_dim/2] fp32; workspace is a
  * device buffer of at least dit_block_workspace_bytes(cfg) bytes, 256-byte
- * aligned. */
+ * aligned, owned by the caller and overwritten (it must not overlap x or y).
+ * Errors: DIT_ERR_INVALID_ARG (NULL or misaligned pointer, bad config),
+ * DIT_ERR_UNSUPPORTED (shape), DIT_ERR_WORKSPACE (missing, small or
+ * misaligned workspace), DIT_ERR_HIP (launch failure). */
 int dit_block_forward(const dit_block_config* cfg, const dit_block_weights* w,
                       const dit_bf16* x, const dit_bf16* temb, const float* rope_cos,
                       const float* rope_sin, dit_bf16* y, void* workspace, size_t ws_bytes,
@@ -255,18 +283,21 @@ int dit_sequential_block_forward(const dit_block_config* cfg, const dit_stream_w
 
 /* ---- block stack replayed over denoising steps --------------------------- */
 
-/* opaque: owns the captured graph, its capture stream and, from the
- * capture on, two small device buffers: the table of the blocks' W_mod /
- * b_mod pointers and the blocks' modulation vectors (3d floats per
- * single-stream block, 6d per stream of a two-stream block), which the
- * graph computes in one launch per block kind at the start of every step */
+/* opaque: owns the captured graph, its capture stream and a host copy of
+ * the table of the blocks' W_mod / b_mod pointers.  Everything the graph
+ * reads or writes is in the caller's workspace: the per-block scratch, the
+ * activation carried from block to block, the staged temb, every block's
+ * modulation vectors (computed in one launch per block kind at the start of
+ * every step), the pointer table (staged with an asynchronous copy on the
+ * caller's stream at every replay call) and the timing-probe counters. */
 typedef struct dit_stack dit_stack;
 
 int dit_stack_create(dit_stack** out);
 int dit_stack_destroy(dit_stack* st);
 
-/* Bytes of workspace dit_stack_replay needs (0 on an invalid config). */
-size_t dit_stack_workspace_bytes(const dit_block_config* cfg);
+/* Bytes of workspace dit_stack_replay and dit_stack_replay_cached need for
+ * a stack of n_blocks single-stream blocks (0 on an invalid config). */
+size_t dit_stack_workspace_bytes(const dit_block_config* cfg, int n_blocks);
 
 /* Runs n_steps denoising steps of the n_blocks-block stack: step s feeds
  * x_in (or, with DIT_STACK_CHAIN, step s-1's output) through blocks
@@ -274,9 +305,15 @@ size_t dit_stack_workspace_bytes(const dit_block_config* cfg);
  * sequence is captured once as a hipGraph on the first call and replayed
  * once per step (capture-once / replay-many, Flux page sections 1.2-1.3).
  * blocks: HOST array [n_blocks] of device weight pointers; temb_steps
- * [n_steps, temb_dim]; out [n_steps, S, d].  The graph is keyed by the
- * config, every pointer and n_blocks; a later call with another key returns
- * DIT_ERR_GRAPH_KEY (destroy and re-create the stack to re-capture). */
+ * [n_steps, temb_dim]; out [n_steps, S, d]; workspace of at least
+ * dit_stack_workspace_bytes(cfg, n_blocks) bytes, 256-byte aligned, which
+ * the replay overwrites.  The graph is keyed by the config, every pointer
+ * (the workspace's included) and n_blocks; a later call with another key
+ * returns DIT_ERR_GRAPH_KEY and enqueues nothing (destroy and re-create the
+ * stack to re-capture: the Wan2.1 video page, section 5.2, warns that a
+ * shape change needs a new capture).  On a capturing stream: DIT_ERR_CAPTURE.
+ * The first call captures on the stack's own stream (graph instantiation
+ * allocates the runtime's own memory for the graph). */
 int dit_stack_replay(dit_stack* st, const dit_block_config* cfg, const dit_block_weights* blocks,
                      int n_blocks, const dit_bf16* x_in, const dit_bf16* temb_steps,
                      int n_steps, const float* rope_cos, const float* rope_sin, dit_bf16* out,
@@ -301,8 +338,10 @@ int dit_stack_replay_cached(dit_stack* st, const dit_block_config* cfg, const di
                             const float* rope_cos, const float* rope_sin, dit_bf16* out, void* workspace,
                             size_t ws_bytes, const uint8_t* fresh, const float* t_steps, void* stream);
 
-/* Bytes of workspace dit_stack_replay_mixed needs (0 on an invalid config). */
-size_t dit_stack_mixed_workspace_bytes(const dit_block_config* cfg);
+/* Bytes of workspace dit_stack_replay_mixed needs for n_double two-stream
+ * blocks with txt_len text tokens and n_single single-stream blocks (0 on
+ * an invalid config). */
+size_t dit_stack_mixed_workspace_bytes(const dit_block_config* cfg, int64_t txt_len, int n_double, int n_single);
 
 /* A Flux-style stack: n_double two-stream blocks (text rows [0, txt_len),
  * weights txt[b] and img[b], HOST arrays of n_double) followed by n_single
@@ -346,6 +385,26 @@ int dit_stack_set_probe(dit_stack* st, uint32_t kernel_mask);
  * n_blocks must match the captured stack.  No probed step since the last
  * read, or a mismatched n_blocks -> DIT_ERR_INVALID_ARG. */
 int dit_stack_probe_ms(dit_stack* st, float* ms, int n_blocks);
+
+/* Structure of the captured graph: the number of kernel nodes and of all
+ * nodes (the Flux page, sections 2 and 3.2, counts the kernels of one block
+ * forward: 52 eager, 12 compiled).  Before the first replay:
+ * DIT_ERR_INVALID_ARG. */
+int dit_stack_graph_info(dit_stack* st, int* n_kernel_nodes, int* n_nodes);
+
+/* ---- ceiling probes (not part of the block's path) ---------------------------
+ * What the chip delivers, to place the kernels against it as well as against
+ * the published peaks.
+ * dit_probe_copy: a streaming copy of `bytes` bytes (a multiple of 16; src
+ * and dst 16-byte aligned and disjoint), 16-byte loads and stores.
+ * dit_probe_mfma: n_workgroups workgroups of 4 wavefronts; every wavefront
+ * issues iters x 16 independent v_mfma_f32_16x16x32_bf16 (16384 flop each)
+ * on register operands: the same operands every time (vary_operands 0) or
+ * operands that change from one instruction to the next (1, as in a GEMM).
+ * out [n_workgroups * 256] fp32 receives per-lane sums (keeps the work
+ * live).  n_workgroups in [1, 2^20], iters in [1, 2^24]. */
+int dit_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+int dit_probe_mfma(float* out, int64_t n_workgroups, int64_t iters, int32_t vary_operands, void* stream);
 
 /* ---- diagnostics ------------------------------------------------------------ */
 

@@ -53,7 +53,13 @@ def test_workspace_bytes(lib):
     S, d, mlp = 256, 256, 1024
     want = a(3 * d * 4) + a(S * d * 2) + a(S * 3 * d * 2) + a(S * (d + mlp) * 2)
     assert binding.block_workspace_bytes(c) == want
-    assert binding.stack_workspace_bytes(c) == want + a(S * d * 2) + a(d * 2)
+    # stack: the block scratch, the carried activation, the staged temb, every
+    # block's modulation vectors, the W_mod / b_mod pointer table and the probe
+    # counters, all inside the caller's workspace
+    for n in (1, 57):
+        assert binding.stack_workspace_bytes(c, n) == (want + a(S * d * 2) + a(d * 2) + a(n * 3 * d * 4)
+                                                       + a(2 * n * 8) + a(n * 7 * 2 * 8))
+    assert binding.stack_workspace_bytes(c, 0) == 0
     assert binding.block_workspace_bytes(cfg(head_dim=96, num_heads=3, dim=288)) == 0
     assert binding.block_workspace_bytes(cfg(num_heads=3)) == 0
 
@@ -186,7 +192,7 @@ def test_stack_argument_checks(lib):
     assert lib.dit_stack_create(ctypes.byref(h)) == B.DIT_OK and h.value
     c = cfg()
     w = (B.BlockWeightsC * 1)(B.BlockWeightsC(0x1000, 0, 0x1000, 0, 0x1000, 0, 0x1000, 0x1000))
-    need = B.stack_workspace_bytes(c)
+    need = B.stack_workspace_bytes(c, 1)
     rep = lambda st, nb, ns, ws_bytes: lib.dit_stack_replay(
         st, ctypes.byref(c), ctypes.cast(w, ctypes.c_void_p), nb, P, P, ns, P, P, P, P, ws_bytes, None)
     assert rep(None, 1, 1, need) == B.DIT_ERR_INVALID_ARG
@@ -204,7 +210,7 @@ def test_stack_cached_argument_checks(lib):
     assert lib.dit_stack_create(ctypes.byref(h)) == B.DIT_OK and h.value
     c = cfg()
     w = (B.BlockWeightsC * 1)(B.BlockWeightsC(0x1000, 0, 0x1000, 0, 0x1000, 0, 0x1000, 0x1000))
-    need = B.stack_workspace_bytes(c)
+    need = B.stack_workspace_bytes(c, 1)
 
     def rep(fresh, t, ns=3, ws_bytes=need, st=h):
         fr = None if fresh is None else ctypes.cast((ctypes.c_uint8 * len(fresh))(*fresh), ctypes.c_void_p)
@@ -229,8 +235,14 @@ def test_stack_mixed_argument_checks(lib):
     c = cfg()
     a = lambda n: (n + 255) // 256 * 256
     S, d = 256, 256
-    need = B.stack_mixed_workspace_bytes(c)
-    assert need == max(B.block_workspace_bytes(c), B.mmdit_block_workspace_bytes(c)) + a(S * d * 2) + a(d * 2)
+    need = B.stack_mixed_workspace_bytes(c, 16, 2, 1)
+    # two two-stream blocks with both streams (6d vectors each) and one single-stream block (3d)
+    assert need == (max(B.block_workspace_bytes(c), B.mmdit_block_workspace_bytes(c)) + a(S * d * 2) + a(d * 2)
+                    + a((2 * 2 * 6 * d + 3 * d) * 4) + a(2 * 5 * 8) + a(7 * 2 * 8))
+    # text only or image only: one stream per two-stream block
+    assert B.stack_mixed_workspace_bytes(c, 0, 2, 1) < need
+    assert B.stack_mixed_workspace_bytes(c, S + 1, 2, 1) == 0
+    assert B.stack_mixed_workspace_bytes(c, 16, 0, 0) == 0
     sw = (B.StreamWeightsC * 2)(*([B.StreamWeightsC(*([0x1000] * 12))] * 2))
     bw = (B.BlockWeightsC * 1)(B.BlockWeightsC(0x1000, 0, 0x1000, 0, 0x1000, 0, 0x1000, 0x1000))
     V = lambda arr: ctypes.cast(arr, ctypes.c_void_p)
@@ -246,7 +258,7 @@ def test_stack_mixed_argument_checks(lib):
     assert rep(16, V(sw), V(sw), 2, None, 1) == B.DIT_ERR_INVALID_ARG        # singles NULL with n_single 1
     assert rep(16, V(sw), V(sw), 2, V(bw), 1, need - 256) == B.DIT_ERR_WORKSPACE
     # a mixed stack needs more than the single-stream stack's workspace
-    assert rep(16, V(sw), V(sw), 2, V(bw), 1, B.stack_workspace_bytes(c)) == B.DIT_ERR_WORKSPACE
+    assert rep(16, V(sw), V(sw), 2, V(bw), 1, B.stack_workspace_bytes(c, 3)) == B.DIT_ERR_WORKSPACE
     assert lib.dit_stack_destroy(h) == B.DIT_OK
 
 
@@ -260,4 +272,28 @@ def test_stack_probe_argument_checks(lib):
     buf = (ctypes.c_float * 6)()
     # no probed replay has run yet
     assert lib.dit_stack_probe_ms(h, ctypes.cast(buf, ctypes.c_void_p), 1) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_stack_destroy(h) == B.DIT_OK
+
+
+def test_binding_declares_every_header_function(lib):
+    from diffusion_transformer_dit_amd import binding
+    assert sorted(binding.SIGNATURES) == declared_functions()
+
+
+def test_probe_and_graph_info_argument_checks(lib):
+    from diffusion_transformer_dit_amd import binding as B
+    P, Q = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x100000)
+    assert lib.dit_probe_copy(P, Q, 0, None) == B.DIT_OK                     # nothing to copy
+    assert lib.dit_probe_copy(None, Q, 64, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_probe_copy(P, Q, 24, None) == B.DIT_ERR_INVALID_ARG       # not a multiple of 16
+    assert lib.dit_probe_copy(ctypes.c_void_p(0x1008), Q, 64, None) == B.DIT_ERR_INVALID_ARG  # misaligned
+    assert lib.dit_probe_copy(P, ctypes.c_void_p(0x1010), 64, None) == B.DIT_ERR_INVALID_ARG  # overlap
+    assert lib.dit_probe_mfma(None, 1, 1, 0, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_probe_mfma(P, 0, 1, 0, None) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_probe_mfma(P, 1, 0, 1, None) == B.DIT_ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    assert lib.dit_stack_create(ctypes.byref(h)) == B.DIT_OK
+    k, n = ctypes.c_int(), ctypes.c_int()
+    assert lib.dit_stack_graph_info(h, ctypes.byref(k), ctypes.byref(n)) == B.DIT_ERR_INVALID_ARG  # not captured
+    assert lib.dit_stack_graph_info(None, ctypes.byref(k), ctypes.byref(n)) == B.DIT_ERR_INVALID_ARG
     assert lib.dit_stack_destroy(h) == B.DIT_OK

@@ -5,7 +5,8 @@ import pytest
 
 import dit_inputs as DI
 from oracle import dit_oracle as O
-from tests.parity import assert_parity, dev_bf16, dev_f32, host
+from tests import bf16_boundaries as BB
+from tests.parity import assert_attributed, assert_parity, dev_bf16, dev_f32, host
 from tests.test_gpu_block import cfg_of, rope_dev, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -56,9 +57,12 @@ def test_mmdit_block_forward(gpu_lib, shape, n_txt):
     torch.cuda.synchronize()
     rows = sample_rows(shape.seq_len, extra=(n_txt - 1, n_txt))
     rows = rows[(rows >= 0) & (rows < shape.seq_len)]
+    print(f"  comparing {len(rows)} rows", flush=True)
     ref = O.double_block_forward(shape, txt.w if txt else None, img.w if img else None, x, temb, pos,
                                  n_txt=n_txt, rows=rows)
-    assert_parity(host(y)[rows], ref, f"mmdit y {shape.name} T={n_txt}")
+    mref = BB.double_block_forward_bf16(shape, txt.w if txt else None, img.w if img else None, x, temb, pos,
+                                        n_txt=n_txt, rows=rows)
+    assert_attributed(host(y)[rows], ref, mref, f"mmdit y {shape.name} T={n_txt}")
 
 
 SEQ_CASES = [DI.VIDEO, _shape("seq300", 300, 256, 2, 128, 512, (10, 12), 0, (64, 64))]
@@ -67,7 +71,9 @@ SEQ_CASES = [DI.VIDEO, _shape("seq300", 300, 256, 2, 128, 512, (10, 12), 0, (64,
 @pytest.mark.parametrize("shape", SEQ_CASES, ids=[s.name for s in SEQ_CASES])
 def test_sequential_block_forward(gpu_lib, shape):
     """The sequential (Wan-style) block at the video shape (S = 16384,
-    d = 1536, 12 heads, MLP 8960, 3D RoPE) on sampled rows."""
+    d = 1536, 12 heads, MLP 8960, 3D RoPE) on sampled rows (the oracle's
+    attention over 16384 keys in float64 makes every row too slow for a
+    test), and a ragged short case on every row."""
     import torch
     B = gpu_lib
     print(f"sequential block {shape.name} S={shape.seq_len}", flush=True)
@@ -78,8 +84,10 @@ def test_sequential_block_forward(gpu_lib, shape):
     y = B.sequential_block_forward(cfg, w.dev, dev_bf16(x), dev_bf16(temb), rc, rs)
     torch.cuda.synchronize()
     rows = sample_rows(shape.seq_len)
+    print(f"  comparing {len(rows)} rows", flush=True)
     ref = O.sequential_block_forward(shape, w.w, x, temb, pos, rows=rows)
-    assert_parity(host(y)[rows], ref, f"sequential y {shape.name}")
+    mref = BB.double_block_forward_bf16(shape, None, w.w, x, temb, pos, n_txt=0, rows=rows)
+    assert_attributed(host(y)[rows], ref, mref, f"sequential y {shape.name}")
 
 
 def test_mmdit_in_place_deterministic_and_sequential_alias(gpu_lib):

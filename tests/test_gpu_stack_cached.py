@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 def _run(B, shape, blocks, x, tembs, rc, rs, fresh=None, t=None, chain=False):
     import torch
     cfg = cfg_of(B, shape, B.DIT_STACK_CHAIN if chain else 0)
-    ws = B.alloc_workspace(B.stack_workspace_bytes(cfg))
+    ws = B.alloc_workspace(B.stack_workspace_bytes(cfg, len(blocks)))
     n = tembs.shape[0]
     out = torch.empty(n, shape.seq_len, shape.dim, dtype=torch.bfloat16, device="cuda")
     st = B.Stack()

@@ -26,7 +26,7 @@ def _weights(B, n_double, n_single):
 def _run(B, doubles, singles, x, tembs, rc, rs, fresh=None, chain=False):
     import torch
     cfg = cfg_of(B, MIX, B.DIT_STACK_CHAIN if chain else 0)
-    ws = B.alloc_workspace(B.stack_mixed_workspace_bytes(cfg))
+    ws = B.alloc_workspace(B.stack_mixed_workspace_bytes(cfg, T, len(doubles), len(singles)))
     out = torch.empty(tembs.shape[0], MIX.seq_len, MIX.dim, dtype=torch.bfloat16, device="cuda")
     st = B.Stack()
     st.replay_mixed(cfg, T, [(t.dev, i.dev) for t, i in doubles], [s.dev for s in singles], dev_bf16(x),
@@ -106,7 +106,7 @@ def test_mixed_stack_replay_equals_eager_bitwise_flux_shape(gpu_lib):
     tembs = rn(2, d, s=1.0)
     _, rc, rs = rope_dev(B, shape)
     cfg = cfg_of(B, shape)
-    ws = B.alloc_workspace(B.stack_mixed_workspace_bytes(cfg))
+    ws = B.alloc_workspace(B.stack_mixed_workspace_bytes(cfg, txt, len(doubles), len(singles)))
     wsm = B.alloc_workspace(B.mmdit_block_workspace_bytes(cfg))
     wsb = B.alloc_workspace(B.block_workspace_bytes(cfg))
     out = torch.empty(2, S, d, dtype=torch.bfloat16, device="cuda")
