@@ -358,16 +358,16 @@ def ceiling_times(B, g, dev, reps=3):
                                   frac_of_8TBs=round(2 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
         del srcs, dsts
         torch.cuda.synchronize()
-    nwg, iters = 2 * 256, 20000
+    nwg, iters = 2 * 256, 40000
     out = torch.empty(nwg * 256, dtype=torch.float32, device=dev)
-    flop = nwg * 4.0 * iters * 16 * 16384
+    flop = nwg * 4.0 * iters * 4 * 32768
     for label, vary in (("fixed_operands", 0), ("changing_operands", 1)):
         ms = time_graph(lambda i: B.probe_mfma(out, nwg, iters, vary), 2, reps)
         tfl = flop / (ms * 1e-3) / 1e12
         res["mfma"][label] = dict(tflops=round(tfl, 1), frac=round(tfl / BF16_PEAK_TFLOPS, 4),
                                   ms=round(ms, 3))
-    res["mfma"]["shape"] = (f"{nwg} workgroups x 4 waves x {iters} x 16 v_mfma_f32_16x16x32_bf16, "
-                            "16 independent accumulators per wave")
+    res["mfma"]["shape"] = (f"{nwg} workgroups x 4 waves x {iters} x 4 v_mfma_f32_32x32x16_bf16, "
+                            "4 independent accumulators per wave (2 waves per SIMD)")
     return res
 
 

@@ -424,7 +424,7 @@ def probe_copy(src, dst, stream=None):
 
 
 def probe_mfma(out, n_workgroups, iters, vary_operands, stream=None):
-    """Ceiling probe: n_workgroups x 4 waves x iters x 16 bf16 MFMAs of 16384 flop."""
+    """Ceiling probe: n_workgroups x 4 waves x iters x 4 bf16 MFMAs of 32768 flop."""
     _need(out, F32T, "out", 1)
     if out.numel() < n_workgroups * 256:
         raise ValueError("out needs n_workgroups * 256 floats")

@@ -106,54 +106,36 @@ __device__ __forceinline__ float xor32_sum(float v) {
 }
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-// PARTIAL: attend to keys [kv_begin, kv_end) only and write the chunk's
-// normalised output in fp32 to out_f32 [S, H*DH] and its log-sum-exp (natural
-// log) to lse [H, S], the per-hop step of ring attention; otherwise write
-// bf16 to out (row stride ld_out) over all keys.
-// With PARTIAL, blockIdx.z selects one of gridDim.z consecutive key chunks
-// of kv_chunk tokens inside [kv_begin, kv_end) and its output slices
-// (out_f32 + z*S*H*DH, lse + z*H*S): a split of the keys over more
-// workgroups when one workgroup per query block and head cannot fill the chip.
-// NW waves per workgroup (32 NW queries): 8 (one workgroup per CU) or 4 (two).
-template <int DH, bool PARTIAL, int NW>
-__global__ void __launch_bounds__(64 * NW, 8 / NW)
-attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ out_f32,
-                     float* __restrict__ lse, int S, int H, int ld_out, float c_log2, int kv_begin,
-                     int kv_end, int kv_chunk, int xcd_remap) {
+// Online-softmax state of one lane after a range of keys: the O^T
+// accumulators (registers 4g..4g+3 of oacc[b] hold dims b*32 + 8g + 4hh +
+// (0..3) of the lane's query, hh = lane / 32), the running max of the raw
+// scores (the same in lanes l and l^32) and this lane's share of the
+// softmax denominator (lanes l and l^32 hold the two halves).
+template <int DH>
+struct AttState {
+  f32x16 oacc[DH / 32];
+  float m_run, l_run;
+};
+
+// One wave's 32 queries (this lane's query row qc, clamped to S - 1 by the
+// caller) of head `head` against the keys [kv_begin, kv_end), streamed
+// through the two K/V stages in `smem`.  Ends after a workgroup barrier with
+// every LDS read done, so the caller may start another range at once.
+template <int DH, int NW>
+__device__ __forceinline__ void att_range(const bf16_t* __restrict__ qkv, unsigned char* smem, int H, int head,
+                                          int qc, int kv_begin, int kv_end, float c_log2, AttState<DH>& state) {
   using C = AttCfg<DH>;
-  constexpr int BM = 32 * NW;                      // queries per workgroup
   constexpr int LPW = ATT_BN * C::KCH / 64 / NW;  // 1 KB wave-loads per wave per tile
-  if constexpr (PARTIAL) {
-    const int z = blockIdx.z;
-    kv_begin += z * kv_chunk;
-    kv_end = min(kv_end, kv_begin + kv_chunk);
-    out_f32 += size_t(z) * S * H * DH;
-    lse += size_t(z) * H * S;
-  }
   constexpr int KCH = C::KCH;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS targets stay scalar
-  // (query block, head) from the linear block id; with xcd_remap the ids are
-  // remapped so that the workgroups one XCD runs at a time (blocks are dealt
-  // round-robin to the 8 XCDs) are consecutive query blocks of the same few
-  // heads, whose K and V then stay in that XCD's 4 MB L2 (the launchers set
-  // it when one head's K and V fit in 4 MB: +2-3 % at the Flux shape, -1.5 %
-  // at S = 16384 where they do not).
-  int bid = blockIdx.x + blockIdx.y * gridDim.x;
-  const int nb = gridDim.x * gridDim.y;
-  if (xcd_remap && (nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-  const int qblock = bid % gridDim.x;
-  const int head = bid / gridDim.x;
   const int d = H * DH;
   const int ld = 3 * d;
   const bf16_t* Qg = qkv + head * DH;
 
   const int ql = lane & 31;  // query column of this lane
   const int hh = lane >> 5;  // lane half
-  const int q = qblock * BM + wave * 32 + ql;
-  const int qc = min(q, S - 1);
 
   // Q^T operand: 8 dims (16*s + 8*hh ..) of this lane's query for each K-step s.
   bf16x8 qf[DH / 16];
@@ -204,13 +186,15 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
     vaddr[b] = C::TILE + vrow * C::ROW + (((dim >> 3) ^ v_swz<KCH>(vrow)) << 4) + 2 * (dim & 7);
   }
 
-  f32x16 oacc[DH / 32];
+  f32x16 (&oacc)[DH / 32] = state.oacc;
 #pragma unroll
   for (int b = 0; b < DH / 32; ++b)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[b][i] = 0.f;
-  float m_run = -1e30f;  // running max of raw scores of this lane's query
-  float l_run = 0.f;     // this lane's share of the running softmax denominator
+  float& m_run = state.m_run;  // running max of raw scores of this lane's query
+  float& l_run = state.l_run;  // this lane's share of the running softmax denominator
+  m_run = -1e30f;
+  l_run = 0.f;
 
   const int ntiles = (kv_end - kv_begin + ATT_BN - 1) / ATT_BN;
   issue(kv_begin, 0);
@@ -297,6 +281,53 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
     wait_all();
     __syncthreads();
   }
+}
+
+// PARTIAL: attend to keys [kv_begin, kv_end) only and write the chunk's
+// normalised output in fp32 to out_f32 [S, H*DH] and its log-sum-exp (natural
+// log) to lse [H, S], the per-hop step of ring attention; otherwise write
+// bf16 to out (row stride ld_out) over all keys.
+// With PARTIAL, blockIdx.z selects one of gridDim.z consecutive key chunks
+// of kv_chunk tokens inside [kv_begin, kv_end) and its output slices
+// (out_f32 + z*S*H*DH, lse + z*H*S): a split of the keys over more
+// workgroups when one workgroup per query block and head cannot fill the chip.
+// NW waves per workgroup (32 NW queries): 8 (one workgroup per CU) or 4 (two).
+template <int DH, bool PARTIAL, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
+attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ out_f32,
+                     float* __restrict__ lse, int S, int H, int ld_out, float c_log2, int kv_begin,
+                     int kv_end, int kv_chunk, int xcd_remap) {
+  using C = AttCfg<DH>;
+  constexpr int BM = 32 * NW;                      // queries per workgroup
+  if constexpr (PARTIAL) {
+    const int z = blockIdx.z;
+    kv_begin += z * kv_chunk;
+    kv_end = min(kv_end, kv_begin + kv_chunk);
+    out_f32 += size_t(z) * S * H * DH;
+    lse += size_t(z) * H * S;
+  }
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  // (query block, head) from the linear block id; with xcd_remap the ids are
+  // remapped so that the workgroups one XCD runs at a time (blocks are dealt
+  // round-robin to the 8 XCDs) are consecutive query blocks of the same few
+  // heads, whose K and V then stay in that XCD's 4 MB L2 (the launchers set
+  // it when one head's K and V fit in 4 MB: +2-3 % at the Flux shape, -1.5 %
+  // at S = 16384 where they do not).
+  int bid = blockIdx.x + blockIdx.y * gridDim.x;
+  const int nb = gridDim.x * gridDim.y;
+  if (xcd_remap && (nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int qblock = bid % gridDim.x;
+  const int head = bid / gridDim.x;
+  const int d = H * DH;
+  const int q = qblock * BM + wave * 32 + (lane & 31);
+  const int hh = lane >> 5;
+  AttState<DH> st;
+  att_range<DH, NW>(qkv, smem, H, head, min(q, S - 1), kv_begin, kv_end, c_log2, st);
+  const f32x16 (&oacc)[DH / 32] = st.oacc;
+  const float m_run = st.m_run, l_run = st.l_run;
 
   const float l_tot = xor32_sum(l_run);
   const float inv = 1.0f / l_tot;

@@ -3,11 +3,10 @@
 //   copy16_kernel    a plain streaming copy (16-byte loads and stores, four
 //                    chunks in flight per thread): the practical HBM rate at
 //                    a given size, the ceiling of the memory-bound chain;
-//   mfma_peak_kernel back-to-back v_mfma_f32_16x16x32_bf16 on register
-//                    operands, either the same operands every time or ones
-//                    that change with every instruction (as in a GEMM, whose
-//                    matrix cores then draw more power): the practical rate
-//                    of the GEMMs' instruction.
+//   mfma_peak_kernel back-to-back bf16 MFMAs on register operands, either
+//                    the same operands every time or ones that change with
+//                    every instruction (as in a GEMM, whose matrix cores then
+//                    draw more power): the practical bf16 matrix-core rate.
 // Neither is part of the block's path.
 #include "dit_common.hpp"
 #include "launch.hpp"
@@ -67,40 +66,38 @@ __device__ __forceinline__ bf16x8 operand(uint32_t seed) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// 4 waves per workgroup; every wave issues `iters` rounds of 16 independent
-// MFMAs (16 accumulators, so no instruction waits on the previous one).
+// 4 waves per workgroup; every wave issues `iters` rounds of 4 independent
+// v_mfma_f32_32x32x16_bf16 (32768 flop each; the same flop rate per cycle as
+// the GEMMs' 16x16x32 instruction, and the attention's instruction), so no
+// instruction waits on the previous one.  VARY: the operands change from one
+// instruction to the next (two A and two B fragments in rotation) instead of
+// staying the same.
+template <bool VARY>
 __global__ void __launch_bounds__(256)
-mfma_peak_kernel(float* __restrict__ out, int iters, int vary) {
+mfma_peak_kernel(float* __restrict__ out, int iters) {
   const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
-  bf16x8 a[4], b[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    a[r] = operand(gid * 8u + r);
-    b[r] = operand(gid * 8u + 4 + r);
+  const bf16x8 a0 = operand(gid * 4u), a1 = operand(gid * 4u + 1);
+  const bf16x8 b0 = operand(gid * 4u + 2), b1 = operand(gid * 4u + 3);
+  f32x16 c0{}, c1{}, c2{}, c3{};
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(VARY ? a1 : a0, b0, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, VARY ? b1 : b0, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(VARY ? a1 : a0, VARY ? b1 : b0, c3, 0, 0, 0);
   }
-  f32x4 acc[16];
+  const f32x16 sv = (c0 + c1) + (c2 + c3);
+  float t = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (vary) {
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i >> 2], b[i & 3], acc[i], 0, 0, 0);
-    }
-  } else {
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[0], acc[i], 0, 0, 0);
-    }
-  }
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) s += (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
-  out[gid] = s;
+  for (int i = 0; i < 16; ++i) t += sv[i];
+  out[gid] = t;
 }
 
 hipError_t launch_probe_mfma(float* out, int n_workgroups, int iters, int vary, hipStream_t st) {
   if (n_workgroups <= 0) return hipSuccess;
-  mfma_peak_kernel<<<n_workgroups, 256, 0, st>>>(out, iters, vary);
+  if (vary)
+    mfma_peak_kernel<true><<<n_workgroups, 256, 0, st>>>(out, iters);
+  else
+    mfma_peak_kernel<false><<<n_workgroups, 256, 0, st>>>(out, iters);
   return hipGetLastError();
 }
 

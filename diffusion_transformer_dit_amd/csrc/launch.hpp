@@ -117,7 +117,7 @@ hipError_t launch_extrapolate(const bf16_t* a, const bf16_t* b, float w, bf16_t*
 hipError_t launch_probe_stamp(unsigned long long* ch, int finish, hipStream_t st);
 
 // ceiling probes: a streaming copy of `bytes` (a multiple of 16) and
-// n_workgroups x 4 waves x iters x 16 bf16 MFMAs (out: n_workgroups*256 floats)
+// n_workgroups x 4 waves x iters x 4 bf16 32x32x16 MFMAs (out: n_workgroups*256 floats)
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 hipError_t launch_probe_mfma(float* out, int n_workgroups, int iters, int vary, hipStream_t st);
 

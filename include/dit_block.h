@@ -398,7 +398,7 @@ int dit_stack_graph_info(dit_stack* st, int* n_kernel_nodes, int* n_nodes);
  * dit_probe_copy: a streaming copy of `bytes` bytes (a multiple of 16; src
  * and dst 16-byte aligned and disjoint), 16-byte loads and stores.
  * dit_probe_mfma: n_workgroups workgroups of 4 wavefronts; every wavefront
- * issues iters x 16 independent v_mfma_f32_16x16x32_bf16 (16384 flop each)
+ * issues iters x 4 independent v_mfma_f32_32x32x16_bf16 (32768 flop each)
  * on register operands: the same operands every time (vary_operands 0) or
  * operands that change from one instruction to the next (1, as in a GEMM).
  * out [n_workgroups * 256] fp32 receives per-lane sums (keeps the work
