@@ -60,6 +60,8 @@ SIGNATURES = {
     "dit_rope_table": ([VP, I64, I32, VP, I64, F32, VP, VP, VP], ctypes.c_int),
     "dit_block_workspace_bytes": ([VP], SZ),
     "dit_block_forward": ([VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
+    "dit_block_noalloc_max_bytes": ([], SZ),
+    "dit_block_forward_noalloc": ([VP, VP, VP, VP, VP, VP, VP, VP], ctypes.c_int),
     "dit_mmdit_block_workspace_bytes": ([VP], SZ),
     "dit_mmdit_block_forward": ([VP, I64, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
     "dit_sequential_block_forward": ([VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
@@ -430,6 +432,25 @@ def probe_mfma(out, n_workgroups, iters, vary_operands, stream=None):
         raise ValueError("out needs n_workgroups * 256 floats")
     _check(_lib.dit_probe_mfma(_p(out), n_workgroups, iters, 1 if vary_operands else 0, _stream(stream)))
     return out
+
+
+def block_noalloc_max_bytes() -> int:
+    return int(_lib.dit_block_noalloc_max_bytes())
+
+
+def block_forward_noalloc(cfg, weights: BlockWeights, x, temb, rope_cos, rope_sin, y, stream=None):
+    """block_forward with the library's built-in per-GPU scratch instead of a
+    workspace (no allocation anywhere; y must be given)."""
+    _need(x, BF16, "x", 2)
+    _need(temb, BF16, "temb", 1)
+    _need(rope_cos, F32T, "rope_cos", 2)
+    _need(rope_sin, F32T, "rope_sin", 2)
+    _need(y, BF16, "y", 2)
+    if x.shape != (cfg.seq_len, cfg.dim) or y.shape != x.shape:
+        raise ValueError("x / y shape does not match the config")
+    _check(_lib.dit_block_forward_noalloc(ctypes.byref(cfg), ctypes.byref(weights.c), _p(x), _p(temb),
+                                          _p(rope_cos), _p(rope_sin), _p(y), _stream(stream)))
+    return y
 
 
 class Stack:

@@ -10,6 +10,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -497,6 +498,58 @@ extern "C" int dit_block_forward(const dit_block_config* cfg, const dit_block_we
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(DIT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   return enqueue_block(D, cfg, w, x, temb, rope_cos, rope_sin, y, static_cast<unsigned char*>(workspace),
                        as_stream(stream));
+}
+
+// ======================================== whole block without any allocation
+// For callers that cannot allocate device memory at all: the block's scratch
+// (modulation vectors, u, q|k|v, concat buffer) lives in one file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never uses
+// the array's name as an address: the first call on each device looks up that
+// device's copy with hipGetSymbolAddress and keeps the pointer.
+constexpr size_t kNoAllocScratchBytes = size_t(256) << 20;  // one Flux-shape block needs 243 MiB
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch`, looked up once per device.
+int scratch_for_current_device(unsigned char** out) {
+  int dev = 0;
+  DIT_CHECK_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DIT_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    DIT_CHECK_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p || reinterpret_cast<uintptr_t>(p) % 256 != 0)
+      return fail(DIT_ERR_HIP, "scratch array of device %d is missing or misaligned", dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<unsigned char*>(g_scratch_ptr[dev]);
+  return DIT_OK;
+}
+}  // namespace
+
+extern "C" size_t dit_block_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int dit_block_forward_noalloc(const dit_block_config* cfg, const dit_block_weights* w, const dit_bf16* x,
+                                         const dit_bf16* temb, const float* rope_cos, const float* rope_sin,
+                                         dit_bf16* y, void* stream) {
+  Dims D;
+  int rc = dims_of(cfg, &D);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (!x || !temb || !rope_cos || !rope_sin || !y) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+  if ((rc = check_aligned({x, temb, rope_cos, rope_sin, y}))) return rc;
+  const WsLayout L = layout(D);
+  if (L.block_end > kNoAllocScratchBytes)
+    return fail(DIT_ERR_WORKSPACE, "this config needs %zu bytes of scratch; the built-in array holds %zu",
+                L.block_end, kNoAllocScratchBytes);
+  unsigned char* ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws))) return rc;
+  return enqueue_block(D, cfg, w, x, temb, rope_cos, rope_sin, y, ws, as_stream(stream));
 }
 
 // ================================================= two-stream / sequential blocks

@@ -226,6 +226,24 @@ int dit_block_forward(const dit_block_config* cfg, const dit_block_weights* w,
                       const float* rope_sin, dit_bf16* y, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): dit_block_forward
+ * with the workspace taken from a scratch array built into the library, one
+ * copy per GPU of dit_block_noalloc_max_bytes() = 256 MiB, held from the
+ * first call on that GPU until the process ends (one Flux-shape block needs
+ * 243 MiB).  Same kernels and results as dit_block_forward.  Configs whose
+ * workspace exceeds the array give DIT_ERR_WORKSPACE.  The first call on
+ * each device looks up that device's copy of the array (hipGetSymbolAddress;
+ * make that first call outside a capture); no call allocates.  Every call on
+ * one GPU uses the same array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must be ordered by
+ * the caller.  The array keeps the last call's contents; nothing in it needs
+ * to start at zero. */
+size_t dit_block_noalloc_max_bytes(void);
+int dit_block_forward_noalloc(const dit_block_config* cfg, const dit_block_weights* w, const dit_bf16* x,
+                              const dit_bf16* temb, const float* rope_cos, const float* rope_sin, dit_bf16* y,
+                              void* stream);
+
 /* ---- two-stream (MMDiT) and sequential blocks ------------------------------ */
 
 /* Weights of one stream.  The Flux page (section 3.1) names the block lists
