@@ -419,8 +419,10 @@ def trace_summary(path, n_blocks=57):
             i = j
         else:
             i += 1
-    # only the plain (unprobed) 57-block replays: a probed step interleaves stamp kernels
-    want = [st for st in steps if (len(st) - 1) % n_blocks == 0 and (len(st) - 1) // n_blocks in (5, 6)]
+    # only the plain (unprobed) single-stream replays: a probed step
+    # interleaves stamp kernels, a mixed stack has two block kinds
+    want = [st for st in steps if (len(st) - 1) % n_blocks == 0 and 1 <= (len(st) - 1) // n_blocks <= 8
+            and all("EpiGated" not in r["Kernel_Name"] for r in st)]
     if not want:
         raise SystemExit("no replayed step of the stack found in the trace")
     out = []
@@ -431,6 +433,14 @@ def trace_summary(path, n_blocks=57):
         out.append(dict(kernels=len(st), kernels_per_block=(len(st) - 1) / n_blocks, span_us=(t1 - t0) / 1e3,
                         busy_us=busy / 1e3, gap_us=sum(gaps) / 1e3, max_gap_us=max(gaps) / 1e3,
                         mean_gap_us=sum(gaps) / len(gaps) / 1e3, negative_gaps=sum(1 for x in gaps if x < 0)))
+    # mean duration of each kernel inside the replayed steps (block kernels
+    # by name; the batched modulation once per step)
+    per_kernel = {}
+    for st in want:
+        for r in st:
+            nm = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("dit::", "")
+            per_kernel.setdefault(nm, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    kernel_means = {k: dict(calls=len(v), mean_us=round(sum(v) / len(v) / 1e3, 2)) for k, v in per_kernel.items()}
     agg = dict(source=os.path.relpath(path), steps=len(out), kernels_per_step=out[0]["kernels"],
                kernels_per_block=out[0]["kernels_per_block"],
                span_us_mean=round(sum(o["span_us"] for o in out) / len(out), 1),
@@ -438,6 +448,7 @@ def trace_summary(path, n_blocks=57):
                mean_gap_us=round(sum(o["mean_gap_us"] for o in out) / len(out), 3),
                max_gap_us=round(max(o["max_gap_us"] for o in out), 3),
                gap_frac=round(sum(o["gap_us"] for o in out) / sum(o["span_us"] for o in out), 5),
+               kernel_means=kernel_means,
                per_step=[{k: (round(v, 3) if isinstance(v, float) else v) for k, v in o.items()} for o in out])
     return agg
 

@@ -9,7 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dit_block.h")
-LIB = os.path.join(ROOT, "diffusion_transformer_dit_amd", "libdit_block.so")
+LIB = os.environ.get("DIT_LIB") or os.path.join(ROOT, "diffusion_transformer_dit_amd", "libdit_block.so")
 
 
 @pytest.fixture(scope="module")
@@ -17,7 +17,7 @@ def lib():
     if not os.path.exists(LIB):
         from diffusion_transformer_dit_amd import build
         build.build()
-    from diffusion_transformer_dit_amd import binding
+    from diffusion_transformer_dit_amd import abi as binding
     return binding._lib
 
 
@@ -35,19 +35,19 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    from diffusion_transformer_dit_amd import binding
+    from diffusion_transformer_dit_amd import abi as binding
     assert "gfx950" in binding.version()
 
 
 def cfg(**kw):
-    from diffusion_transformer_dit_amd import binding
+    from diffusion_transformer_dit_amd import abi as binding
     base = dict(seq_len=256, dim=256, num_heads=4, head_dim=64, mlp_hidden=1024)
     base.update(kw)
     return binding.make_config(**base)
 
 
 def test_workspace_bytes(lib):
-    from diffusion_transformer_dit_amd import binding
+    from diffusion_transformer_dit_amd import abi as binding
     c = cfg()
     a = lambda n: (n + 255) // 256 * 256
     S, d, mlp = 256, 256, 1024
@@ -65,7 +65,7 @@ def test_workspace_bytes(lib):
 
 
 def test_invalid_arguments_are_rejected_before_hip(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     P = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     assert lib.dit_modulate_norm(None, P, P, P, 4, 8, 1e-6, None) == B.DIT_ERR_INVALID_ARG
     assert lib.dit_modulate_norm(P, P, P, P, 4, 12, 1e-6, None) == B.DIT_ERR_UNSUPPORTED
@@ -84,7 +84,7 @@ def test_invalid_arguments_are_rejected_before_hip(lib):
 
 
 def test_misaligned_tensor_pointers_are_rejected(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     P, Q = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)  # Q: 8-byte aligned only
     assert lib.dit_modulate_norm(Q, P, P, P, 4, 64, 1e-6, None) == B.DIT_ERR_INVALID_ARG
     assert "aligned" in lib.dit_last_error().decode()
@@ -102,7 +102,7 @@ def test_misaligned_tensor_pointers_are_rejected(lib):
 
 
 def test_sizes_beyond_32bit_ranges_are_unsupported(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     P = ctypes.c_void_p(0x1000)
     # 60000 tokens x 3 x 6144 dims > 2^30 q|k|v elements
     assert lib.dit_attention(P, P, 60000, 48, 128, 6144, None) == B.DIT_ERR_UNSUPPORTED
@@ -111,7 +111,7 @@ def test_sizes_beyond_32bit_ranges_are_unsupported(lib):
 
 
 def test_split_attention_argument_checks(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     P = ctypes.c_void_p(0x1000)
     split = lambda S, n, ld=128, lses=P: lib.dit_attention_split(P, P, S, 1, 128, ld, n, P, lses, None)
     assert split(64, 0) == B.DIT_ERR_INVALID_ARG
@@ -124,7 +124,7 @@ def test_split_attention_argument_checks(lib):
 
 
 def test_chunked_attention_argument_checks(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     P, Q = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)
     assert lib.dit_attention_partial(P, 64, 2, 64, 10, 10, P, P, None) == B.DIT_ERR_INVALID_ARG  # empty range
     assert lib.dit_attention_partial(P, 64, 2, 64, 0, 65, P, P, None) == B.DIT_ERR_INVALID_ARG   # past the end
@@ -138,7 +138,7 @@ def test_chunked_attention_argument_checks(lib):
 
 
 def test_block_forward_argument_checks(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     P = ctypes.c_void_p(0x1000)
     c = cfg()
     w = B.BlockWeightsC(0x1000, 0, 0x1000, 0, 0x1000, 0, 0x1000, 0x1000)
@@ -156,7 +156,7 @@ def test_block_forward_argument_checks(lib):
 
 
 def test_mmdit_block_argument_checks(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     P = ctypes.c_void_p(0x1000)
     c = cfg()
     a = lambda n: (n + 255) // 256 * 256
@@ -186,7 +186,7 @@ def test_mmdit_block_argument_checks(lib):
 
 
 def test_stack_argument_checks(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     P = ctypes.c_void_p(0x1000)
     h = ctypes.c_void_p()
     assert lib.dit_stack_create(ctypes.byref(h)) == B.DIT_OK and h.value
@@ -204,7 +204,7 @@ def test_stack_argument_checks(lib):
 
 
 def test_stack_cached_argument_checks(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     P = ctypes.c_void_p(0x1000)
     h = ctypes.c_void_p()
     assert lib.dit_stack_create(ctypes.byref(h)) == B.DIT_OK and h.value
@@ -228,7 +228,7 @@ def test_stack_cached_argument_checks(lib):
 
 
 def test_stack_mixed_argument_checks(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     P = ctypes.c_void_p(0x1000)
     h = ctypes.c_void_p()
     assert lib.dit_stack_create(ctypes.byref(h)) == B.DIT_OK and h.value
@@ -263,7 +263,7 @@ def test_stack_mixed_argument_checks(lib):
 
 
 def test_stack_probe_argument_checks(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     h = ctypes.c_void_p()
     assert lib.dit_stack_create(ctypes.byref(h)) == B.DIT_OK
     assert lib.dit_stack_set_probe(None, 1) == B.DIT_ERR_INVALID_ARG
@@ -276,12 +276,12 @@ def test_stack_probe_argument_checks(lib):
 
 
 def test_binding_declares_every_header_function(lib):
-    from diffusion_transformer_dit_amd import binding
+    from diffusion_transformer_dit_amd import abi as binding
     assert sorted(binding.SIGNATURES) == declared_functions()
 
 
 def test_probe_and_graph_info_argument_checks(lib):
-    from diffusion_transformer_dit_amd import binding as B
+    from diffusion_transformer_dit_amd import abi as B
     P, Q = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x100000)
     assert lib.dit_probe_copy(P, Q, 0, None) == B.DIT_OK                     # nothing to copy
     assert lib.dit_probe_copy(None, Q, 64, None) == B.DIT_ERR_INVALID_ARG
