@@ -371,6 +371,27 @@ def ceiling_times(B, g, dev, reps=3):
     return res
 
 
+def library_gemm_times(g, dev, reps=3):
+    """The vendor library on the same GEMM shapes, for comparison only:
+    torch.matmul (hipBLASLt) of u [S, d] by W1^T [d, N1] and of the concat
+    buffer [S, N2] by W2^T [N2, d], bf16 in and out, no epilogue, captured in
+    a graph and replayed.  The weights are stored [out, in] as in the block,
+    so the right operand is a transposed view (made contiguous first)."""
+    import torch
+    res = {}
+    for name, (m, k, n, flop) in (("linear1", (S, D, N1, GEMM1_FLOP)), ("linear2", (S, N2, D, GEMM2_FLOP))):
+        a = (torch.randn(m, k, generator=g, device=dev)).to(torch.bfloat16)
+        w = (torch.randn(n, k, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        wt = w.t().contiguous()
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        ms = time_graph(lambda i: torch.matmul(a, wt, out=out), 4, reps)
+        tfl = flop / (ms * 1e-3) / 1e12
+        res[name] = dict(us=round(ms * 1e3, 1), tflops=round(tfl, 1), frac=round(tfl / BF16_PEAK_TFLOPS, 4))
+        del a, w, wt, out
+    torch.cuda.synchronize()
+    return res
+
+
 def host_cpu():
     model = "unknown"
     try:
@@ -602,6 +623,7 @@ def main():
             out["config_blocks"] = config_block_times(B, g, dev)
         if "ceilings" in only:
             out["ceilings"] = ceiling_times(B, g, dev)
+            out["ceilings"]["library_gemm"] = library_gemm_times(g, dev)
         print(json.dumps(out), flush=True)
         return 0
 
@@ -815,6 +837,10 @@ def main():
     log("config blocks: " + ", ".join(f"{n} {v['ms']:.4f} ms ({v['tflops']} TFLOP/s)"
                                       for n, v in cb.items() if isinstance(v, dict)))
     ce = ceiling_times(B, g, dev)
+    lg = library_gemm_times(g, dev)
+    ce["library_gemm"] = lg
+    ce["library_gemm"]["note"] = ("torch.matmul (hipBLASLt) on the same shapes without epilogues, graph-timed "
+                                  "outside the stack; comparison only")
     result["ceilings"] = ce
     cpy_n, cpy_g = ce["copy"]["56.6MB_moved"]["gbs"], ce["copy"]["84.9MB_moved"]["gbs"]
     kernels["modulate_norm"]["frac_of_copy_same_size"] = round(kernels["modulate_norm"]["gbs"] / cpy_n, 4)
@@ -824,7 +850,8 @@ def main():
     kernels["gated_residual"]["frac_of_copy_4GiB"] = round(kernels["gated_residual"]["gbs"] /
                                                            ce["copy"]["4GiB_moved"]["gbs"], 4)
     log("ceilings: copy " + ", ".join(f"{n} {v['gbs']} GB/s" for n, v in ce["copy"].items()) + "; mfma "
-        + ", ".join(f"{n} {v['tflops']} TFLOP/s" for n, v in ce["mfma"].items() if isinstance(v, dict)))
+        + ", ".join(f"{n} {v['tflops']} TFLOP/s" for n, v in ce["mfma"].items() if isinstance(v, dict))
+        + "; library gemm " + ", ".join(f"{n} {v['us']} us" for n, v in lg.items() if isinstance(v, dict)))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one Flux block ...")
         result["cpu_baseline"] = cpu_baseline()
