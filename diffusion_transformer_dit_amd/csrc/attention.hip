@@ -146,9 +146,11 @@ __device__ __forceinline__ void att_range(const bf16_t* __restrict__ qkv, unsign
   // ---- tile loads: wave-load w of a tile fills LDS chunks [64w, 64w + 64);
   // chunk p holds row p / KCH, global chunk (p % KCH) ^ swz(row).
   // Byte offsets of this lane's chunks inside a tile (rows = tokens of the
-  // tile).  Each tile gets a descriptor whose range ends with the key range,
-  // so the rows of a ragged last tile past it read as zero: their scores are
-  // masked to -inf and their V rows meet zero probabilities.
+  // tile).  Each tile gets a descriptor whose range ends with the tile or
+  // with the key range, whichever comes first, so the rows of a ragged last
+  // tile past it read as zero: their scores are masked to -inf and their V
+  // rows meet zero probabilities.  (The range is at most 64 rows, so its
+  // 32-bit byte count cannot wrap even when q|k|v spans more than 4 GiB.)
   int koff[LPW], voff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
@@ -160,7 +162,8 @@ __device__ __forceinline__ void att_range(const bf16_t* __restrict__ qkv, unsign
   auto issue = [&](int t0, int stage) {
     unsigned char* sK = smem + stage * C::STAGE;
     unsigned char* sV = sK + C::TILE;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(qkv + size_t(t0) * ld, uint32_t(kv_end - t0) * uint32_t(ld) * 2u);
+    const uint32_t rows = uint32_t(min(kv_end - t0, ATT_BN));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(qkv + size_t(t0) * ld, rows * uint32_t(ld) * 2u);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int w = wave * LPW + i;

@@ -72,10 +72,6 @@ int check_dims(int64_t S, int64_t d, int64_t H, int64_t Dh, int64_t mlp, int64_t
   if (mlp % 64 != 0 || mlp > (int64_t(1) << 20)) return fail(DIT_ERR_UNSUPPORTED, "mlp_hidden=%lld must be a multiple of 64", (long long)mlp);
   if (tdim % 8 != 0 || tdim > kMaxRowCols) return fail(DIT_ERR_UNSUPPORTED, "temb_dim=%lld must be a multiple of 8 and <= 8192", (long long)tdim);
   if (S > (1 << 24)) return fail(DIT_ERR_UNSUPPORTED, "seq_len=%lld too large", (long long)S);
-  // the attention addresses its q|k|v rows through 32-bit buffer ranges
-  if (S * 3 * d * 2 > kMaxInt)
-    return fail(DIT_ERR_UNSUPPORTED, "seq_len * 3 * dim = %lld elements is too large (at most 2^30)",
-                (long long)(S * 3 * d));
   return DIT_OK;
 }
 

@@ -38,9 +38,8 @@
  *     pointers may then be NULL.
  *   - Supported shapes: any seq_len >= 0 (ragged tails are handled);
  *     dim % 64 == 0; head_dim in {64, 128} with num_heads*head_dim == dim;
- *     mlp_hidden % 64 == 0; temb_dim % 8 == 0; seq_len * 3 * dim <= 2^30
- *     (the q|k|v buffer is addressed with 32-bit ranges).  Others give
- *     DIT_ERR_UNSUPPORTED.
+ *     dim <= 8192; mlp_hidden % 64 == 0; temb_dim % 8 == 0;
+ *     seq_len <= 2^24.  Others give DIT_ERR_UNSUPPORTED.
  */
 #ifndef DIT_BLOCK_H
 #define DIT_BLOCK_H

@@ -101,13 +101,16 @@ def test_misaligned_tensor_pointers_are_rejected(lib):
         == B.DIT_ERR_INVALID_ARG
 
 
-def test_sizes_beyond_32bit_ranges_are_unsupported(lib):
+def test_size_limits(lib):
     from diffusion_transformer_dit_amd import abi as B
     P = ctypes.c_void_p(0x1000)
-    # 60000 tokens x 3 x 6144 dims > 2^30 q|k|v elements
-    assert lib.dit_attention(P, P, 60000, 48, 128, 6144, None) == B.DIT_ERR_UNSUPPORTED
-    assert B.block_workspace_bytes(B.make_config(60000, 6144, 48, 128, 12288)) == 0
-    assert B.block_workspace_bytes(B.make_config(50000, 6144, 48, 128, 12288)) > 0
+    # q|k|v beyond 4 GiB is supported (a Wan-size video sequence at width 8192 and more)
+    ws = B.block_workspace_bytes(B.make_config(90000, 8192, 64, 128, 32768))
+    assert ws >= 90000 * 3 * 8192 * 2 > 1 << 32
+    # seq_len is capped at 2^24, dim at 8192
+    assert lib.dit_attention(P, P, (1 << 24) + 1, 1, 128, 128, None) == B.DIT_ERR_UNSUPPORTED
+    assert B.block_workspace_bytes(B.make_config((1 << 24) + 1, 256, 2, 128, 1024)) == 0
+    assert lib.dit_attention(P, P, 64, 72, 128, 9216, None) == B.DIT_ERR_UNSUPPORTED
 
 
 def test_split_attention_argument_checks(lib):

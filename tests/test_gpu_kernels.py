@@ -184,6 +184,51 @@ def test_attention_full_size(gpu_lib, S, H):
     assert_parity(host(out)[rows], ref, f"attention S={S} ({len(rows)} rows)")
 
 
+def test_attention_qkv_beyond_4gib(gpu_lib):
+    """q|k|v larger than 4 GiB (S = 87500 tokens at width 8192): every key
+    tile must be read whole wherever it sits.  Head h is the seeded one-head
+    q, k, v rolled by h tokens; query rows 0 and S-1 point at key 120 (a
+    needle that takes almost all of their softmax weight), so a key tile
+    read as zeros would change their outputs completely."""
+    import torch
+    S, H, Dh, needle = 87500, 64, 128, 120
+    d = H * Dh
+    assert S * 3 * d * 2 > 1 << 32
+    base = _qkv_for_attention(S, 1, Dh, 35)            # [S, 3*Dh]: q | k | v of one head
+    rows = np.array([0, 1, 40000, S - 1])
+    qb = base[:, :Dh].copy()
+    kb, vb = base[:, Dh:2 * Dh], base[:, 2 * Dh:]
+
+    def head(a, h):
+        return np.roll(a, h, axis=0)
+
+    # needle rows, per head: q = 2 k_needle (the rolled head's key at that token)
+    qrows = {}
+    for h in range(H):
+        kh = kb[(needle - h) % S]
+        for r in (0, S - 1):
+            qrows[(h, r)] = DI.round_bf16((2.0 * kh).astype(np.float32))
+    qkv = torch.empty(S, 3 * d, dtype=torch.bfloat16, device="cuda")
+    parts = [dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)]
+    for h in range(H):
+        for part in range(3):
+            qkv[:, part * d + h * Dh: part * d + (h + 1) * Dh] = torch.roll(parts[part], h, 0)
+        for r in (0, S - 1):
+            qkv[r, h * Dh:(h + 1) * Dh] = dev_bf16(qrows[(h, r)])
+    del parts
+    out = torch.empty(S, d, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.attention(qkv, out, H, Dh)
+    torch.cuda.synchronize()
+    g = host(out[torch.from_numpy(rows).cuda()])
+    del qkv, out
+    for h in (0, 1, 31, 63):
+        qh = head(qb, h)
+        for r in (0, S - 1):
+            qh[r] = qrows[(h, r)]
+        ref = O.attention(qh, head(kb, h), head(vb, h), 1, Dh, q_rows=rows)
+        assert_parity(g[:, h * Dh:(h + 1) * Dh], ref, f"attention beyond 4 GiB, head {h}")
+
+
 # ------------------------------------------ chunked attention + LSE merge
 @pytest.mark.parametrize("S,H,Dh,bounds", [
     (333, 3, 128, [0, 100, 333]),                 # ragged chunks
