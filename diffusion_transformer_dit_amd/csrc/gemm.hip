@@ -454,6 +454,7 @@ gemm_bf16_tn_kernel(GemmGroup<Epi, NP> grp) {
 using T288x192 = TileCfg<288, 192, 2, 4, 4>;  // 8 waves of 144 x 48; groups own 144-row halves
 using T256 = TileCfg<256, 256, 4, 2, 4>;      // 8 waves of 64 x 128; groups own 128-row halves
 using T128x256 = TileCfg<128, 256, 4, 2, 4>;  // 8 waves of 32 x 128 (whole heads per wave, small M)
+using T256x192 = TileCfg<256, 192, 4, 2, 4>;  // 8 waves of 64 x 96 (N = 1536 in 8 tiles: two full rounds at S = 16384)
 using T128 = TileCfg<128, 128, 4, 2, 4>;      // 8 waves of 32 x 64
 
 int num_cus() {
@@ -470,7 +471,7 @@ int num_cus() {
 
 void prepare_device() { (void)num_cus(); }
 
-enum TileKind { K288x192 = 0, K256 = 1, K128 = 2, K128x256 = 3 };
+enum TileKind { K288x192 = 0, K256 = 1, K128 = 2, K128x256 = 3, K256x192 = 4 };
 
 // Pick the tile that minimises rounds-of-workgroups x tile area / efficiency
 // (a proxy for the time of the busiest CU) over the tiles of all problems of
@@ -480,9 +481,10 @@ static TileKind choose_tile(const int* Ms, const int* Ns, int np, bool head_tile
   const int cus = num_cus();
   struct Opt { TileKind k; int bm, bn; double eff; bool heads; } opts[] = {
       // per-tile efficiency measured at the Flux shape (288x192 waves hold a
-      // thinner 144 x 48 sub-tile and run at 0.87 of the 256x256 rate)
+      // thinner 144 x 48 sub-tile and run at 0.87 of the 256x256 rate) and,
+      // for 256x192 (64 x 96 per wave), at the video shape's N = 1536 GEMMs
       {K288x192, 288, 192, 0.87, false}, {K256, 256, 256, 1.0, true}, {K128, 128, 128, 0.6, false},
-      {K128x256, 128, 256, 0.75, true}};
+      {K128x256, 128, 256, 0.75, true}, {K256x192, 256, 192, 0.82, false}};
   TileKind best = head_tiles ? K128x256 : K128;
   double best_cost = 1e300;
   for (const Opt& o : opts) {
@@ -546,6 +548,7 @@ static hipError_t launch_gemm_group(const GemmProblem<Epi>* ps, int np, hipStrea
   switch (choose_group_tile(ps, np)) {
     case K288x192: return launch_tile_group<T288x192>(ps, np, st);
     case K256: return launch_tile_group<T256>(ps, np, st);
+    case K256x192: return launch_tile_group<T256x192>(ps, np, st);
     default: return launch_tile_group<T128>(ps, np, st);
   }
 }
@@ -557,6 +560,7 @@ static hipError_t launch_gemm(const bf16_t* A, const bf16_t* B, int M, int N, in
   switch (choose_tile(M, N)) {
     case K288x192: return launch_tile<T288x192>(A, B, M, N, K, e, st);
     case K256: return launch_tile<T256>(A, B, M, N, K, e, st);
+    case K256x192: return launch_tile<T256x192>(A, B, M, N, K, e, st);
     default: return launch_tile<T128>(A, B, M, N, K, e, st);
   }
 }
