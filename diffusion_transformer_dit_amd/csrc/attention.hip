@@ -29,6 +29,7 @@
 //                 leaves the contraction unchanged.
 #include "dit_common.hpp"
 #include "launch.hpp"
+#include "mod_gemv.hpp"
 
 namespace dit {
 
@@ -286,6 +287,21 @@ __device__ __forceinline__ void att_range(const bf16_t* __restrict__ qkv, unsign
   }
 }
 
+// bf16 output row of the lane's query: registers 4g..4g+3 of oacc[b] hold
+// dims b*32 + 8g + 4hh + (0..3), scaled by the reciprocal denominator.
+template <int DH>
+__device__ __forceinline__ void att_store_bf16(const f32x16 (&oacc)[DH / 32], float inv, bf16_t* orow, int hh) {
+#pragma unroll
+  for (int b = 0; b < DH / 32; ++b)
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      u32x2 w;
+      w[0] = pack_bf2(oacc[b][4 * gg] * inv, oacc[b][4 * gg + 1] * inv);
+      w[1] = pack_bf2(oacc[b][4 * gg + 2] * inv, oacc[b][4 * gg + 3] * inv);
+      *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * gg + 4 * hh) = w;
+    }
+}
+
 // PARTIAL: attend to keys [kv_begin, kv_end) only and write the chunk's
 // normalised output in fp32 to out_f32 [S, H*DH] and its log-sum-exp (natural
 // log) to lse [H, S], the per-hop step of ring attention; otherwise write
@@ -349,19 +365,45 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
       // scores in exp2 units are s * log2(e)/sqrt(Dh): lse = (m c + log2 l) ln 2
       if (hh == 0) lse[size_t(head) * S + q] = (m_run * c_log2 + __log2f(l_tot)) * 0.6931471805599453f;
     } else {
-      bf16_t* orow = out + size_t(q) * ld_out + head * DH;
-#pragma unroll
-      for (int b = 0; b < DH / 32; ++b)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          // registers 4gg..4gg+3 hold dims b*32 + 8gg + 4hh + (0..3)
-          u32x2 w;
-          w[0] = pack_bf2(oacc[b][4 * gg] * inv, oacc[b][4 * gg + 1] * inv);
-          w[1] = pack_bf2(oacc[b][4 * gg + 2] * inv, oacc[b][4 * gg + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * gg + 4 * hh) = w;
-        }
+      att_store_bf16<DH>(oacc, inv, out + size_t(q) * ld_out + head * DH, hh);
     }
   }
+}
+
+// The attention of attention_fwd_kernel<DH, false, 8> in workgroups
+// [0, n_qb * H) and, in the workgroups after them, a modulation GEMV (the
+// next block's, in a block stack): those workgroups are dispatched after
+// every attention workgroup, so they run on the CUs that the attention's
+// last, partial round of workgroups leaves idle (432 workgroups on 256 CUs at
+// the Flux shape).  The GEMV rows' arithmetic is that of
+// mod_gemv_multi_kernel.
+template <int DH, int NCH>
+__global__ void __launch_bounds__(512, 1)
+attention_mod_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, int S, int H, int ld_out,
+                     float c_log2, int xcd_remap, int n_qb, const bf16_t* __restrict__ temb, ModTab2 tab,
+                     float* __restrict__ mods, int mod_rows, int mod_cols, int mod_rpw) {
+  using C = AttCfg<DH>;
+  static_assert(NCH * 512 * 4 <= 2 * C::STAGE, "SiLU(temb) must fit the K/V stages");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
+  const int n_att = n_qb * H;
+  if (int(blockIdx.x) >= n_att) {
+    mod_gemv_rows<NCH>(temb, tab, mods, mod_rows, mod_rows, mod_cols, mod_rpw,
+                       (int(blockIdx.x) - n_att) * 8 + int(threadIdx.x >> 6), reinterpret_cast<float*>(smem));
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int bid = blockIdx.x;
+  if (xcd_remap && (n_att & 7) == 0) bid = (bid & 7) * (n_att >> 3) + (bid >> 3);
+  const int qblock = bid % n_qb;
+  const int head = bid / n_qb;
+  const int q = qblock * 256 + wave * 32 + (lane & 31);
+  const int hh = lane >> 5;
+  AttState<DH> st;
+  att_range<DH, 8>(qkv, smem, H, head, min(q, S - 1), 0, S, c_log2, st);
+  const float l_tot = xor32_sum(st.l_run);
+  const float inv = 1.0f / l_tot;
+  if (q < S) att_store_bf16<DH>(st.oacc, inv, out + size_t(q) * ld_out + head * DH, hh);
 }
 
 // Merge of the partial results of disjoint key chunks: with
@@ -448,6 +490,63 @@ static hipError_t launch_fwd(const bf16_t* qkv, bf16_t* out, float* o_part, floa
   }
 #undef DIT_ATT_LAUNCH
   return hipGetLastError();
+}
+
+// The attention launch carries the GEMV when it runs 8-wave workgroups (its
+// last round then leaves CUs idle) and the GEMV's row length is one of the
+// instantiated ones (16-byte chunks per lane: temb widths up to 8192).
+static bool mod_nch_supported(int nch) {
+  return nch == 1 || nch == 2 || nch == 3 || nch == 4 || nch == 6 || nch == 8 || nch == 10 || nch == 12 ||
+         nch == 16;
+}
+
+bool attention_hosts_modulation(int S, int H, int DH, int mod_cols) {
+  if (S <= 0 || (DH != 128 && DH != 64) || mod_cols <= 0 || mod_cols % 8 != 0) return false;
+  if (!mod_nch_supported((mod_cols / 8 + 63) / 64)) return false;
+  return (long long)((S + 255) / 256) * H >= num_cus();
+}
+
+template <int DH>
+static hipError_t launch_att_mod(dim3 grid, int nch, const bf16_t* qkv, bf16_t* out, int S, int H, int ld_out,
+                                 float c, int rm, int n_qb, const bf16_t* temb, const ModTab2& tab, float* mods,
+                                 int mod_rows, int mod_cols, int rpw, hipStream_t st) {
+  switch (nch) {
+#define DIT_ATT_MOD(N)                                                                                            \
+  case N:                                                                                                         \
+    attention_mod_kernel<DH, N><<<grid, dim3(512), 0, st>>>(qkv, out, S, H, ld_out, c, rm, n_qb, temb, tab, mods, \
+                                                            mod_rows, mod_cols, rpw);                             \
+    break;
+    DIT_ATT_MOD(1) DIT_ATT_MOD(2) DIT_ATT_MOD(3) DIT_ATT_MOD(4) DIT_ATT_MOD(6) DIT_ATT_MOD(8) DIT_ATT_MOD(10)
+    DIT_ATT_MOD(12) DIT_ATT_MOD(16)
+#undef DIT_ATT_MOD
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_mod(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
+                                const bf16_t* temb, const bf16_t* w_mod, const bf16_t* b_mod, float* mods,
+                                int mod_rows, int mod_cols, hipStream_t st) {
+  if (!attention_hosts_modulation(S, H, DH, mod_cols) || mod_rows <= 0) return hipErrorInvalidValue;
+  const float c = kLog2e / sqrtf(float(DH));
+  const int rm = att_remap(S, DH);
+  const int n_qb = (S + 255) / 256;
+  const int n_att = n_qb * H;
+  // 9 rows per wave: the GEMV adds ~1/4 of a round of workgroups at the Flux width
+  const int rpw = 9;
+  const int n_mod = (mod_rows + 8 * rpw - 1) / (8 * rpw);
+  ModTab2 tab;
+  tab.ws[0] = w_mod;
+  tab.ws[1] = nullptr;
+  tab.bs[0] = b_mod;
+  tab.bs[1] = nullptr;
+  const int nch = (mod_cols / 8 + 63) / 64;
+  const dim3 grid(n_att + n_mod);
+  if (DH == 128)
+    return launch_att_mod<128>(grid, nch, qkv, out, S, H, ld_out, c, rm, n_qb, temb, tab, mods, mod_rows, mod_cols,
+                               rpw, st);
+  return launch_att_mod<64>(grid, nch, qkv, out, S, H, ld_out, c, rm, n_qb, temb, tab, mods, mod_rows, mod_cols, rpw,
+                            st);
 }
 
 hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,

@@ -130,13 +130,23 @@ struct Probe {
   unsigned long long* ch = nullptr;    // [kProbeChannels][2] for this block
 };
 
-// The six launches of one block on `st`.  x and y may alias.  With mod_pre
-// the modulation vectors were computed beforehand (a stack computes all its
-// blocks' vectors in one launch) and the block's GEMV is skipped.
+// The next block's modulation (W_mod, b_mod, output vectors), computed by a
+// block's attention launch in the CUs its last round leaves idle.
+struct NextMod {
+  const dit_bf16* w_mod;
+  const dit_bf16* b_mod;
+  float* out;
+};
+
+// The launches of one block on `st`.  x and y may alias.  With mod_pre the
+// modulation vectors were computed beforehand (by a stack's step-level
+// launch or by the previous block's attention launch) and the block's GEMV
+// is skipped.  With next (only where attention_hosts_modulation holds), the
+// attention launch also computes the next block's modulation vectors.
 int enqueue_block(const Dims& D, const dit_block_config* cfg, const dit_block_weights* w,
                   const dit_bf16* x, const dit_bf16* temb, const float* rcos, const float* rsin,
                   dit_bf16* y, unsigned char* ws, hipStream_t st, const Probe& pr = Probe(),
-                  const float* mod_pre = nullptr) {
+                  const float* mod_pre = nullptr, const NextMod* next = nullptr) {
   const WsLayout L = layout(D);
   const float* mod = mod_pre ? mod_pre : reinterpret_cast<float*>(ws + L.mod);
   dit_bf16* u = reinterpret_cast<dit_bf16*>(ws + L.u);
@@ -180,7 +190,11 @@ int enqueue_block(const Dims& D, const dit_block_config* cfg, const dit_block_we
     DIT_CHECK_HIP(post(3), "probe");
   }
   DIT_CHECK_HIP(pre(4), "probe");
-  DIT_CHECK_HIP(dit::launch_attention(qkv, cat, D.S, D.H, D.Dh, D.d + D.mlp, st), "attention");
+  if (next)
+    DIT_CHECK_HIP(dit::launch_attention_mod(qkv, cat, D.S, D.H, D.Dh, D.d + D.mlp, temb, next->w_mod, next->b_mod,
+                                            next->out, 3 * D.d, D.tdim, st), "attention + next modulation");
+  else
+    DIT_CHECK_HIP(dit::launch_attention(qkv, cat, D.S, D.H, D.Dh, D.d + D.mlp, st), "attention");
   DIT_CHECK_HIP(post(4), "probe");
   DIT_CHECK_HIP(pre(5), "probe");
   DIT_CHECK_HIP(dit::launch_linear2(cat, w->w2, w->b2, x, mod + 2 * D.d, y, D.S, D.d, D.mlp, st), "linear2");
@@ -777,7 +791,9 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
     st->probe_replays = 0;
   }
   // Every block's modulation depends on temb only: one launch per block kind
-  // computes them all at the start of the step.  Table: W_mod pointers of
+  // computes them all at the start of the step, except that single-stream
+  // blocks after the first get theirs from the previous block's attention
+  // launch where the attention's last round leaves CUs idle.  Table: W_mod pointers of
   // the two-stream blocks' present streams (text first), then of the
   // single-stream blocks; the b_mod pointers after them in the same order.
   // Its host copy stays with the stack; run_steps stages it into the
@@ -794,6 +810,7 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
   float* mods_d = reinterpret_cast<float*>(ws + W.mods);     // [n_dm][6d]
   float* mods_s = mods_d + size_t(n_dm) * 6 * D.d;           // [n_single][3d]
   const int n_streams = W.n_streams;
+  const bool chain_mod = P.n_single > 1 && dit::attention_hosts_modulation(D.S, D.H, D.Dh, D.tdim);
 
   DIT_CHECK_HIP(hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
   int brc = DIT_OK;
@@ -805,8 +822,8 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
     const bool pb = (st->probe_mask & 1u) != 0;
     if (pb) me = dit::launch_probe_stamp(st->probe_buf, 0, st->cap);
     if (me == hipSuccess)
-      me = dit::launch_modulation_multi(tbuf, mod_ptrs + n_dm, mod_ptrs + n_mats + n_dm, mods_s, P.n_single,
-                                        3 * D.d, D.tdim, st->cap);
+      me = dit::launch_modulation_multi(tbuf, mod_ptrs + n_dm, mod_ptrs + n_mats + n_dm, mods_s,
+                                        chain_mod ? 1 : P.n_single, 3 * D.d, D.tdim, st->cap);
     if (me == hipSuccess && pb) me = dit::launch_probe_stamp(st->probe_buf, 1, st->cap);
   }
   if (me != hipSuccess) brc = hip_fail(me, "modulation");
@@ -823,8 +840,11 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
       pr.mask = st->probe_mask;
       pr.ch = st->probe_buf + size_t(b) * kProbeChannels * 2;
     }
+    NextMod nm{nullptr, nullptr, nullptr};
+    if (chain_mod && b + 1 < P.n_single)
+      nm = NextMod{P.singles[b + 1].w_mod, P.singles[b + 1].b_mod, mods_s + size_t(b + 1) * 3 * D.d};
     brc = enqueue_block(D, cfg, &P.singles[b], xin, tbuf, rope_cos, rope_sin, xbuf, ws, st->cap, pr,
-                        mods_s + size_t(b) * 3 * D.d);
+                        mods_s + size_t(b) * 3 * D.d, nm.w_mod ? &nm : nullptr);
   }
   hipGraph_t g = nullptr;
   hipError_t e = hipStreamEndCapture(st->cap, &g);

@@ -96,6 +96,15 @@ hipError_t launch_gated_f32in_group(const GatedArgs* a, const float* const* x32,
 // attention over qkv [S, 3*H*DH] -> out [S, ld_out] columns [0, H*DH)
 hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
                             hipStream_t st);
+// whether launch_attention_mod takes this shape: an attention on 8-wave
+// workgroups whose last round leaves CUs idle, and a supported GEMV width
+bool attention_hosts_modulation(int S, int H, int DH, int mod_cols);
+// the same attention plus, in workgroups dispatched after it, the
+// modulation GEMV mods[r] = W_mod[r] . SiLU(temb) + b_mod[r] (mod_rows rows
+// of mod_cols), bitwise that of launch_modulation
+hipError_t launch_attention_mod(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
+                                const bf16_t* temb, const bf16_t* w_mod, const bf16_t* b_mod, float* mods,
+                                int mod_rows, int mod_cols, hipStream_t st);
 // attention over keys [kv_begin, kv_end): o_part [S, H*DH] fp32, lse [H, S] fp32
 hipError_t launch_attention_partial(const bf16_t* qkv, int S, int H, int DH, int kv_begin, int kv_end,
                                     float* o_part, float* lse, hipStream_t st);
