@@ -712,7 +712,8 @@ def main():
                                 frac=gbs(QKNORM_BYTES, k["qk_rmsnorm_rope_standalone"]) / HBM_PEAK_GBS,
                                 in_graph_us=k["qk_rmsnorm_rope"] * 1e3),
         "modulation": dict(us=k["modulation"] * 1e3, gbs=gbs(MOD_BYTES, k["modulation"]),
-                           frac=gbs(MOD_BYTES, k["modulation"]) / HBM_PEAK_GBS),
+                           frac=gbs(MOD_BYTES, k["modulation"]) / HBM_PEAK_GBS,
+                           blocks_in_attention_launches=nb - 1),
         "block_modulate_norm": dict(us=k["block_modulate_norm"] * 1e3,
                                     gbs=gbs(NORM_BYTES, k["block_modulate_norm"])),
     }
