@@ -374,8 +374,10 @@ def test_linear1_gelu(gpu_lib, S, d, mlp):
 
 
 # ------------------------------------------------------------ linear2 + gated residual
+# (16384, 1536, 8960) and (16000, 1536, 8960) run on 256x192 tiles, the
+# second with a half-filled last tile row
 @pytest.mark.parametrize("S,d,mlp", [(300, 256, 1024), (4608, 3072, 12288), (97, 128, 192), (16384, 1536, 8960),
-                                   (300, 8192, 8192)])
+                                   (16000, 1536, 8960), (300, 8192, 8192)])
 def test_linear2_gated_residual(gpu_lib, S, d, mlp):
     cat = DI.draw(51, (S, d + mlp), 1.0)
     w2 = DI.draw(52, (d, d + mlp), 0.02)
