@@ -371,8 +371,8 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
 }
 
 // The attention of attention_fwd_kernel<DH, false, 8> in workgroups
-// [0, n_qb * H) and, in the workgroups after them, a modulation GEMV (the
-// next block's, in a block stack): those workgroups are dispatched after
+// [0, n_qb * H) and, in the workgroups after them, the modulation GEMVs of
+// one or two matrices (the next block's, in a block stack): those workgroups are dispatched after
 // every attention workgroup, so they run on the CUs that the attention's
 // last, partial round of workgroups leaves idle (432 workgroups on 256 CUs at
 // the Flux shape).  The GEMV rows' arithmetic is that of
@@ -381,13 +381,13 @@ template <int DH, int NCH>
 __global__ void __launch_bounds__(512, 1)
 attention_mod_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, int S, int H, int ld_out,
                      float c_log2, int xcd_remap, int n_qb, const bf16_t* __restrict__ temb, ModTab2 tab,
-                     float* __restrict__ mods, int mod_rows, int mod_cols, int mod_rpw) {
+                     float* __restrict__ mods, int rows_per_mat, int mod_rows, int mod_cols, int mod_rpw) {
   using C = AttCfg<DH>;
   static_assert(NCH * 512 * 4 <= 2 * C::STAGE, "SiLU(temb) must fit the K/V stages");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
   const int n_att = n_qb * H;
   if (int(blockIdx.x) >= n_att) {
-    mod_gemv_rows<NCH>(temb, tab, mods, mod_rows, mod_rows, mod_cols, mod_rpw,
+    mod_gemv_rows<NCH>(temb, tab, mods, rows_per_mat, mod_rows, mod_cols, mod_rpw,
                        (int(blockIdx.x) - n_att) * 8 + int(threadIdx.x >> 6), reinterpret_cast<float*>(smem));
     return;
   }
@@ -509,12 +509,12 @@ bool attention_hosts_modulation(int S, int H, int DH, int mod_cols) {
 template <int DH>
 static hipError_t launch_att_mod(dim3 grid, int nch, const bf16_t* qkv, bf16_t* out, int S, int H, int ld_out,
                                  float c, int rm, int n_qb, const bf16_t* temb, const ModTab2& tab, float* mods,
-                                 int mod_rows, int mod_cols, int rpw, hipStream_t st) {
+                                 int rows_per_mat, int mod_rows, int mod_cols, int rpw, hipStream_t st) {
   switch (nch) {
 #define DIT_ATT_MOD(N)                                                                                            \
   case N:                                                                                                         \
     attention_mod_kernel<DH, N><<<grid, dim3(512), 0, st>>>(qkv, out, S, H, ld_out, c, rm, n_qb, temb, tab, mods, \
-                                                            mod_rows, mod_cols, rpw);                             \
+                                                            rows_per_mat, mod_rows, mod_cols, rpw);               \
     break;
     DIT_ATT_MOD(1) DIT_ATT_MOD(2) DIT_ATT_MOD(3) DIT_ATT_MOD(4) DIT_ATT_MOD(6) DIT_ATT_MOD(8) DIT_ATT_MOD(10)
     DIT_ATT_MOD(12) DIT_ATT_MOD(16)
@@ -525,28 +525,31 @@ static hipError_t launch_att_mod(dim3 grid, int nch, const bf16_t* qkv, bf16_t* 
 }
 
 hipError_t launch_attention_mod(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
-                                const bf16_t* temb, const bf16_t* w_mod, const bf16_t* b_mod, float* mods,
-                                int mod_rows, int mod_cols, hipStream_t st) {
-  if (!attention_hosts_modulation(S, H, DH, mod_cols) || mod_rows <= 0) return hipErrorInvalidValue;
+                                const bf16_t* temb, const bf16_t* w0, const bf16_t* b0, const bf16_t* w1,
+                                const bf16_t* b1, int n_mats, float* mods, int rows_per_mat, int mod_cols,
+                                hipStream_t st) {
+  if (!attention_hosts_modulation(S, H, DH, mod_cols) || rows_per_mat <= 0 || n_mats < 1 || n_mats > 2)
+    return hipErrorInvalidValue;
   const float c = kLog2e / sqrtf(float(DH));
   const int rm = att_remap(S, DH);
   const int n_qb = (S + 255) / 256;
   const int n_att = n_qb * H;
-  // 9 rows per wave: the GEMV adds ~1/4 of a round of workgroups at the Flux width
+  const int mod_rows = n_mats * rows_per_mat;
+  // 9 rows per wave: one block's GEMV (3 x 3072 rows) is 128 workgroups at the Flux width
   const int rpw = 9;
   const int n_mod = (mod_rows + 8 * rpw - 1) / (8 * rpw);
   ModTab2 tab;
-  tab.ws[0] = w_mod;
-  tab.ws[1] = nullptr;
-  tab.bs[0] = b_mod;
-  tab.bs[1] = nullptr;
+  tab.ws[0] = w0;
+  tab.ws[1] = w1;
+  tab.bs[0] = b0;
+  tab.bs[1] = b1;
   const int nch = (mod_cols / 8 + 63) / 64;
   const dim3 grid(n_att + n_mod);
   if (DH == 128)
-    return launch_att_mod<128>(grid, nch, qkv, out, S, H, ld_out, c, rm, n_qb, temb, tab, mods, mod_rows, mod_cols,
-                               rpw, st);
-  return launch_att_mod<64>(grid, nch, qkv, out, S, H, ld_out, c, rm, n_qb, temb, tab, mods, mod_rows, mod_cols, rpw,
-                            st);
+    return launch_att_mod<128>(grid, nch, qkv, out, S, H, ld_out, c, rm, n_qb, temb, tab, mods, rows_per_mat,
+                               mod_rows, mod_cols, rpw, st);
+  return launch_att_mod<64>(grid, nch, qkv, out, S, H, ld_out, c, rm, n_qb, temb, tab, mods, rows_per_mat, mod_rows,
+                            mod_cols, rpw, st);
 }
 
 hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,

@@ -130,13 +130,24 @@ struct Probe {
   unsigned long long* ch = nullptr;    // [kProbeChannels][2] for this block
 };
 
-// The next block's modulation (W_mod, b_mod, output vectors), computed by a
-// block's attention launch in the CUs its last round leaves idle.
+// The next block's modulation, computed by a block's attention launch in
+// the CUs its last round leaves idle: n_mats (1 or 2: a two-stream block's
+// present streams, text first) matrices W_mod of rows_per_mat rows, their
+// biases, and the output vectors [n_mats][rows_per_mat].
 struct NextMod {
-  const dit_bf16* w_mod;
-  const dit_bf16* b_mod;
+  const dit_bf16* w[2];
+  const dit_bf16* b[2];
+  int n_mats, rows_per_mat;
   float* out;
 };
+
+// The attention of a block, with the next block's modulation when `next`.
+hipError_t enqueue_attention(const Dims& D, const dit_bf16* qkv, dit_bf16* out, int ld_out, const dit_bf16* temb,
+                             const NextMod* next, hipStream_t st) {
+  if (!next) return dit::launch_attention(qkv, out, D.S, D.H, D.Dh, ld_out, st);
+  return dit::launch_attention_mod(qkv, out, D.S, D.H, D.Dh, ld_out, temb, next->w[0], next->b[0], next->w[1],
+                                   next->b[1], next->n_mats, next->out, next->rows_per_mat, D.tdim, st);
+}
 
 // The launches of one block on `st`.  x and y may alias.  With mod_pre the
 // modulation vectors were computed beforehand (by a stack's step-level
@@ -190,11 +201,7 @@ int enqueue_block(const Dims& D, const dit_block_config* cfg, const dit_block_we
     DIT_CHECK_HIP(post(3), "probe");
   }
   DIT_CHECK_HIP(pre(4), "probe");
-  if (next)
-    DIT_CHECK_HIP(dit::launch_attention_mod(qkv, cat, D.S, D.H, D.Dh, D.d + D.mlp, temb, next->w_mod, next->b_mod,
-                                            next->out, 3 * D.d, D.tdim, st), "attention + next modulation");
-  else
-    DIT_CHECK_HIP(dit::launch_attention(qkv, cat, D.S, D.H, D.Dh, D.d + D.mlp, st), "attention");
+  DIT_CHECK_HIP(enqueue_attention(D, qkv, cat, D.d + D.mlp, temb, next, st), "attention");
   DIT_CHECK_HIP(post(4), "probe");
   DIT_CHECK_HIP(pre(5), "probe");
   DIT_CHECK_HIP(dit::launch_linear2(cat, w->w2, w->b2, x, mod + 2 * D.d, y, D.S, D.d, D.mlp, st), "linear2");
@@ -234,7 +241,8 @@ MmLayout mm_layout(const Dims& D) {
 // attention and MLP halves (x') stays fp32.  x and y may alias.
 int enqueue_mmdit(const Dims& D, int T, const dit_block_config* cfg, const dit_stream_weights* wt,
                   const dit_stream_weights* wi, const dit_bf16* x, const dit_bf16* temb, const float* rcos,
-                  const float* rsin, dit_bf16* y, unsigned char* ws, hipStream_t st, const float* mod_pre = nullptr) {
+                  const float* rsin, dit_bf16* y, unsigned char* ws, hipStream_t st, const float* mod_pre = nullptr,
+                  const NextMod* next = nullptr) {
   const MmLayout L = mm_layout(D);
   const int d = D.d, mlp = D.mlp, half = D.Dh / 2;
   // mod_pre: the present streams' six vectors, text first, computed beforehand
@@ -279,7 +287,7 @@ int enqueue_mmdit(const Dims& D, int T, const dit_block_config* cfg, const dit_s
       DIT_CHECK_HIP(dit::launch_qk_rmsnorm_rope(qkv + ss[i].r0 * 3 * rd, qn[i].qw, qn[i].kw, qn[i].rcos, qn[i].rsin,
                                                 ss[i].rows, D.H, D.Dh, cfg->qk_eps, st), "qk_rmsnorm_rope");
   }
-  DIT_CHECK_HIP(dit::launch_attention(qkv, o, D.S, D.H, D.Dh, d, st), "attention");
+  DIT_CHECK_HIP(enqueue_attention(D, qkv, o, d, temb, next, st), "attention");
   dit::GatedArgs ga[2];
   float* x1s[2];
   for (int i = 0; i < n; ++i) {
@@ -791,9 +799,10 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
     st->probe_replays = 0;
   }
   // Every block's modulation depends on temb only: one launch per block kind
-  // computes them all at the start of the step, except that single-stream
-  // blocks after the first get theirs from the previous block's attention
-  // launch where the attention's last round leaves CUs idle.  Table: W_mod pointers of
+  // computes them all at the start of the step.  Where the attention's last
+  // round of workgroups leaves CUs idle (chain), the step's launch covers the
+  // first block only and every later block's vectors come from the previous
+  // block's attention launch.  Table: W_mod pointers of
   // the two-stream blocks' present streams (text first), then of the
   // single-stream blocks; the b_mod pointers after them in the same order.
   // Its host copy stays with the stack; run_steps stages it into the
@@ -810,15 +819,27 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
   float* mods_d = reinterpret_cast<float*>(ws + W.mods);     // [n_dm][6d]
   float* mods_s = mods_d + size_t(n_dm) * 6 * D.d;           // [n_single][3d]
   const int n_streams = W.n_streams;
-  const bool chain_mod = P.n_single > 1 && dit::attention_hosts_modulation(D.S, D.H, D.Dh, D.tdim);
+  const bool chain_mod = P.n_double + P.n_single > 1 && dit::attention_hosts_modulation(D.S, D.H, D.Dh, D.tdim);
+  // the vectors of two-stream block b / single-stream block b, produced by the previous block's attention
+  auto double_next = [&](int b) {
+    NextMod nm{{nullptr, nullptr}, {nullptr, nullptr}, 0, 6 * D.d, mods_d + size_t(b) * n_streams * 6 * D.d};
+    if (P.T > 0) nm.w[nm.n_mats] = P.txt[b].w_mod, nm.b[nm.n_mats] = P.txt[b].b_mod, ++nm.n_mats;
+    if (P.T < D.S) nm.w[nm.n_mats] = P.img[b].w_mod, nm.b[nm.n_mats] = P.img[b].b_mod, ++nm.n_mats;
+    return nm;
+  };
+  auto single_next = [&](int b) {
+    return NextMod{{P.singles[b].w_mod, nullptr}, {P.singles[b].b_mod, nullptr}, 1, 3 * D.d,
+                   mods_s + size_t(b) * 3 * D.d};
+  };
 
   DIT_CHECK_HIP(hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
   int brc = DIT_OK;
   hipError_t me = hipSuccess;
-  if (n_dm > 0)
-    me = dit::launch_modulation_multi(tbuf, mod_ptrs, mod_ptrs + n_mats, mods_d, n_dm, 6 * D.d, D.tdim, st->cap);
-  if (me == hipSuccess && P.n_single > 0) {
-    // probes: kernel 0 of block 0 brackets the whole batched launch
+  if (n_dm > 0)  // with chain, the first two-stream block's streams only
+    me = dit::launch_modulation_multi(tbuf, mod_ptrs, mod_ptrs + n_mats, mods_d, chain_mod ? n_streams : n_dm,
+                                      6 * D.d, D.tdim, st->cap);
+  if (me == hipSuccess && P.n_single > 0 && !(chain_mod && P.n_double > 0)) {
+    // probes: kernel 0 of block 0 brackets this launch
     const bool pb = (st->probe_mask & 1u) != 0;
     if (pb) me = dit::launch_probe_stamp(st->probe_buf, 0, st->cap);
     if (me == hipSuccess)
@@ -830,8 +851,12 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
   int idx = 0;  // position in the whole sequence: only block 0 reads x_in
   for (int b = 0; b < P.n_double && brc == DIT_OK; ++b, ++idx) {
     const dit_bf16* xin = (idx == 0 && !chain) ? x_in : xbuf;
+    NextMod nm{};
+    const bool has_next = chain_mod && (b + 1 < P.n_double || P.n_single > 0);
+    if (has_next) nm = b + 1 < P.n_double ? double_next(b + 1) : single_next(0);
     brc = enqueue_mmdit(D, int(P.T), cfg, P.txt ? &P.txt[b] : nullptr, P.img ? &P.img[b] : nullptr, xin, tbuf,
-                        rope_cos, rope_sin, xbuf, ws, st->cap, mods_d + size_t(b) * n_streams * 6 * D.d);
+                        rope_cos, rope_sin, xbuf, ws, st->cap, mods_d + size_t(b) * n_streams * 6 * D.d,
+                        has_next ? &nm : nullptr);
   }
   for (int b = 0; b < P.n_single && brc == DIT_OK; ++b, ++idx) {
     const dit_bf16* xin = (idx == 0 && !chain) ? x_in : xbuf;
@@ -840,11 +865,11 @@ int stack_setup(dit_stack* st, const dit_block_config* cfg, const StackPlan& P, 
       pr.mask = st->probe_mask;
       pr.ch = st->probe_buf + size_t(b) * kProbeChannels * 2;
     }
-    NextMod nm{nullptr, nullptr, nullptr};
-    if (chain_mod && b + 1 < P.n_single)
-      nm = NextMod{P.singles[b + 1].w_mod, P.singles[b + 1].b_mod, mods_s + size_t(b + 1) * 3 * D.d};
+    NextMod nm{};
+    const bool has_next = chain_mod && b + 1 < P.n_single;
+    if (has_next) nm = single_next(b + 1);
     brc = enqueue_block(D, cfg, &P.singles[b], xin, tbuf, rope_cos, rope_sin, xbuf, ws, st->cap, pr,
-                        mods_s + size_t(b) * 3 * D.d, nm.w_mod ? &nm : nullptr);
+                        mods_s + size_t(b) * 3 * D.d, has_next ? &nm : nullptr);
   }
   hipGraph_t g = nullptr;
   hipError_t e = hipStreamEndCapture(st->cap, &g);

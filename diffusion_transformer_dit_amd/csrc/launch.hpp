@@ -100,11 +100,13 @@ hipError_t launch_attention(const bf16_t* qkv, bf16_t* out, int S, int H, int DH
 // workgroups whose last round leaves CUs idle, and a supported GEMV width
 bool attention_hosts_modulation(int S, int H, int DH, int mod_cols);
 // the same attention plus, in workgroups dispatched after it, the
-// modulation GEMV mods[r] = W_mod[r] . SiLU(temb) + b_mod[r] (mod_rows rows
-// of mod_cols), bitwise that of launch_modulation
+// modulation GEMVs of n_mats (1 or 2) matrices of rows_per_mat rows and
+// mod_cols columns: mods[m * rows_per_mat + r] = W_m[r] . SiLU(temb) + b_m[r],
+// bitwise those of launch_modulation / launch_modulation_pair
 hipError_t launch_attention_mod(const bf16_t* qkv, bf16_t* out, int S, int H, int DH, int ld_out,
-                                const bf16_t* temb, const bf16_t* w_mod, const bf16_t* b_mod, float* mods,
-                                int mod_rows, int mod_cols, hipStream_t st);
+                                const bf16_t* temb, const bf16_t* w0, const bf16_t* b0, const bf16_t* w1,
+                                const bf16_t* b1, int n_mats, float* mods, int rows_per_mat, int mod_cols,
+                                hipStream_t st);
 // attention over keys [kv_begin, kv_end): o_part [S, H*DH] fp32, lse [H, S] fp32
 hipError_t launch_attention_partial(const bf16_t* qkv, int S, int H, int DH, int kv_begin, int kv_end,
                                     float* o_part, float* lse, hipStream_t st);

@@ -87,8 +87,11 @@ def test_mixed_stack_replay_equals_eager_bitwise(gpu_lib):
 
 def test_mixed_stack_replay_equals_eager_bitwise_flux_shape(gpu_lib):
     """The Flux composition at the Flux shape (512 text + 4096 image tokens):
-    1 two-stream + 2 single-stream blocks x 2 steps, replayed twice, each
-    step bitwise the eager block forwards.  Seeded device draws; no oracle."""
+    2 two-stream + 2 single-stream blocks x 2 steps, replayed twice, each
+    step bitwise the eager block forwards (at this shape every block after
+    the first gets its modulation vectors from the previous block's
+    attention launch: two-stream -> two-stream, two-stream -> single-stream
+    and single-stream -> single-stream).  Seeded device draws; no oracle."""
     import torch
     B = gpu_lib
     shape = DI.FLUX
@@ -99,7 +102,7 @@ def test_mixed_stack_replay_equals_eager_bitwise_flux_shape(gpu_lib):
     nw = lambda: torch.rand(Dh, generator=g, device="cuda") + 0.5
     stream = lambda: B.StreamWeights(rn(6 * d, d), rn(6 * d), rn(3 * d, d), rn(3 * d), nw(), nw(), rn(d, d), rn(d),
                                      rn(mlp, d), rn(mlp), rn(d, mlp), rn(d))
-    doubles = [(stream(), stream())]
+    doubles = [(stream(), stream()) for _ in range(2)]
     singles = [B.BlockWeights(rn(3 * d, d), rn(3 * d), rn(3 * d + mlp, d), rn(3 * d + mlp), rn(d, d + mlp), rn(d),
                               nw(), nw()) for _ in range(2)]
     x = rn(S, d, s=1.0)
