@@ -304,9 +304,12 @@ int dit_sequential_block_forward(const dit_block_config* cfg, const dit_stream_w
  * the table of the blocks' W_mod / b_mod pointers.  Everything the graph
  * reads or writes is in the caller's workspace: the per-block scratch, the
  * activation carried from block to block, the staged temb, every block's
- * modulation vectors (computed in one launch per block kind at the start of
- * every step), the pointer table (staged with an asynchronous copy on the
- * caller's stream at every replay call) and the timing-probe counters. */
+ * modulation vectors (they depend on temb alone: one launch per block kind
+ * at the start of every step computes them, or, where the attention's last
+ * round of workgroups leaves CUs idle, that launch computes the first
+ * block's and every block's attention launch computes the next block's),
+ * the pointer table (staged with an asynchronous copy on the caller's
+ * stream at every replay call) and the timing-probe counters. */
 typedef struct dit_stack dit_stack;
 
 int dit_stack_create(dit_stack** out);
@@ -388,9 +391,10 @@ int dit_stack_replay_mixed(dit_stack* st, const dit_block_config* cfg, int64_t t
  * by the stack; a bracket around nothing, once per block, measures the
  * probe's own overhead.  The kernels being timed and their results are
  * unchanged; the graph gains 2 + 2*popcount(mask) tiny nodes per block.
- * A stack computes every block's modulation in one launch at the start of
- * the step: kernel 0 of block 0 then reports that whole launch and kernel
- * 0 of the other blocks ~0 (their mean is the per-block share).
+ * A stack's step-level modulation launch is reported as kernel 0 of block
+ * 0 (all blocks' GEMVs, or block 0's alone where the later blocks' run in
+ * the attention launches, which kernel 4 then includes); kernel 0 of the
+ * other blocks reads ~0.
  * kernel_mask bits above 5 -> DIT_ERR_INVALID_ARG. */
 int dit_stack_set_probe(dit_stack* st, uint32_t kernel_mask);
 
