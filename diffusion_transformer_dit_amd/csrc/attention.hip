@@ -372,11 +372,11 @@ attention_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
 
 // The attention of attention_fwd_kernel<DH, false, 8> in workgroups
 // [0, n_qb * H) and, in the workgroups after them, the modulation GEMVs of
-// one or two matrices (the next block's, in a block stack): those workgroups are dispatched after
-// every attention workgroup, so they run on the CUs that the attention's
-// last, partial round of workgroups leaves idle (432 workgroups on 256 CUs at
-// the Flux shape).  The GEMV rows' arithmetic is that of
-// mod_gemv_multi_kernel.
+// one or two matrices (the next block's, in a block stack).  Those
+// workgroups are dispatched after every attention workgroup, so they run on
+// the CUs that the attention's last, partial round of workgroups leaves idle
+// (432 workgroups on 256 CUs at the Flux shape).  The GEMV rows' arithmetic
+// is that of mod_gemv_multi_kernel.
 template <int DH, int NCH>
 __global__ void __launch_bounds__(512, 1)
 attention_mod_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, int S, int H, int ld_out,
@@ -492,9 +492,11 @@ static hipError_t launch_fwd(const bf16_t* qkv, bf16_t* out, float* o_part, floa
   return hipGetLastError();
 }
 
-// The attention launch carries the GEMV when it runs 8-wave workgroups (its
-// last round then leaves CUs idle) and the GEMV's row length is one of the
-// instantiated ones (16-byte chunks per lane: temb widths up to 8192).
+// The attention launch carries the GEMV when it runs 8-wave workgroups, at
+// least one per CU (unless their count is a multiple of the CU count, the
+// last round then leaves CUs idle for the GEMV), and the GEMV's row length
+// is one of the instantiated ones (16-byte chunks per lane: temb widths up
+// to 8192).
 static bool mod_nch_supported(int nch) {
   return nch == 1 || nch == 2 || nch == 3 || nch == 4 || nch == 6 || nch == 8 || nch == 10 || nch == 12 ||
          nch == 16;
