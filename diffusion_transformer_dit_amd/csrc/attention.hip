@@ -27,6 +27,8 @@
 //                 four consecutive rows).  The key order inside each 16-key
 //                 MFMA step is permuted identically on both operands, which
 //                 leaves the contraction unchanged.
+#include <type_traits>
+
 #include "dit_common.hpp"
 #include "launch.hpp"
 #include "mod_gemv.hpp"
@@ -204,8 +206,11 @@ __device__ __forceinline__ void att_range(const bf16_t* __restrict__ qkv, unsign
   issue(kv_begin, 0);
   wait_all();
   __syncthreads();
-  for (int jt = 0; jt < ntiles; ++jt) {
-    const int cur = jt & 1;
+  // One K/V tile; the stage is a compile-time constant (the loop below runs
+  // tiles in pairs), so every LDS read address is a per-lane base plus an
+  // immediate offset, with no per-tile address arithmetic.
+  auto tile = [&](int jt, auto stage_c) {
+    constexpr int cur = decltype(stage_c)::value;
     if (jt + 1 < ntiles) issue(kv_begin + (jt + 1) * ATT_BN, cur ^ 1);
     const unsigned char* st = smem + cur * C::STAGE;
     const int key0 = kv_begin + jt * ATT_BN;
@@ -284,6 +289,10 @@ __device__ __forceinline__ void att_range(const bf16_t* __restrict__ qkv, unsign
     }
     wait_all();
     __syncthreads();
+  };
+  for (int jt = 0; jt < ntiles; jt += 2) {
+    tile(jt, std::integral_constant<int, 0>{});
+    if (jt + 1 < ntiles) tile(jt + 1, std::integral_constant<int, 1>{});
   }
 }
 
