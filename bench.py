@@ -4,16 +4,22 @@
 A step is one denoising step of a 57-block stack of Flux-shaped
 single-stream blocks (S=4608, dim 3072, 24 heads x 128, MLP 12288, bf16,
 independent random weights), replayed as one captured hipGraph per step.
-The headline value is milliseconds per block forward (step time / 57).
-Beside it: per-kernel times from HIP events (GEMM TFLOP/s, attention
-TFLOP/s, fused LayerNorm+modulate and gated-residual HBM GB/s with buffer
-rotation so the 256 MB last-level cache cannot hold the working set), the
-roofline fraction of the dominant kernel, and the CPU oracle's time for one
-block on the host cores.
+The headline value is milliseconds per block forward (step time / 57,
+HIP events on the replay stream around exactly K steps).  Beside it:
+per-kernel times inside the replayed graph (device wall-clock stamp kernels
+around every kernel of every block in a second replay of the same steps:
+GEMM TFLOP/s, attention TFLOP/s), the fused LayerNorm+modulate and
+gated-residual HBM GB/s (graph-timed, with buffer rotation so the 256 MB
+last-level cache cannot hold the working set) against the same-size copy
+probe, the roofline fraction of the dominant kernel with its byte counters,
+kernels per block and launch gaps from a committed rocprofv3 trace, the
+copy and MFMA ceilings, the other configurations and legs, and the CPU
+oracle's time on the host cores.
 
 Prints ONE JSON line on stdout.  Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--blocks 57] [--no-cpu-baseline]
   python bench.py --kernels-only linear1_gelu,copy --kernel-iters 3   (profiler runs)
+  python bench.py --trace-summary <rocprofv3 output dir>               (kernels per block, gaps)
 """
 from __future__ import annotations
 
