@@ -266,9 +266,9 @@ int enqueue_mmdit(const Dims& D, int T, const dit_block_config* cfg, const dit_s
     DIT_CHECK_HIP(dit::launch_modulation_pair(temb, ss[0].w->w_mod, ss[0].w->b_mod, ss[n - 1].w->w_mod,
                                               ss[n - 1].w->b_mod, n, mod0, 6 * d, D.tdim, st),
                   "modulation");
-  for (int i = 0; i < n; ++i)
-    DIT_CHECK_HIP(dit::launch_modulate_norm(x + ss[i].r0 * rd, ss[i].mod, ss[i].mod + d, u + ss[i].r0 * rd,
-                                            ss[i].rows, d, cfg->ln_eps, st), "modulate_norm");
+  // one launch over both streams' rows: rows below T take the text vectors
+  DIT_CHECK_HIP(dit::launch_modulate_norm_pair(x, ss[0].mod, ss[0].mod + d, ss[n - 1].mod, ss[n - 1].mod + d, T, u,
+                                               D.S, d, cfg->ln_eps, st), "modulate_norm");
   // q | k | v of both streams into one [S, 3d] buffer (text rows first)
   dit::BiasActArgs qa[2];
   dit::QKNormArgs qn[2];
@@ -296,10 +296,9 @@ int enqueue_mmdit(const Dims& D, int T, const dit_block_config* cfg, const dit_s
     x1s[i] = x1 + s.r0 * rd;
   }
   DIT_CHECK_HIP(dit::launch_gated_f32out_group(ga, x1s, n, st), "proj");
-  for (int i = 0; i < n; ++i)
-    DIT_CHECK_HIP(dit::launch_modulate_norm(static_cast<const float*>(x1s[i]), ss[i].mod + 3 * d,
-                                            ss[i].mod + 4 * d, u + ss[i].r0 * rd, ss[i].rows, d, cfg->ln_eps, st),
-                  "modulate_norm2");
+  DIT_CHECK_HIP(dit::launch_modulate_norm_pair(static_cast<const float*>(x1), ss[0].mod + 3 * d, ss[0].mod + 4 * d,
+                                               ss[n - 1].mod + 3 * d, ss[n - 1].mod + 4 * d, T, u, D.S, d,
+                                               cfg->ln_eps, st), "modulate_norm2");
   dit::BiasActArgs fa[2];
   for (int i = 0; i < n; ++i) {
     const Stream& s = ss[i];

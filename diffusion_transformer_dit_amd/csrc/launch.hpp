@@ -30,6 +30,14 @@ hipError_t launch_modulate_norm(const bf16_t* x, const float* shift, const float
 // the same with an fp32 input x [rows, cols]
 hipError_t launch_modulate_norm(const float* x, const float* shift, const float* scale,
                                 bf16_t* out, int rows, int cols, float eps, hipStream_t st);
+// the two streams of a two-stream block in one launch: rows [0, split) with
+// (shift0, scale0), rows [split, rows) with (shift1, scale1)
+hipError_t launch_modulate_norm_pair(const bf16_t* x, const float* shift0, const float* scale0, const float* shift1,
+                                     const float* scale1, int split, bf16_t* out, int rows, int cols, float eps,
+                                     hipStream_t st);
+hipError_t launch_modulate_norm_pair(const float* x, const float* shift0, const float* scale0, const float* shift1,
+                                     const float* scale1, int split, bf16_t* out, int rows, int cols, float eps,
+                                     hipStream_t st);
 hipError_t launch_gated_residual(const bf16_t* x, const bf16_t* h, const float* gate, bf16_t* y,
                                  int rows, int cols, hipStream_t st);
 hipError_t launch_qk_rmsnorm_rope(bf16_t* qkv, const float* qw, const float* kw, const float* rcos,
