@@ -10,8 +10,10 @@
 // 3.2) finds these GEMMs dominating the block's timeline before and after
 // fusion; the elementwise work around them is what its section 1.1 fuses.
 //
-// Design: one workgroup of 8 wavefronts owns a BM x BN output tile; two
-// groups of 4 waves each own half of it.  K is walked in BK = 32 slices
+// Two kernels.  The 256 x 256 tile runs the four-wave kernel further down
+// (one wave per SIMD, 128 x 128 per wave, 64-wide K slices).  The other tiles
+// run the ping-pong kernel: one workgroup of 8 wavefronts owns a BM x BN
+// output tile; two groups of 4 waves each own half of it.  K is walked in BK = 32 slices
 // through a ring of 4 LDS buffers filled by direct global->LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land in LDS without passing
 // through registers), issued 3 slices ahead.  The two groups run half a slice
@@ -86,10 +88,25 @@ __device__ __forceinline__ void load_lds_16(const bf16_t* src, unsigned char* ld
 
 // Epilogues act on 4 consecutive columns of one output row (the layout of
 // the transposed MFMA product, see the kernel): col(col0) loads what depends
-// only on the columns, store() finishes and writes one row's 4 values.
+// only on the columns, pre(row, col0) what one row's 4 values need besides
+// the accumulators (the residual of the gated epilogues), and
+// store<Guard>(row, colb, lc, ...) finishes and writes them, at column
+// colb + lc where colb (the 16-column block) is the same for the whole wave.
+// Guard = false when the wave's whole sub-tile is inside M x N: the stores
+// are then unconditional, with no branch around each one (a branch that may
+// skip a store makes the compiler count fewer stores in flight and wait for
+// earlier stores before later loads are used).
+// Loaded values are kept as loaded (bf16 bits) and widened at the store, so
+// that the loads of a batch are all issued before the first wait.
 struct Cols4 {
-  f32x4 a, b;
+  u32x2 a;  // bias (bf16 bits)
+  f32x4 b;  // gate
 };
+struct NoPre {};
+__device__ __forceinline__ f32x4 widen_bf4(const u32x2& w) {
+  return f32x4{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
+}
+__device__ __forceinline__ u32x2 load_raw4(const bf16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ f32x4 load_bf4(const bf16_t* p) {
   const u32x2 w = *reinterpret_cast<const u32x2*>(p);
   return f32x4{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
@@ -108,21 +125,30 @@ struct EpiLinear1 {
   bf16_t* qkv;
   bf16_t* cat;
   int M, N, split, d, ld_qkv, ld_cat, gelu_col0;
+  // columns past N (never stored) read the last 4 columns: no per-lane branch
+  template <bool HasBias>
   __device__ __forceinline__ Cols4 col(int col0) const {
     Cols4 c;
-    c.a = (bias && col0 < N) ? load_bf4(bias + col0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    c.a = HasBias ? load_raw4(bias + min(col0, N - 4)) : u32x2{0u, 0u};
     return c;
   }
-  __device__ __forceinline__ void store(int row, int col0, const Cols4& c, const f32x4& v) const {
-    if (row >= M || col0 >= N) return;  // N and split are multiples of 64
-    f32x4 z = v + c.a;
-    if (col0 < split) {
-      store_bf4(qkv + size_t(row) * ld_qkv + col0, z);
-    } else {
+  using Pre = NoPre;
+  __device__ __forceinline__ Pre pre(int, int) const { return {}; }
+  template <bool Guard>
+  __device__ __forceinline__ void store(int row, int colb, int lc, const Cols4& c, const Pre&, const f32x4& v) const {
+    const int col0 = colb + lc;
+    if (Guard && (row >= M || col0 >= N)) return;
+    f32x4 z = v + widen_bf4(c.a);
+    // split is a multiple of 64: the whole 16-column block is on one side, so
+    // the branch is uniform and holds no memory access; the one store below
+    // is unconditional
+    const bool act = colb >= split;
+    if (act) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[i] = gelu_tanh(z[i]);
-      store_bf4(cat + size_t(row) * ld_cat + gelu_col0 + (col0 - split), z);
     }
+    bf16_t* dst = act ? cat + size_t(row) * ld_cat + gelu_col0 + (col0 - split) : qkv + size_t(row) * ld_qkv + col0;
+    store_bf4(dst, z);
   }
 };
 
@@ -144,29 +170,49 @@ struct EpiLinear1QK : EpiLinear1 {
   // 2d, a multiple of 64); lane columns 4*fk + 16 j + (0..3) of block j.
   // With head_dim 64, blocks j < 4 and j >= 4 are two heads; the q | k
   // boundary (column d) may fall between them.
-  template <int FM, int FN>
+  template <int FM, int FN, bool Guard>
   __device__ __forceinline__ void store_head(int row_base, int colw, int fk, const f32x4 (&acc)[FM][FN]) const {
     static_assert(FN == 8, "128 columns per wave");
     const int hm = head_dim - 1;       // column inside the head = c & hm
     const int half = head_dim >> 1;    // RoPE table row length
     const float inv_hd = head_dim == 128 ? (1.0f / 128.0f) : (1.0f / 64.0f);
-    f32x4 wv[FN], bv[FN];
+    f32x4 wv[FN];
+    u32x2 bv[FN];  // bf16 bits, widened at use
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int c = j * 16 + 4 * fk;  // column inside the wave's 128
       const float* w = colw + c < d ? qw : kw;
       wv[j] = *reinterpret_cast<const f32x4*>(w + (c & hm));
-      bv[j] = bias ? load_bf4(bias + colw + c) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    if (bias) {  // one uniform branch around all the bias loads
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bv[j] = load_raw4(bias + colw + j * 16 + 4 * fk);
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bv[j] = u32x2{0u, 0u};
+    }
+    // the RoPE table entries of row block i+1 are loaded before row block i
+    // is stored (a wait for a load also waits for every store issued before it)
+    f32x2 cs[2][FN], sn[2][FN];
+    auto tables = [&](int buf, int i) {
+      const int rc = min(row_base + 16 * i, M - 1);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int ch = (j * 16 + 4 * fk) & hm;
+        cs[buf][j] = *reinterpret_cast<const f32x2*>(rcos + size_t(rc) * half + ch / 2);
+        sn[buf][j] = *reinterpret_cast<const f32x2*>(rsin + size_t(rc) * half + ch / 2);
+      }
+    };
+    tables(0, 0);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = row_base + 16 * i;
-      const int rc = min(row, M - 1);
+      if (i + 1 < FM) tables((i + 1) & 1, i + 1);
       f32x4 z[FN];
       float s0 = 0.f, s1 = 0.f;  // sums of squares over blocks 0..3 and 4..7
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        z[j] = acc[i][j] + bv[j];
+        z[j] = acc[i][j] + widen_bf4(bv[j]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (j < 4) s0 = fmaf(z[j][e], z[j][e], s0);
@@ -184,19 +230,17 @@ struct EpiLinear1QK : EpiLinear1 {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int c = j * 16 + 4 * fk;
-        const int ch = c & hm;  // column inside the head
         const float r = j < 4 ? r0 : r1;
-        const f32x2 cs = *reinterpret_cast<const f32x2*>(rcos + size_t(rc) * half + ch / 2);
-        const f32x2 sn = *reinterpret_cast<const f32x2*>(rsin + size_t(rc) * half + ch / 2);
+        const f32x2 cj = cs[i & 1][j], sj = sn[i & 1][j];
         f32x4 n;
 #pragma unroll
         for (int e = 0; e < 4; ++e) n[e] = z[j][e] * r * wv[j][e];
         f32x4 o;
-        o[0] = n[0] * cs[0] - n[1] * sn[0];
-        o[1] = n[0] * sn[0] + n[1] * cs[0];
-        o[2] = n[2] * cs[1] - n[3] * sn[1];
-        o[3] = n[2] * sn[1] + n[3] * cs[1];
-        if (row < M) store_bf4(qkv + size_t(row) * ld_qkv + colw + c, o);
+        o[0] = n[0] * cj[0] - n[1] * sj[0];
+        o[1] = n[0] * sj[0] + n[1] * cj[0];
+        o[2] = n[2] * cj[1] - n[3] * sj[1];
+        o[3] = n[2] * sj[1] + n[3] * cj[1];
+        if (!Guard || row < M) store_bf4(qkv + size_t(row) * ld_qkv + colw + c, o);
       }
     }
   }
@@ -209,20 +253,28 @@ struct EpiLinear2 {
   const float* gate;
   bf16_t* y;
   int M, N;
+  // rows and columns past M and N (never stored) read the last ones: no per-lane branch
+  template <bool HasBias>
   __device__ __forceinline__ Cols4 col(int col0) const {
     Cols4 c;
-    c.a = (bias && col0 < N) ? load_bf4(bias + col0) : f32x4{0.f, 0.f, 0.f, 0.f};
-    c.b = col0 < N ? *reinterpret_cast<const f32x4*>(gate + col0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int cc = min(col0, N - 4);
+    c.a = HasBias ? load_raw4(bias + cc) : u32x2{0u, 0u};
+    c.b = *reinterpret_cast<const f32x4*>(gate + cc);
     return c;
   }
-  __device__ __forceinline__ void store(int row, int col0, const Cols4& c, const f32x4& v) const {
-    if (row >= M || col0 >= N) return;
-    const size_t o = size_t(row) * N + col0;
-    const f32x4 xv = load_bf4(x + o);
+  using Pre = u32x2;  // the residual x (bf16 bits)
+  __device__ __forceinline__ Pre pre(int row, int col0) const {
+    return load_raw4(x + size_t(min(row, M - 1)) * N + min(col0, N - 4));
+  }
+  template <bool Guard>
+  __device__ __forceinline__ void store(int row, int colb, int lc, const Cols4& c, const Pre& xr, const f32x4& v) const {
+    const int col0 = colb + lc;
+    if (Guard && (row >= M || col0 >= N)) return;
+    const f32x4 xv = widen_bf4(xr), bv = widen_bf4(c.a);
     f32x4 z;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) z[i] = fmaf(c.b[i], v[i] + c.a[i], xv[i]);
-    store_bf4(y + o, z);
+    for (int i = 0; i < 4; ++i) z[i] = fmaf(c.b[i], v[i] + bv[i], xv[i]);
+    store_bf4(y + size_t(row) * N + col0, z);
   }
 };
 
@@ -242,22 +294,86 @@ struct EpiGated {
   const float* gate;
   YT* y;
   int M, N;
+  // rows and columns past M and N (never stored) read the last ones: no per-lane branch
+  template <bool HasBias>
   __device__ __forceinline__ Cols4 col(int col0) const {
     Cols4 c;
-    c.a = (bias && col0 < N) ? load_bf4(bias + col0) : f32x4{0.f, 0.f, 0.f, 0.f};
-    c.b = col0 < N ? *reinterpret_cast<const f32x4*>(gate + col0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int cc = min(col0, N - 4);
+    c.a = HasBias ? load_raw4(bias + cc) : u32x2{0u, 0u};
+    c.b = *reinterpret_cast<const f32x4*>(gate + cc);
     return c;
   }
-  __device__ __forceinline__ void store(int row, int col0, const Cols4& c, const f32x4& v) const {
-    if (row >= M || col0 >= N) return;
-    const size_t o = size_t(row) * N + col0;
-    const f32x4 xv = load4(x + o);
+  // the residual x as loaded (bf16 bits or fp32)
+  using Pre = std::conditional_t<std::is_same_v<XT, float>, f32x4, u32x2>;
+  __device__ __forceinline__ Pre pre(int row, int col0) const {
+    const XT* p = x + size_t(min(row, M - 1)) * N + min(col0, N - 4);
+    if constexpr (std::is_same_v<XT, float>) return *reinterpret_cast<const f32x4*>(p);
+    else return load_raw4(p);
+  }
+  template <bool Guard>
+  __device__ __forceinline__ void store(int row, int colb, int lc, const Cols4& c, const Pre& xr, const f32x4& v) const {
+    const int col0 = colb + lc;
+    if (Guard && (row >= M || col0 >= N)) return;
+    f32x4 xv;
+    if constexpr (std::is_same_v<XT, float>) xv = xr;
+    else xv = widen_bf4(xr);
+    const f32x4 bv = widen_bf4(c.a);
     f32x4 z;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) z[i] = fmaf(c.b[i], v[i] + c.a[i], xv[i]);
-    store4(y + o, z);
+    for (int i = 0; i < 4; ++i) z[i] = fmaf(c.b[i], v[i] + bv[i], xv[i]);
+    store4(y + size_t(row) * N + col0, z);
   }
 };
+
+// A wave's stores: lane rows row0 + 16 i, columns col0 + 16 j + (0..3).  The
+// column loads come first; the per-row loads of column block j+1 are issued
+// before block j is stored.  The vector-memory counter counts loads and
+// stores alike and completes in issue order, so a wait for a load issued
+// after some stores would also wait for those stores to drain.
+template <int FM, int FN, bool Guard, class Epi>
+__device__ __forceinline__ void store_tile(const Epi& epi, int row0, int colb0, int lc, const f32x4 (&acc)[FM][FN]) {
+  Cols4 c[FN];
+  if (epi.bias) {  // one uniform branch around all the column loads
+#pragma unroll
+    for (int j = 0; j < FN; ++j) c[j] = epi.template col<true>(colb0 + 16 * j + lc);
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) c[j] = epi.template col<false>(colb0 + 16 * j + lc);
+  }
+  typename Epi::Pre p[2][FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) p[0][i] = epi.pre(row0 + 16 * i, colb0 + lc);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    if (j + 1 < FN) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) p[(j + 1) & 1][i] = epi.pre(row0 + 16 * i, colb0 + 16 * (j + 1) + lc);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      epi.template store<Guard>(row0 + 16 * i, colb0 + 16 * j, lc, c[j], p[j & 1][i], acc[i][j]);
+  }
+}
+
+// A wave's whole epilogue: the q/k head path for the tiles whose waves own
+// whole heads, otherwise store_tile; unguarded stores when the wave's
+// sub-tile lies inside the output.
+template <int FM, int FN, class Epi>
+__device__ __forceinline__ void wave_epilogue(const Epi& epi, int M, int N, int rw, int cw, int fr, int fk,
+                                              const f32x4 (&acc)[FM][FN]) {
+  rw = __builtin_amdgcn_readfirstlane(rw);  // the wave's first row and column: uniform
+  cw = __builtin_amdgcn_readfirstlane(cw);
+  const bool full = rw + 16 * FM <= M && cw + 16 * FN <= N;
+  if constexpr (Epi::kHeadNorm && FN == 8) {
+    if (cw < 2 * epi.d) {  // a whole head: q or k columns get normalised and rotated
+      if (full) epi.template store_head<FM, FN, false>(rw + fr, cw, fk, acc);
+      else epi.template store_head<FM, FN, true>(rw + fr, cw, fk, acc);
+      return;
+    }
+  }
+  if (full) store_tile<FM, FN, false>(epi, rw + fr, cw, 4 * fk, acc);
+  else store_tile<FM, FN, true>(epi, rw + fr, cw, 4 * fk, acc);
+}
 
 // One GEMM of a launch: C = A B^T with A [M, K], B [N, K], finished by epi.
 template <class Epi>
@@ -434,25 +550,192 @@ gemm_bf16_tn_kernel(GemmGroup<Epi, NP> grp) {
   // The MFMAs compute the transposed product C^T = B A^T per 16x16 block, so
   // lane l holds row (l & 15) of the block and its 4 consecutive columns
   // 4*(l >> 4) + (0..3): one 8-byte store per block and lane.
-  if constexpr (Epi::kHeadNorm && C::WN == 128) {
-    const int colw = n0 + wn * C::WN;  // a whole head: q or k columns get normalised and rotated
-    if (colw < 2 * epi.d) {
-      epi.template store_head<C::FM, C::FN>(m0 + wm * C::WM + fr, colw, fk, acc);
-      return;
+  wave_epilogue<C::FM, C::FN>(epi, M, N, m0 + wm * C::WM, n0 + wn * C::WN, fr, fk, acc);
+}
+
+// ------------------------------------------------------------ four-wave kernel
+// One wave per SIMD: 4 waves in a 2 x 2 grid, each owning a (BM/2) x (BN/2)
+// sub-tile whose fp32 accumulators live in the accumulation registers.  K is
+// walked in slices of 64 (128-byte rows: every refill request covers a whole
+// 128-byte cache line, half as many L2 requests as 64-byte rows need) through
+// two LDS slots.  A wave streams its own MFMAs and, between them, reads the
+// next half-slice's operands from LDS and issues its share of the refill, so
+// a 128 x 128 sub-tile reads 0.25 operand fragments per MFMA and one
+// workgroup barrier is needed per slice.  Same K order, MFMA and operand
+// pairing as the ping-pong kernel, so both produce bitwise the same results.
+template <int BM_, int BN_>
+struct Tile4Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = 64, NSTAGE = 2;
+  static constexpr int WAVES_M = 2, WAVES_N = 2, NW = 4, NT = 256;
+  static constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
+  static constexpr int ROW_BYTES = BK * 2;  // 128
+  static constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  // one wave-load = 64 lanes x 16 bytes = 8 rows of a slice
+  static constexpr int A_WL = BM / 8, B_WL = BN / 8, WL = A_WL + B_WL;
+  static constexpr int LA = A_WL / NW, LB = B_WL / NW, L = LA + LB;  // wave-loads per wave per slice
+  static constexpr int LDS_BYTES = NSTAGE * STAGE;
+  static_assert(A_WL % NW == 0 && B_WL % NW == 0, "every wave issues the same number of loads");
+  static_assert(FM == 8 && FN == 8 && L == 16, "the interleave is written for 128 x 128 sub-tiles");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
+};
+
+// 16-byte chunk c of a 128-byte row r sits at position c ^ ((r >> 1) & 7): the
+// 16 rows of a fragment read then cover the 64 banks once per 16 lanes.
+__device__ __forceinline__ int row_swz8(int r) { return (r >> 1) & 7; }
+
+// Buffer descriptor over `bytes` bytes from `base` (raw, 32-bit data format):
+// loads at offsets past the range read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel_rsrc(const bf16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), 0, int(bytes), 0x00020000);
+}
+
+// acc += B-fragment x A-fragment (the transposed product, as in the ping-pong
+// kernel) with the accumulator pinned to an accumulation register: written as
+// the instruction itself so that the compiler neither copies the 256
+// accumulators between register files nor spills them.  Each accumulator is
+// written once per 64 MFMAs here, so no dependent pair is adjacent; the reads
+// after the last one are preceded by explicit wait states (mfma_drain).
+__device__ __forceinline__ void mfma_acc(f32x4& acc, const bf16x8& b, const bf16x8& a) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+// the first product of a tile: acc = B-fragment x A-fragment (zero accumulator input)
+__device__ __forceinline__ void mfma_first(f32x4& acc, const bf16x8& b, const bf16x8& a) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(b), "v"(a));
+}
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+template <class C, class Epi, int NP>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm4w_kernel(GemmGroup<Epi, NP> grp) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
+  int bid = xcd_block_id();
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < NP; ++i)
+    if (bid >= grp.first[i]) pi = i;
+  bid -= grp.first[pi];
+  const bf16_t* __restrict__ A = grp.p[pi].A;
+  const bf16_t* __restrict__ B = grp.p[pi].B;
+  const int M = grp.p[pi].M, N = grp.p[pi].N, K = grp.p[pi].K;
+  const Epi& epi = grp.p[pi].epi;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
+  int tm, tn;
+  tile_coords<4>(bid, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+
+  // Refill loads through buffer descriptors over the tile's A and B row
+  // panels (rows past M or N read as zero and are never stored).  Wave w
+  // issues wave-loads j = w + 4 i (A for i < LA, then B): lane l fetches row
+  // 8 j + l/8 of its panel, global chunk (l % 8) ^ swz8(row), into LDS bytes
+  // [16 l, 16 l + 16) of the j-th 1 KB block of the slice.  The per-lane
+  // offset is the same for every load; the row block and the slice go into
+  // the scalar offset.
+  const int lrow = lane >> 3;
+  const __amdgpu_buffer_rsrc_t ra = panel_rsrc(A + size_t(m0) * K, uint32_t(min(C::BM, M - m0)) * uint32_t(K) * 2u);
+  const __amdgpu_buffer_rsrc_t rb = panel_rsrc(B + size_t(n0) * K, uint32_t(min(C::BN, N - n0)) * uint32_t(K) * 2u);
+  const int kb = K * 2;  // bytes per row
+  const int voff0 = (8 * wave + lrow) * kb;
+  const int blk_stride = 32 * kb;  // 32 rows: the next load of the same wave
+  // row 8 (w + 4 i) + lrow has swz8 = (4 (w + 4 i) + (lrow >> 1)) & 7 = (4 w + (lrow >> 1)) & 7,
+  // the same for every load of the wave
+  const int voff = voff0 + (((lane & 7) ^ ((4 * wave + (lrow >> 1)) & 7)) * 16);
+  auto issue1 = [&](int i, int kt, uint32_t sbase) {
+    const bool isa = i < C::LA;
+    const int ii = isa ? i : i - C::LA;
+    const int soff = ii * blk_stride + kt * (C::BK * 2);
+    unsigned char* dst = smem + sbase + (isa ? 0u : uint32_t(C::A_BYTES)) + uint32_t(wave + 4 * ii) * 1024u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isa ? ra : rb, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
+  };
+
+  f32x4 acc[C::FM][C::FN];  // born in the accumulation registers by the first MFMAs
+
+  // Fragment reads: lane holds row (lane & 15) of a 16-row block and the 8
+  // K-values of chunk 4 h + (lane >> 4) of half-slice h.
+  const int fr = lane & 15;
+  const int fk = lane >> 4;
+  const uint32_t a_row = uint32_t(wm * C::WM + fr) * C::ROW_BYTES;
+  const uint32_t b_row = C::A_BYTES + uint32_t(wn * C::WN + fr) * C::ROW_BYTES;
+  // position of chunk 4 h + fk in row fr (+ 16 i: bits 1..3 of the row do not change)
+  const uint32_t sw0 = uint32_t(((0 + fk) ^ row_swz8(fr)) << 4), sw1 = uint32_t(((4 + fk) ^ row_swz8(fr)) << 4);
+  bf16x8 fa[2][C::FM], fb[2][C::FN];
+  // half-slice h of the slice in the LDS slot at sb into buffer buf: B first
+  auto read_b = [&](int buf, int j, const unsigned char* sb, uint32_t sw) {
+    fb[buf][j] = *reinterpret_cast<const bf16x8*>(sb + b_row + sw + j * 16 * C::ROW_BYTES);
+  };
+  auto read_a = [&](int buf, int i, const unsigned char* sb, uint32_t sw) {
+    fa[buf][i] = *reinterpret_cast<const bf16x8*>(sb + a_row + sw + i * 16 * C::ROW_BYTES);
+  };
+
+  const int KT = K / C::BK;  // >= 1
+  // prologue: slices 0 and 1 in flight (a slice past the end re-fetches the
+  // last one into a slot nobody reads), half-slice 0 of slice 0 in registers
+#pragma unroll
+  for (int i = 0; i < C::L; ++i) issue1(i, 0, 0);
+#pragma unroll
+  for (int i = 0; i < C::L; ++i) issue1(i, min(1, KT - 1), C::STAGE);
+  wait_cnt<C::L, 15>();
+  block_barrier();
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) read_b(0, j, smem, sw0);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) read_a(0, i, smem, sw0);
+
+  // Slice k in slot k & 1.  Phase 0: multiply half 0 (buffer 0) while
+  // reading half 1 of the same slot into buffer 1.  Then this wave's loads
+  // of slice k+1 have landed and its reads are done; a barrier makes that
+  // hold for every wave.  Phase 1: multiply half 1 while reading half 0 of
+  // slice k+1 (the other slot) and refilling slot k & 1 with slice k+2.
+  auto phase = [&](int k, auto ph_c, auto first_c) {
+    constexpr int cur = decltype(ph_c)::value, nxt = cur ^ 1;
+    constexpr bool first = decltype(first_c)::value;
+    const uint32_t slot = uint32_t(k & 1) * C::STAGE;
+    const unsigned char* sb = smem + (cur == 0 ? slot : slot ^ uint32_t(C::STAGE));
+    const uint32_t sw = cur == 0 ? sw1 : sw0;
+    const int kl = min(k + 2, KT - 1);
+#pragma unroll
+    for (int g = 0; g < C::FM; ++g) {
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        if constexpr (first) mfma_first(acc[g][j], fb[cur][j], fa[cur][g]);
+        else mfma_acc(acc[g][j], fb[cur][j], fa[cur][g]);
+      }
+      // the next half's B fragments first: its first row block needs all of
+      // them but only its first A fragment
+      if (g < C::FM / 2) {
+        read_b(nxt, 2 * g, sb, sw);
+        read_b(nxt, 2 * g + 1, sb, sw);
+      } else {
+        read_a(nxt, 2 * (g - C::FM / 2), sb, sw);
+        read_a(nxt, 2 * (g - C::FM / 2) + 1, sb, sw);
+      }
+      if constexpr (cur == 1) {
+        issue1(2 * g, kl, slot);
+        issue1(2 * g + 1, kl, slot);
+      }
     }
-  }
-#pragma unroll
-  for (int j = 0; j < C::FN; ++j) {
-    const int col0 = n0 + wn * C::WN + j * 16 + 4 * fk;
-    const Cols4 c = epi.col(col0);
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) epi.store(m0 + wm * C::WM + i * 16 + fr, col0, c, acc[i][j]);
-  }
+  };
+  auto slice = [&](int k, auto first_c) {
+    phase(k, std::integral_constant<int, 0>{}, first_c);
+    wait_cnt<0, 0>();
+    block_barrier();
+    phase(k, std::integral_constant<int, 1>{}, std::false_type{});
+  };
+  slice(0, std::true_type{});
+  for (int k = 1; k < KT; ++k) slice(k, std::false_type{});
+  mfma_drain();
+  wait_cnt<0, 0>();  // the tail's re-fetches land before the workgroup ends
+
+  wave_epilogue<C::FM, C::FN>(epi, M, N, m0 + wm * C::WM, n0 + wn * C::WN, fr, fk, acc);
 }
 
 // ------------------------------------------------------------------ tile choice
 using T288x192 = TileCfg<288, 192, 2, 4, 4>;  // 8 waves of 144 x 48; groups own 144-row halves
-using T256 = TileCfg<256, 256, 4, 2, 4>;      // 8 waves of 64 x 128; groups own 128-row halves
+using T256 = Tile4Cfg<256, 256>;              // 4 waves of 128 x 128, 64-wide K slices
 using T128x256 = TileCfg<128, 256, 4, 2, 4>;  // 8 waves of 32 x 128 (whole heads per wave, small M)
 using T256x192 = TileCfg<256, 192, 4, 2, 4>;  // 8 waves of 64 x 96 (N = 1536 in 8 tiles: two full rounds at S = 16384)
 using T128 = TileCfg<128, 128, 4, 2, 4>;      // 8 waves of 32 x 64
@@ -509,7 +792,10 @@ static hipError_t launch_tile(const bf16_t* A, const bf16_t* B, int M, int N, in
   GemmGroup<Epi, 1> g;
   g.p[0] = GemmProblem<Epi>{A, B, M, N, K, e};
   g.first[0] = 0;
-  gemm_bf16_tn_kernel<C, Epi, 1><<<tiles, C::NT, 0, st>>>(g);
+  if constexpr (C::NW == 4)
+    gemm4w_kernel<C, Epi, 1><<<tiles, C::NT, 0, st>>>(g);
+  else
+    gemm_bf16_tn_kernel<C, Epi, 1><<<tiles, C::NT, 0, st>>>(g);
   return hipGetLastError();
 }
 
@@ -528,7 +814,10 @@ static hipError_t launch_tile_group(const GemmProblem<Epi>* ps, int np, hipStrea
   }
   if (n == 0) return hipSuccess;
   if (n == 1) return launch_tile<C>(g.p[0].A, g.p[0].B, g.p[0].M, g.p[0].N, g.p[0].K, g.p[0].epi, st);
-  gemm_bf16_tn_kernel<C, Epi, 2><<<tiles, C::NT, 0, st>>>(g);
+  if constexpr (C::NW == 4)
+    gemm4w_kernel<C, Epi, 2><<<tiles, C::NT, 0, st>>>(g);
+  else
+    gemm_bf16_tn_kernel<C, Epi, 2><<<tiles, C::NT, 0, st>>>(g);
   return hipGetLastError();
 }
 
