@@ -63,11 +63,13 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // GELU, tanh form: 0.5 g (1 + tanh(u)) with u = sqrt(2/pi) (g + 0.044715 g^3).
-// Since 0.5 (1 + tanh(u)) = 1 / (1 + e^{-2u}), this is g / (1 + 2^{-2u log2 e}).
+// Since 0.5 (1 + tanh(u)) = 1 / (1 + e^{-2u}), this is g / (1 + 2^{-2u log2 e}),
+// and -2u log2 e = g (k0 + k1 g^2) with the constants folded: 4 VALU + 2
+// transcendentals + 1 add per value.
 __device__ __forceinline__ float gelu_tanh(float g) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  float u = c * (g + 0.044715f * g * g * g);
-  return g * rcp_fast(1.0f + exp2_fast(-2.0f * kLog2e * u));
+  constexpr float k0 = -2.0f * kLog2e * 0.7978845608028654f;  // sqrt(2/pi)
+  constexpr float k1 = k0 * 0.044715f;
+  return g * rcp_fast(1.0f + exp2_fast(g * fmaf(k1, g * g, k0)));
 }
 
 __device__ __forceinline__ float silu(float z) { return z * rcp_fast(1.0f + exp2_fast(-kLog2e * z)); }
