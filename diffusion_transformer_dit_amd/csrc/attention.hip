@@ -71,11 +71,6 @@ __device__ __forceinline__ void buffer_load_lds_16(__amdgpu_buffer_rsrc_t r, uns
 __device__ __forceinline__ u32x2 read_tr16(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p));
 }
-// max / sum of the values held by lanes l and l^32
-__device__ __forceinline__ float xor32_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 // pairwise sum of 16 values (a tree of depth 4 instead of a serial chain)
 __device__ __forceinline__ float sum16(const float* e) {
   float s8[8], s4[4];
@@ -102,10 +97,6 @@ __device__ __forceinline__ float pack_p(const float* e, u32x4* p) {
       s[t & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, s[t & 1], false);
     }
   return s[0] + s[1];
-}
-__device__ __forceinline__ float xor32_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 

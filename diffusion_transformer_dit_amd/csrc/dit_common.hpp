@@ -44,6 +44,23 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
   return v;
 }
 
+// max / sum of the values held by lanes l and l^32, or l^16, on the lane-swap
+// instructions (no LDS round trip): with both operands v, the swap's two
+// results hold v and its partner, in an order that differs between the halves;
+// max and sum do not depend on it (IEEE addition commutes).
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum / max over the 64 lanes of a wavefront (butterfly; every lane gets the result).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -220,10 +220,8 @@ struct EpiLinear1QK : EpiLinear1 {
         }
       }
       // a row's 128 values sit in lanes fr + 16 fk, fk = 0..3
-      s0 += __shfl_xor(s0, 16, 64);
-      s0 += __shfl_xor(s0, 32, 64);
-      s1 += __shfl_xor(s1, 16, 64);
-      s1 += __shfl_xor(s1, 32, 64);
+      s0 = xor32_sum(xor16_sum(s0));
+      s1 = xor32_sum(xor16_sum(s1));
       if (head_dim == 128) s0 = s1 = s0 + s1;
       const float r0 = __frsqrt_rn(s0 * inv_hd + eps);
       const float r1 = __frsqrt_rn(s1 * inv_hd + eps);
