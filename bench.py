@@ -379,21 +379,25 @@ def ceiling_times(B, g, dev, reps=3):
 
 def library_gemm_times(g, dev, reps=3):
     """The vendor library on the same GEMM shapes, for comparison only:
-    torch.matmul (hipBLASLt) of u [S, d] by W1^T [d, N1] and of the concat
-    buffer [S, N2] by W2^T [N2, d], bf16 in and out, no epilogue, captured in
-    a graph and replayed.  The weights are stored [out, in] as in the block,
-    so the right operand is a transposed view (made contiguous first)."""
+    torch.matmul (hipBLASLt) of u [S, d] by W1^T and of the concat buffer
+    [S, N2] by W2^T, bf16 in and out, no epilogue, captured in a graph and
+    replayed.  "tn": the weight stored [out, in] as the block's kernels take
+    it (both operands K-contiguous; the right operand is a transposed view of
+    a 2-D weight, a plain matrix product); "nn": the weight made contiguous
+    as [in, out] first, a different problem for the library."""
     import torch
     res = {}
     for name, (m, k, n, flop) in (("linear1", (S, D, N1, GEMM1_FLOP)), ("linear2", (S, N2, D, GEMM2_FLOP))):
         a = (torch.randn(m, k, generator=g, device=dev)).to(torch.bfloat16)
         w = (torch.randn(n, k, generator=g, device=dev) * 0.02).to(torch.bfloat16)
-        wt = w.t().contiguous()
         out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
-        ms = time_graph(lambda i: torch.matmul(a, wt, out=out), 4, reps)
-        tfl = flop / (ms * 1e-3) / 1e12
-        res[name] = dict(us=round(ms * 1e3, 1), tflops=round(tfl, 1), frac=round(tfl / BF16_PEAK_TFLOPS, 4))
-        del a, w, wt, out
+        for layout, rhs in (("tn", w.t()), ("nn", w.t().contiguous())):
+            ms = time_graph(lambda i: torch.matmul(a, rhs, out=out), 4, reps)
+            tfl = flop / (ms * 1e-3) / 1e12
+            res[f"{name}_{layout}"] = dict(us=round(ms * 1e3, 1), tflops=round(tfl, 1),
+                                           frac=round(tfl / BF16_PEAK_TFLOPS, 4))
+            del rhs
+        del a, w, out
     torch.cuda.synchronize()
     return res
 
@@ -431,7 +435,7 @@ def trace_summary(path, n_blocks=57):
     with open(path) as f:
         rows = list(csv.DictReader(f))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    block_kernels = ("gemm_bf16_tn_kernel", "attention_fwd_kernel", "attention_mod_kernel", "ln_modulate_kernel",
+    block_kernels = ("gemm_bf16_tn_kernel", "gemm4w_kernel", "attention_fwd_kernel", "attention_mod_kernel", "ln_modulate_kernel",
                      "qk_rmsnorm_rope_kernel", "mod_gemv")
     is_block = lambda name: any(k in name for k in block_kernels)
     steps = []

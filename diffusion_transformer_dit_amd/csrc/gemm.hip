@@ -734,6 +734,20 @@ gemm4w_kernel(GemmGroup<Epi, NP> grp) {
 // ------------------------------------------------------------------ tile choice
 using T288x192 = TileCfg<288, 192, 2, 4, 4>;  // 8 waves of 144 x 48; groups own 144-row halves
 using T256 = Tile4Cfg<256, 256>;              // 4 waves of 128 x 128, 64-wide K slices
+using T256pp = TileCfg<256, 256, 4, 2, 4>;    // the same tile on the ping-pong kernel (8 waves of 64 x 128)
+// The four-wave kernel's refills have one phase of lead (two 64 KB slots),
+// the ping-pong kernel's three 32-wide slices.  For long K both operands
+// stream from HBM (fc2 of the two-stream block: K = 12288, 402 against
+// 347 us) and the deeper prefetch wins.  An epilogue that loads a residual
+// per output (the gated ones) has its latency hidden only with two waves per
+// SIMD (two-stream output projection: 132 against 115 us).  Otherwise (the
+// linear1 epilogues at K = d) the four-wave kernel's larger sub-tiles and
+// whole-line refills win.
+constexpr int kFourWaveMaxK = 4096;
+template <class Epi>
+constexpr bool four_wave(int K) {
+  return std::is_same_v<typename Epi::Pre, NoPre> && K <= kFourWaveMaxK;
+}
 using T128x256 = TileCfg<128, 256, 4, 2, 4>;  // 8 waves of 32 x 128 (whole heads per wave, small M)
 using T256x192 = TileCfg<256, 192, 4, 2, 4>;  // 8 waves of 64 x 96 (N = 1536 in 8 tiles: two full rounds at S = 16384)
 using T128 = TileCfg<128, 128, 4, 2, 4>;      // 8 waves of 32 x 64
@@ -834,7 +848,10 @@ static hipError_t launch_gemm_group(const GemmProblem<Epi>* ps, int np, hipStrea
   if (np < 1 || np > 2) return hipErrorInvalidValue;
   switch (choose_group_tile(ps, np)) {
     case K288x192: return launch_tile_group<T288x192>(ps, np, st);
-    case K256: return launch_tile_group<T256>(ps, np, st);
+    case K256:
+      if constexpr (std::is_same_v<typename Epi::Pre, NoPre>)  // the four-wave kernel is built only for these
+        if (four_wave<Epi>(ps[0].K)) return launch_tile_group<T256>(ps, np, st);
+      return launch_tile_group<T256pp>(ps, np, st);
     case K256x192: return launch_tile_group<T256x192>(ps, np, st);
     default: return launch_tile_group<T128>(ps, np, st);
   }
@@ -846,7 +863,10 @@ static hipError_t launch_gemm(const bf16_t* A, const bf16_t* B, int M, int N, in
   if (M == 0 || N == 0) return hipSuccess;
   switch (choose_tile(M, N)) {
     case K288x192: return launch_tile<T288x192>(A, B, M, N, K, e, st);
-    case K256: return launch_tile<T256>(A, B, M, N, K, e, st);
+    case K256:
+      if constexpr (std::is_same_v<typename Epi::Pre, NoPre>)
+        if (four_wave<Epi>(K)) return launch_tile<T256>(A, B, M, N, K, e, st);
+      return launch_tile<T256pp>(A, B, M, N, K, e, st);
     case K256x192: return launch_tile<T256x192>(A, B, M, N, K, e, st);
     default: return launch_tile<T128>(A, B, M, N, K, e, st);
   }
@@ -876,7 +896,8 @@ hipError_t launch_linear1_qk(const bf16_t* u, const bf16_t* w1, const bf16_t* b1
   e.eps = eps;
   e.head_dim = DH;
   const int N = 3 * d + mlp;
-  if (choose_tile(&S, &N, 1, true) == K256) return launch_tile<T256>(u, w1, S, N, d, e, st);
+  if (choose_tile(&S, &N, 1, true) == K256)
+    return four_wave<EpiLinear1QK>(d) ? launch_tile<T256>(u, w1, S, N, d, e, st) : launch_tile<T256pp>(u, w1, S, N, d, e, st);
   return launch_tile<T128x256>(u, w1, S, N, d, e, st);
 }
 
@@ -922,7 +943,8 @@ hipError_t launch_bias_act_qk_group(const BiasActArgs* a, const QKNormArgs* q, i
     Ms[i] = a[i].M;
     Ns[i] = a[i].N;
   }
-  if (choose_tile(Ms, Ns, np, true) == K256) return launch_tile_group<T256>(ps, np, st);
+  if (choose_tile(Ms, Ns, np, true) == K256)
+    return four_wave<EpiLinear1QK>(ps[0].K) ? launch_tile_group<T256>(ps, np, st) : launch_tile_group<T256pp>(ps, np, st);
   return launch_tile_group<T128x256>(ps, np, st);
 }
 
