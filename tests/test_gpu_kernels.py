@@ -355,8 +355,11 @@ def test_attention_partial_rejects_bad_ranges(gpu_lib):
 
 
 # ------------------------------------------------------------ linear1 + GELU
-# (300, 8192, 8192): the largest dim the row kernels accept
-@pytest.mark.parametrize("S,d,mlp", [(300, 256, 1024), (4608, 3072, 12288), (97, 128, 192), (300, 8192, 8192)])
+# (300, 8192, 8192): the largest dim the row kernels accept.  (3000, 64, 4288),
+# (3000, 128, 4096) and (3000, 256, 3776) run on the four-wave 256x256 kernel
+# with a partial last tile row and column and 1, 2 and 4 K slices of 64.
+@pytest.mark.parametrize("S,d,mlp", [(300, 256, 1024), (4608, 3072, 12288), (97, 128, 192), (300, 8192, 8192),
+                                   (3000, 64, 4288), (3000, 128, 4096), (3000, 256, 3776)])
 def test_linear1_gelu(gpu_lib, S, d, mlp):
     import torch
     u = DI.draw(41, (S, d), 1.0)
@@ -396,6 +399,20 @@ def test_linear2_gated_residual(gpu_lib, S, d, mlp):
                                         dev_bf16(np.zeros((S, d), np.float32)), dev_f32(np.ones(d, np.float32)),
                                         dev_bf16(np.zeros((S, d), np.float32)))
     assert_parity(host(hb)[rows], h, f"linear2 branch S={S}")
+
+
+def test_linear1_gelu_without_bias(gpu_lib):
+    """The epilogue path without a bias (no column loads), four-wave kernel, partial edge tiles."""
+    import torch
+    S, d, mlp = 3000, 256, 3776
+    u = DI.draw(44, (S, d), 1.0)
+    w1 = DI.draw(45, (3 * d + mlp, d), 0.02)
+    qkv = torch.empty(S, 3 * d, dtype=torch.bfloat16, device="cuda")
+    cat = torch.zeros(S, d + mlp, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.linear1_gelu(dev_bf16(u), dev_bf16(w1), None, qkv, cat, mlp)
+    z = O.linear(u, w1)
+    assert_parity(host(qkv), z[:, :3 * d], "linear1 qkv, no bias")
+    assert_parity(host(cat)[:, d:], O.gelu_tanh(z[:, 3 * d:]), "linear1 gelu, no bias")
 
 
 def test_linear2_in_place(gpu_lib):
