@@ -121,6 +121,7 @@ __device__ __forceinline__ void store_bf4(bf16_t* p, const f32x4& v) {
 // norm of EpiLinear1QK.
 struct EpiLinear1 {
   static constexpr bool kHeadNorm = false;
+  static constexpr bool kRowStore = true;
   const bf16_t* bias;
   bf16_t* qkv;
   bf16_t* cat;
@@ -150,6 +151,31 @@ struct EpiLinear1 {
     bf16_t* dst = act ? cat + size_t(row) * ld_cat + gelu_col0 + (col0 - split) : qkv + size_t(row) * ld_qkv + col0;
     store_bf4(dst, z);
   }
+  // A wave's whole sub-tile inside M x N with all its columns [colb0, colb0 +
+  // 16 FN) on one side of split (act, uniform: the GELU side): one row
+  // address per row block, the column blocks at immediate offsets from it,
+  // so a store costs no address arithmetic.  One code path for both sides
+  // (a uniform branch around the GELU): with two, the compiler moves every
+  // accumulator out of the accumulation registers ahead of the branch.
+  template <int FM, int FN>
+  __device__ __forceinline__ void store_rows(int row0, int colb0, int lc, bool act, const u32x2 (&bv)[FN],
+                                             const f32x4 (&acc)[FM][FN]) const {
+    bf16_t* const base = (act ? cat + (gelu_col0 - split) : qkv) + colb0 + lc;
+    const int ld = act ? ld_cat : ld_qkv;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      bf16_t* const rp = base + size_t(row0 + 16 * i) * ld;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        f32x4 z = acc[i][j] + widen_bf4(bv[j]);
+        if (act) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] = gelu_tanh(z[e]);
+        }
+        store_bf4(rp + 16 * j, z);
+      }
+    }
+  }
 };
 
 // linear1 whose q and k columns also get the per-head RMSNorm (weights qw,
@@ -166,12 +192,17 @@ struct EpiLinear1QK : EpiLinear1 {
   const float* rsin;
   float eps;
   int head_dim;  // 64 or 128
-  // Rows row_base + 16 i (i < FM) of the 128 columns starting at colw (<
-  // 2d, a multiple of 64); lane columns 4*fk + 16 j + (0..3) of block j.
-  // With head_dim 64, blocks j < 4 and j >= 4 are two heads; the q | k
-  // boundary (column d) may fall between them.
-  template <int FM, int FN, bool Guard>
-  __device__ __forceinline__ void store_head(int row_base, int colw, int fk, const f32x4 (&acc)[FM][FN]) const {
+  // Rows rw + fr + 16 i (i < FM) of the 128 columns starting at colw (< 2d,
+  // a multiple of 64); lane columns 4*fk + 16 j + (0..3) of block j.  With
+  // head_dim 64, blocks j < 4 and j >= 4 are two heads; the q | k boundary
+  // (column d) may fall between them.  The RoPE tables and the output go
+  // through buffer descriptors over the wave's rows that lie inside M (the
+  // hardware range check covers the scalar offset too): table reads past M
+  // return zero and stores past M are dropped, so no lane takes a branch; the
+  // row block goes into the scalar offset and the column block into the
+  // instruction's immediate, so no access costs address arithmetic.
+  template <int FM, int FN>
+  __device__ __forceinline__ void store_head(int rw, int fr, int colw, int fk, const f32x4 (&acc)[FM][FN]) const {
     static_assert(FN == 8, "128 columns per wave");
     const int hm = head_dim - 1;       // column inside the head = c & hm
     const int half = head_dim >> 1;    // RoPE table row length
@@ -191,23 +222,35 @@ struct EpiLinear1QK : EpiLinear1 {
 #pragma unroll
       for (int j = 0; j < FN; ++j) bv[j] = u32x2{0u, 0u};
     }
-    // the RoPE table entries of row block i+1 are loaded before row block i
-    // is stored (a wait for a load also waits for every store issued before it)
+    const int rows = max(0, min(16 * FM, M - rw));  // the wave's rows inside M (none when rw >= M)
+    const __amdgpu_buffer_rsrc_t out =
+        __builtin_amdgcn_make_buffer_rsrc(qkv + size_t(rw) * ld_qkv + colw, 0, rows * ld_qkv * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t tcos =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(rcos) + size_t(rw) * half, 0, rows * half * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t tsin =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(rsin) + size_t(rw) * half, 0, rows * half * 4, 0x00020000);
+    const int ovoff = (fr * ld_qkv + 4 * fk) * 2;  // bytes: row fr, lane column 4 fk
+    const int tvoff = (fr * half + 2 * fk) * 4;     // bytes: table row fr, pair 2 fk
+    // The RoPE table entries of row block i+1 are loaded before row block i
+    // is stored (a wait for a load also waits for every store issued before
+    // it).  Column block j's pair sits ((16 j) & hm) / 2 entries further.
     f32x2 cs[2][FN], sn[2][FN];
-    auto tables = [&](int buf, int i) {
-      const int rc = min(row_base + 16 * i, M - 1);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int ch = (j * 16 + 4 * fk) & hm;
-        cs[buf][j] = *reinterpret_cast<const f32x2*>(rcos + size_t(rc) * half + ch / 2);
-        sn[buf][j] = *reinterpret_cast<const f32x2*>(rsin + size_t(rc) * half + ch / 2);
-      }
-    };
-    tables(0, 0);
+    for (int j = 0; j < FN; ++j) {
+      const int so = ((j * 16) & hm) * 2;
+      cs[0][j] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(tcos, tvoff, so, 0));
+      sn[0][j] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(tsin, tvoff, so, 0));
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int row = row_base + 16 * i;
-      if (i + 1 < FM) tables((i + 1) & 1, i + 1);
+      if (i + 1 < FM) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int so = (16 * (i + 1) * half + ((j * 16) & hm) / 2) * 4;
+          cs[(i + 1) & 1][j] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(tcos, tvoff, so, 0));
+          sn[(i + 1) & 1][j] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(tsin, tvoff, so, 0));
+        }
+      }
       f32x4 z[FN];
       float s0 = 0.f, s1 = 0.f;  // sums of squares over blocks 0..3 and 4..7
 #pragma unroll
@@ -225,9 +268,9 @@ struct EpiLinear1QK : EpiLinear1 {
       if (head_dim == 128) s0 = s1 = s0 + s1;
       const float r0 = __frsqrt_rn(s0 * inv_hd + eps);
       const float r1 = __frsqrt_rn(s1 * inv_hd + eps);
+      const int orow = 16 * i * ld_qkv * 2;  // row block i, bytes
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int c = j * 16 + 4 * fk;
         const float r = j < 4 ? r0 : r1;
         const f32x2 cj = cs[i & 1][j], sj = sn[i & 1][j];
         f32x4 n;
@@ -238,7 +281,8 @@ struct EpiLinear1QK : EpiLinear1 {
         o[1] = n[0] * sj[0] + n[1] * cj[0];
         o[2] = n[2] * cj[1] - n[3] * sj[1];
         o[3] = n[2] * sj[1] + n[3] * cj[1];
-        if (!Guard || row < M) store_bf4(qkv + size_t(row) * ld_qkv + colw + c, o);
+        const u32x2 w = u32x2{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(w, out, ovoff + 32 * j, orow, 0);
       }
     }
   }
@@ -246,6 +290,7 @@ struct EpiLinear1QK : EpiLinear1 {
 
 struct EpiLinear2 {
   static constexpr bool kHeadNorm = false;
+  static constexpr bool kRowStore = false;
   const bf16_t* bias;
   const bf16_t* x;
   const float* gate;
@@ -287,6 +332,7 @@ __device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_
 template <class XT, class YT>
 struct EpiGated {
   static constexpr bool kHeadNorm = false;
+  static constexpr bool kRowStore = false;
   const bf16_t* bias;
   const XT* x;
   const float* gate;
@@ -354,8 +400,9 @@ __device__ __forceinline__ void store_tile(const Epi& epi, int row0, int colb0, 
 }
 
 // A wave's whole epilogue: the q/k head path for the tiles whose waves own
-// whole heads, otherwise store_tile; unguarded stores when the wave's
-// sub-tile lies inside the output.
+// whole heads; the row-address path of linear1 for a sub-tile inside the
+// output whose columns lie on one side of split; otherwise store_tile, with
+// unguarded stores when the wave's sub-tile lies inside the output.
 template <int FM, int FN, class Epi>
 __device__ __forceinline__ void wave_epilogue(const Epi& epi, int M, int N, int rw, int cw, int fr, int fk,
                                               const f32x4 (&acc)[FM][FN]) {
@@ -364,8 +411,21 @@ __device__ __forceinline__ void wave_epilogue(const Epi& epi, int M, int N, int 
   const bool full = rw + 16 * FM <= M && cw + 16 * FN <= N;
   if constexpr (Epi::kHeadNorm && FN == 8) {
     if (cw < 2 * epi.d) {  // a whole head: q or k columns get normalised and rotated
-      if (full) epi.template store_head<FM, FN, false>(rw + fr, cw, fk, acc);
-      else epi.template store_head<FM, FN, true>(rw + fr, cw, fk, acc);
+      epi.template store_head<FM, FN>(rw, fr, cw, fk, acc);
+      return;
+    }
+  }
+  if constexpr (Epi::kRowStore) {
+    if (full && (cw + 16 * FN <= epi.split || cw >= epi.split)) {
+      u32x2 bv[FN];  // bias bf16 bits, one uniform branch around the loads
+      if (epi.bias) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bv[j] = load_raw4(epi.bias + cw + 16 * j + 4 * fk);
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bv[j] = u32x2{0u, 0u};
+      }
+      epi.template store_rows<FM, FN>(rw + fr, cw, 4 * fk, cw >= epi.split, bv, acc);
       return;
     }
   }

@@ -59,6 +59,10 @@ BLOCK_SHAPES = [
     # above take the separate kernel); the last tile has 160 rows
     DI.small_shape(seq_len=4000, dim=3072, num_heads=24, head_dim=128, mlp_hidden=12288, grid=(60, 60),
                    text_tokens=400, axes=(64, 64), name="flux_ragged4000"),
+    # the last tile has 60 rows: its second row of waves lies wholly past the
+    # sequence, so the head epilogue's row count is zero there
+    DI.small_shape(seq_len=3900, dim=3072, num_heads=24, head_dim=128, mlp_hidden=12288, grid=(60, 58),
+                   text_tokens=420, axes=(64, 64), name="flux_ragged3900"),
 ]
 
 
