@@ -679,7 +679,7 @@ gemm4w_kernel(GemmGroup<Epi, NP> grp) {
   const Epi& epi = grp.p[pi].epi;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the LDS slot addresses are scalar
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
   int tm, tn;
