@@ -757,23 +757,24 @@ gemm4w_kernel(GemmGroup<Epi, NP> grp) {
     const int kl = min(k + 2, KT - 1);
 #pragma unroll
     for (int g = 0; g < C::FM; ++g) {
+      // Between the group's MFMAs, one instruction at a time: operand read,
+      // refill, operand read, refill.  The next half's B fragments come
+      // first: its first row block needs all of them but only its first A
+      // fragment.
+      auto read_next = [&](int h) {
+        if (g < C::FM / 2) read_b(nxt, 2 * g + h, sb, sw);
+        else read_a(nxt, 2 * (g - C::FM / 2) + h, sb, sw);
+      };
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
         if constexpr (first) mfma_first(acc[g][j], fb[cur][j], fa[cur][g]);
         else mfma_acc(acc[g][j], fb[cur][j], fa[cur][g]);
-      }
-      // the next half's B fragments first: its first row block needs all of
-      // them but only its first A fragment
-      if (g < C::FM / 2) {
-        read_b(nxt, 2 * g, sb, sw);
-        read_b(nxt, 2 * g + 1, sb, sw);
-      } else {
-        read_a(nxt, 2 * (g - C::FM / 2), sb, sw);
-        read_a(nxt, 2 * (g - C::FM / 2) + 1, sb, sw);
-      }
-      if constexpr (cur == 1) {
-        issue1(2 * g, kl, slot);
-        issue1(2 * g + 1, kl, slot);
+        if (j == 1) read_next(0);
+        if (j == 5) read_next(1);
+        if constexpr (cur == 1) {
+          if (j == 3) issue1(2 * g, kl, slot);
+          if (j == 7) issue1(2 * g + 1, kl, slot);
+        }
       }
     }
   };
