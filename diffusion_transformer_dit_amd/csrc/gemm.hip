@@ -634,8 +634,42 @@ struct Tile4Cfg {
   static constexpr int LA = A_WL / NW, LB = B_WL / NW, L = LA + LB;  // wave-loads per wave per slice
   static constexpr int LDS_BYTES = NSTAGE * STAGE;
   static_assert(A_WL % NW == 0 && B_WL % NW == 0, "every wave issues the same number of loads");
-  static_assert(FM == 8 && FN == 8 && L == 16, "the interleave is written for 128 x 128 sub-tiles");
+  static_assert(FM * FN * 4 <= 256, "the accumulators fill at most the 256 accumulation registers");
+  static_assert(L <= FM * FN, "at most one refill per MFMA");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
+};
+
+// Where a half-slice's operand reads and refills go between its FM x FN
+// MFMAs: read r (the FN B fragments, then the FM A fragments of the next
+// half) after MFMA (r NM) / NR + 1, refill l after MFMA (l NM) / L + NM /
+// (2 L) + 1, so that no two follow the same MFMA (128 x 128 sub-tiles: reads
+// after MFMAs 1, 5, 9, ..., refills after 3, 7, 11, ...).  -1: nothing.
+template <class C>
+struct Tile4Sched {
+  static constexpr int NM = C::FM * C::FN, NR = C::FM + C::FN;
+  struct Tab {
+    int read[NM];
+    int load[NM];
+  };
+  static constexpr Tab make() {
+    Tab t{};
+    for (int m = 0; m < NM; ++m) t.read[m] = t.load[m] = -1;
+    for (int r = 0; r < NR; ++r) t.read[(r * NM) / NR + 1] = r;
+    for (int l = 0; l < C::L; ++l) t.load[(l * NM) / C::L + NM / (2 * C::L) + 1] = l;
+    return t;
+  }
+  static constexpr bool valid() {
+    const Tab t = make();
+    int nr = 0, nl = 0;
+    for (int m = 0; m < NM; ++m) {
+      nr += t.read[m] >= 0;
+      nl += t.load[m] >= 0;
+    }
+    return nr == NR && nl == C::L && (((NR - 1) * NM) / NR + 1) < NM &&
+           (((C::L - 1) * NM) / C::L + NM / (2 * C::L) + 1) < NM;
+  }
+  static_assert(valid(), "every read and refill has its own MFMA");
+  static constexpr Tab tab = make();
 };
 
 // 16-byte chunk c of a 128-byte row r sits at position c ^ ((r >> 1) & 7): the
@@ -755,26 +789,23 @@ gemm4w_kernel(GemmGroup<Epi, NP> grp) {
     const unsigned char* sb = smem + (cur == 0 ? slot : slot ^ uint32_t(C::STAGE));
     const uint32_t sw = cur == 0 ? sw1 : sw0;
     const int kl = min(k + 2, KT - 1);
+    // The FM x FN MFMAs of the half, row block by row block, with the
+    // half's operand reads for the next half and, in phase 1, its refills
+    // between them one instruction at a time (the table above).
+    using S = Tile4Sched<C>;
 #pragma unroll
-    for (int g = 0; g < C::FM; ++g) {
-      // Between the group's MFMAs, one instruction at a time: operand read,
-      // refill, operand read, refill.  The next half's B fragments come
-      // first: its first row block needs all of them but only its first A
-      // fragment.
-      auto read_next = [&](int h) {
-        if (g < C::FM / 2) read_b(nxt, 2 * g + h, sb, sw);
-        else read_a(nxt, 2 * (g - C::FM / 2) + h, sb, sw);
-      };
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        if constexpr (first) mfma_first(acc[g][j], fb[cur][j], fa[cur][g]);
-        else mfma_acc(acc[g][j], fb[cur][j], fa[cur][g]);
-        if (j == 1) read_next(0);
-        if (j == 5) read_next(1);
-        if constexpr (cur == 1) {
-          if (j == 3) issue1(2 * g, kl, slot);
-          if (j == 7) issue1(2 * g + 1, kl, slot);
-        }
+    for (int m = 0; m < S::NM; ++m) {
+      const int g = m / C::FN, j = m % C::FN;
+      if constexpr (first) mfma_first(acc[g][j], fb[cur][j], fa[cur][g]);
+      else mfma_acc(acc[g][j], fb[cur][j], fa[cur][g]);
+      const int r = S::tab.read[m];
+      if (r >= 0) {
+        if (r < C::FN) read_b(nxt, r, sb, sw);
+        else read_a(nxt, r - C::FN, sb, sw);
+      }
+      if constexpr (cur == 1) {
+        const int l = S::tab.load[m];
+        if (l >= 0) issue1(l, kl, slot);
       }
     }
   };
@@ -795,6 +826,7 @@ gemm4w_kernel(GemmGroup<Epi, NP> grp) {
 // ------------------------------------------------------------------ tile choice
 using T288x192 = TileCfg<288, 192, 2, 4, 4>;  // 8 waves of 144 x 48; groups own 144-row halves
 using T256 = Tile4Cfg<256, 256>;              // 4 waves of 128 x 128, 64-wide K slices
+using T288x192w4 = Tile4Cfg<288, 192>;        // 4 waves of 144 x 96, 64-wide K slices
 using T256pp = TileCfg<256, 256, 4, 2, 4>;    // the same tile on the ping-pong kernel (8 waves of 64 x 128)
 // The four-wave kernel's refills have one phase of lead (two 64 KB slots),
 // the ping-pong kernel's three 32-wide slices.  For long K both operands
@@ -923,7 +955,9 @@ static hipError_t launch_gemm(const bf16_t* A, const bf16_t* B, int M, int N, in
                               hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   switch (choose_tile(M, N)) {
-    case K288x192: return launch_tile<T288x192>(A, B, M, N, K, e, st);
+    case K288x192:
+      if constexpr (std::is_same_v<Epi, EpiLinear2>) return launch_tile<T288x192w4>(A, B, M, N, K, e, st);
+      return launch_tile<T288x192>(A, B, M, N, K, e, st);
     case K256:
       if constexpr (std::is_same_v<typename Epi::Pre, NoPre>)
         if (four_wave<Epi>(K)) return launch_tile<T256>(A, B, M, N, K, e, st);
