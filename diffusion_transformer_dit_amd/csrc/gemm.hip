@@ -827,22 +827,26 @@ gemm4w_kernel(GemmGroup<Epi, NP> grp) {
 using T288x192 = TileCfg<288, 192, 2, 4, 4>;  // 8 waves of 144 x 48; groups own 144-row halves
 using T256 = Tile4Cfg<256, 256>;              // 4 waves of 128 x 128, 64-wide K slices
 using T288x192w4 = Tile4Cfg<288, 192>;        // 4 waves of 144 x 96, 64-wide K slices
+using T256x192w4 = Tile4Cfg<256, 192>;        // 4 waves of 128 x 96 (N = 1536 in 8 tiles: two full rounds at S = 16384)
 using T256pp = TileCfg<256, 256, 4, 2, 4>;    // the same tile on the ping-pong kernel (8 waves of 64 x 128)
 // The four-wave kernel's refills have one phase of lead (two 64 KB slots),
 // the ping-pong kernel's three 32-wide slices.  For long K both operands
 // stream from HBM (fc2 of the two-stream block: K = 12288, 402 against
 // 347 us) and the deeper prefetch wins.  An epilogue that loads a residual
 // per output (the gated ones) has its latency hidden only with two waves per
-// SIMD (two-stream output projection: 132 against 115 us).  Otherwise (the
-// linear1 epilogues at K = d) the four-wave kernel's larger sub-tiles and
-// whole-line refills win.
+// SIMD (two-stream output projection: 132 against 115 us), so the gated
+// epilogues on 256x256 tiles stay on the ping-pong kernel.  Otherwise the
+// four-wave kernel's larger sub-tiles and whole-line refills win: the linear1
+// epilogues at K = d on 256x256 tiles, linear2 on 288x192 tiles (one full
+// round at the Flux shape, K = 15360: 365 against 393-402 us) and every
+// epilogue on 256x192 tiles (the video shape's N = 1536 GEMMs: block -2.5 to
+// -2.9 %).
 constexpr int kFourWaveMaxK = 4096;
 template <class Epi>
 constexpr bool four_wave(int K) {
   return std::is_same_v<typename Epi::Pre, NoPre> && K <= kFourWaveMaxK;
 }
 using T128x256 = TileCfg<128, 256, 4, 2, 4>;  // 8 waves of 32 x 128 (whole heads per wave, small M)
-using T256x192 = TileCfg<256, 192, 4, 2, 4>;  // 8 waves of 64 x 96 (N = 1536 in 8 tiles: two full rounds at S = 16384)
 using T128 = TileCfg<128, 128, 4, 2, 4>;      // 8 waves of 32 x 64
 
 int num_cus() {
@@ -868,9 +872,11 @@ enum TileKind { K288x192 = 0, K256 = 1, K128 = 2, K128x256 = 3, K256x192 = 4 };
 static TileKind choose_tile(const int* Ms, const int* Ns, int np, bool head_tiles = false) {
   const int cus = num_cus();
   struct Opt { TileKind k; int bm, bn; double eff; bool heads; } opts[] = {
-      // per-tile efficiency measured at the Flux shape (288x192 waves hold a
-      // thinner 144 x 48 sub-tile and run at 0.87 of the 256x256 rate) and,
-      // for 256x192 (64 x 96 per wave), at the video shape's N = 1536 GEMMs
+      // per-tile efficiency measured on the ping-pong kernel at the Flux
+      // shape (288x192 waves hold a thinner 144 x 48 sub-tile and run at 0.87
+      // of the 256x256 rate) and, for 256x192 (64 x 96 per wave), at the
+      // video shape's N = 1536 GEMMs; the four-wave configs of these tiles
+      // only widen the margin of the choices they win
       {K288x192, 288, 192, 0.87, false}, {K256, 256, 256, 1.0, true}, {K128, 128, 128, 0.6, false},
       {K128x256, 128, 256, 0.75, true}, {K256x192, 256, 192, 0.82, false}};
   TileKind best = head_tiles ? K128x256 : K128;
@@ -945,7 +951,7 @@ static hipError_t launch_gemm_group(const GemmProblem<Epi>* ps, int np, hipStrea
       if constexpr (std::is_same_v<typename Epi::Pre, NoPre>)  // the four-wave kernel is built only for these
         if (four_wave<Epi>(ps[0].K)) return launch_tile_group<T256>(ps, np, st);
       return launch_tile_group<T256pp>(ps, np, st);
-    case K256x192: return launch_tile_group<T256x192>(ps, np, st);
+    case K256x192: return launch_tile_group<T256x192w4>(ps, np, st);
     default: return launch_tile_group<T128>(ps, np, st);
   }
 }
@@ -962,7 +968,7 @@ static hipError_t launch_gemm(const bf16_t* A, const bf16_t* B, int M, int N, in
       if constexpr (std::is_same_v<typename Epi::Pre, NoPre>)
         if (four_wave<Epi>(K)) return launch_tile<T256>(A, B, M, N, K, e, st);
       return launch_tile<T256pp>(A, B, M, N, K, e, st);
-    case K256x192: return launch_tile<T256x192>(A, B, M, N, K, e, st);
+    case K256x192: return launch_tile<T256x192w4>(A, B, M, N, K, e, st);
     default: return launch_tile<T128>(A, B, M, N, K, e, st);
   }
 }
