@@ -222,7 +222,10 @@ struct EpiLinear1QK : EpiLinear1 {
 #pragma unroll
       for (int j = 0; j < FN; ++j) bv[j] = u32x2{0u, 0u};
     }
-    const int rows = max(0, min(16 * FM, M - rw));  // the wave's rows inside M (none when rw >= M)
+    // the wave's rows inside M (none when rw >= M); the clamp compiles to a
+    // vector instruction, so the result is made scalar again: a descriptor
+    // built from a vector value costs a loop over lanes at every access
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16 * FM, M - rw)));
     const __amdgpu_buffer_rsrc_t out =
         __builtin_amdgcn_make_buffer_rsrc(qkv + size_t(rw) * ld_qkv + colw, 0, rows * ld_qkv * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t tcos =
