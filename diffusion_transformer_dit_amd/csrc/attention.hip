@@ -27,6 +27,8 @@
 //                 four consecutive rows).  The key order inside each 16-key
 //                 MFMA step is permuted identically on both operands, which
 //                 leaves the contraction unchanged.
+// The MFMAs of one half are issued between the softmax instructions of the
+// other, so a wave's matrix-core work overlaps its own VALU work.
 #include <type_traits>
 
 #include "dit_common.hpp"
@@ -197,93 +199,142 @@ __device__ __forceinline__ void att_range(const bf16_t* __restrict__ qkv, unsign
   issue(kv_begin, 0);
   wait_all();
   __syncthreads();
+
+  // S^T of one 32-key half kb of a staged tile: accumulator register i holds
+  // key 32*kb + 8*(i/4) + 4*hh + (i%4) of the tile for this lane's query.
+  auto scores = [&](const unsigned char* st, int kb) {
+    bf16x8 kf[DH / 16];
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(st + kb * 32 * C::ROW + kaddr[s]);
+    f32x16 sacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
+    return sacc;
+  };
+  // keys at or past kv_end (ragged last tile only) score -inf
+  auto mask_tail = [&](f32x16& sacc, int key0, int kb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= kv_end) sacc[i] = -INFINITY;
+  };
+  // Online-softmax update for one half, in two parts so that the common
+  // path has no branch: softmax_exp packs the bf16 probabilities against
+  // the running max into pk and returns this lane's sum of them;
+  // softmax_fix then handles the rare case where the max must move.  The
+  // max of the scores is only taken when some lane's 16 probabilities sum
+  // past 2^8 (or overflow), i.e. a score rose well above the running max
+  // (always on the first tile).  Keeping a stale max is exact: numerator and
+  // denominator share it, and values up to 2^8 cannot overflow the fp32 sums.
+  auto softmax_exp = [&](const f32x16& sacc, u32x4 (&pk)[2]) {
+    float e[16];
+    const float mc = m_run * c_log2;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[i] = exp2_fast(fmaf(sacc[i], c_log2, -mc));
+    return pack_p(e, pk);
+  };
+  auto softmax_fix = [&](const f32x16& sacc, u32x4 (&pk)[2], float hs) {
+    if (__builtin_amdgcn_ballot_w64(!(hs <= 256.0f))) {
+      float mx = sacc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+      mx = xor32_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_fast((m_run - m_new) * c_log2);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < DH / 32; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+      hs = softmax_exp(sacc, pk);
+    }
+    l_run += hs;
+  };
+  // O^T += V^T P^T over the two 16-key steps of half kb; step m covers keys
+  // 16m + 4hh + (0..3) and 16m + 8 + 4hh + (0..3) of the tile.
+  auto pv = [&](const unsigned char* st, int kb, const u32x4 (&pk)[2]) {
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh) {
+      const int m = 2 * kb + mh;
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pk[mh]);
+#pragma unroll
+      for (int b = 0; b < DH / 32; ++b) {
+        const u32x2 lo = read_tr16(st + vaddr[b] + (16 * m) * C::ROW);
+        const u32x2 hi = read_tr16(st + vaddr[b] + (16 * m + 8) * C::ROW);
+        u32x4 av;
+        av[0] = lo[0];
+        av[1] = lo[1];
+        av[2] = hi[0];
+        av[3] = hi[1];
+        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pf, oacc[b], 0, 0, 0);
+      }
+    }
+  };
   // One K/V tile; the stage is a compile-time constant (the loop below runs
   // tiles in pairs), so every LDS read address is a per-lane base plus an
-  // immediate offset, with no per-tile address arithmetic.
-  auto tile = [&](int jt, auto stage_c) {
+  // immediate offset, with no per-tile address arithmetic.  The scores of
+  // the second half are issued before the softmax of the first, and the PV
+  // product of the first half before the softmax of the second, so that the
+  // matrix cores work on one half while the VALU exponentiates the other;
+  // the arithmetic, and its order on every accumulator, is that of the
+  // plain sequence (scores, softmax, PV per half).
+  auto tile = [&](int jt, auto stage_c, auto ragged_c) {
     constexpr int cur = decltype(stage_c)::value;
+    constexpr bool ragged = decltype(ragged_c)::value;
     if (jt + 1 < ntiles) issue(kv_begin + (jt + 1) * ATT_BN, cur ^ 1);
     const unsigned char* st = smem + cur * C::STAGE;
     const int key0 = kv_begin + jt * ATT_BN;
+    f32x16 s0 = scores(st, 0);
+    if constexpr (ragged) mask_tail(s0, key0, 0);
+    f32x16 s1 = scores(st, 1);
+    u32x4 p0[2], p1[2];
+    float hs = softmax_exp(s0, p0);
+    // issue order: the 16 K reads and half 0's MFMAs, then half 1's MFMAs
+    // each followed by a share of half 0's exponentials
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 kf[DH / 16];
-#pragma unroll
-      for (int s = 0; s < DH / 16; ++s)
-        kf[s] = *reinterpret_cast<const bf16x8*>(st + kb * 32 * C::ROW + kaddr[s]);
-      f32x16 sacc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < DH / 16; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
-      // accumulator row of register i: key 32*kb + 8*(i/4) + 4*hh + (i%4)
-      if (key0 + ATT_BN > kv_end) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= kv_end) sacc[i] = -INFINITY;
-      }
-      // Exponentials against the running max; the max of the scores is only
-      // taken when some lane's 16 probabilities sum past 2^8 (or overflow),
-      // i.e. a score rose well above the running max (always on the first
-      // tile).  Keeping a stale max is exact: numerator and denominator share
-      // it, and values up to 2^8 cannot overflow the fp32 sums.
-      // the softmax of a wave takes issue priority over the other wave's
-      // MFMAs on the SIMD (S = 16384: 1.36 -> 1.34 ms alone; no change in the
-      // Flux stack)
-      __builtin_amdgcn_s_setprio(1);
-      float e[16];
-      float mc = m_run * c_log2;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) e[i] = exp2_fast(fmaf(sacc[i], c_log2, -mc));
-      u32x4 pk[2];
-      float hs = pack_p(e, pk);
-      if (__builtin_amdgcn_ballot_w64(!(hs <= 256.0f))) {
-        float mx = sacc[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-        mx = xor32_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2_fast((m_run - m_new) * c_log2);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < DH / 32; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
-        mc = m_run * c_log2;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) e[i] = exp2_fast(fmaf(sacc[i], c_log2, -mc));
-        hs = pack_p(e, pk);
-      }
-      l_run += hs;
-      __builtin_amdgcn_s_setprio(0);
-      const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, pk[0]), __builtin_bit_cast(bf16x8, pk[1])};
-      // O^T += V^T P^T over the two 16-key steps of this half; step m covers
-      // keys 16m + 4hh + (0..3) and 16m + 8 + 4hh + (0..3) of the tile.
-#pragma unroll
-      for (int mh = 0; mh < 2; ++mh) {
-        const int m = 2 * kb + mh;
-#pragma unroll
-        for (int b = 0; b < DH / 32; ++b) {
-          const u32x2 lo = read_tr16(st + vaddr[b] + (16 * m) * C::ROW);
-          const u32x2 hi = read_tr16(st + vaddr[b] + (16 * m + 8) * C::ROW);
-          u32x4 av;
-          av[0] = lo[0];
-          av[1] = lo[1];
-          av[2] = hi[0];
-          av[3] = hi[1];
-          oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pf[mh],
-                                                            oacc[b], 0, 0, 0);
-        }
-      }
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);  // VALU + transcendental
+    }
+    softmax_fix(s0, p0, hs);
+    if constexpr (ragged) mask_tail(s1, key0, 1);
+    pv(st, 0, p0);
+    hs = softmax_exp(s1, p1);
+    // half 0's PV MFMAs, each after its two V reads and followed by a
+    // share of half 1's exponentials
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS transposing reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);  // VALU + transcendental
+    }
+    softmax_fix(s1, p1, hs);
+    pv(st, 1, p1);
     wait_all();
     __syncthreads();
   };
-  for (int jt = 0; jt < ntiles; jt += 2) {
-    tile(jt, std::integral_constant<int, 0>{});
-    if (jt + 1 < ntiles) tile(jt + 1, std::integral_constant<int, 1>{});
+  // every tile but a ragged last one takes the unmasked path
+  const int nfull = (kv_end - kv_begin) / ATT_BN;
+  using Z = std::integral_constant<int, 0>;
+  using O = std::integral_constant<int, 1>;
+  using F = std::false_type;
+  int jt = 0;
+  for (; jt + 1 < nfull; jt += 2) {
+    tile(jt, Z{}, F{});
+    tile(jt + 1, O{}, F{});
+  }
+  if (jt < nfull) {
+    tile(jt, Z{}, F{});
+    if (jt + 1 < ntiles) tile(jt + 1, O{}, std::true_type{});
+  } else if (jt < ntiles) {
+    tile(jt, Z{}, std::true_type{});
   }
 }
 
