@@ -38,6 +38,10 @@
 namespace dit {
 
 constexpr int ATT_BN = 64;  // keys per tile
+// VALU (and transcendental) instructions of a half's softmax issued after
+// each MFMA of the other half's QK product, and after each MFMA of its PV
+// product (the interleave of the tile body below)
+constexpr int kValuPerQK = 9, kValuPerPV = 12;
 
 template <int DH>
 struct AttCfg {
@@ -301,7 +305,7 @@ __device__ __forceinline__ void att_range(const bf16_t* __restrict__ qkv, unsign
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);  // VALU + transcendental
+      __builtin_amdgcn_sched_group_barrier(0x402, kValuPerQK, 0);  // VALU + transcendental
     }
     softmax_fix(s0, p0, hs);
     if constexpr (ragged) mask_tail(s1, key0, 1);
@@ -313,7 +317,7 @@ __device__ __forceinline__ void att_range(const bf16_t* __restrict__ qkv, unsign
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS transposing reads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);  // VALU + transcendental
+      __builtin_amdgcn_sched_group_barrier(0x402, kValuPerPV, 0);  // VALU + transcendental
     }
     softmax_fix(s1, p1, hs);
     pv(st, 1, p1);
